@@ -1,0 +1,173 @@
+"""Benchmark of the per-rank ZeRO-1/2 optimizer step on one MI355X.
+
+One step = the whole hot path over one batch of synthetic gradients already resident in
+HBM: pack (fused with the overflow check and fp64 sum of squares), norm + clip finalize,
+AdamW on the fp32 master / m / v with cast + scatter-back into the bf16 parameter
+tensors, loss-scaler commit.  Default workload: the Llama-3-8B-shaped list (291 tensors,
+8,030,261,248 elements, one rank).  Prints one JSON line on stdout.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(wl, n_elems, steps):
+    """Time the CPU oracle (as it stands) on a bounded slice of the workload: one tensor of
+    n_elems elements drawn from the workload's distributions, `steps` whole steps."""
+    import torch
+
+    import oracle as O
+    gen = torch.Generator().manual_seed(wl.seed)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float16
+    params = [torch.randn(n_elems, generator=gen).mul_(wl.param_sigma).to(dt)]
+    rank = O.OracleRank([n_elems], 1, 0, params, O.OracleScaler(wl.init_scale, 1.0, wl.dynamic), wl.hparams)
+    times = []
+    for s in range(steps):
+        g = [torch.randn(n_elems, generator=gen).mul_(wl.grad_sigma * rank.scaler.loss_scale).to(dt)]
+        t0 = time.perf_counter()
+        flat = O.pack(g, rank.layout)
+        rank.step(O.shard_of(flat, rank.layout))
+        times.append(time.perf_counter() - t0)
+    per_step = sum(times) / len(times)
+    return {"value": n_elems / per_step, "unit": "elements/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"{steps} whole oracle steps (pack, flag, norm, AdamW, cast, scaler) on a {n_elems}-element "
+                      f"single-tensor slice with the workload's distributions; elements/s = slice size / mean "
+                      f"step time ({per_step:.2f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3_8b")
+    ap.add_argument("--cpu-baseline-elems", type=int, default=1 << 27)
+    ap.add_argument("--cpu-baseline-steps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU: the per-rank step runs on one MI355X with no "
+                                   "collectives, so --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+
+    import zero_sharded_mixed_buffer_amd as Z
+    from workloads import WORKLOADS, gen
+
+    Z.lib()
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    hp = wl.hparams
+    log(f"workload {wl.name}: {len(wl.numels)} tensors, {wl.n_elems} elements, dp {wl.dp_world}")
+    t_setup = time.perf_counter()
+    params = gen.make_params(wl, dev)
+    grads = gen.make_grads(wl, 1, wl.init_scale, dev, with_faults=False)
+    torch.cuda.synchronize()
+    log(f"inputs resident after {time.perf_counter() - t_setup:.1f} s")
+    opt = Z.ZeroShardedAdamW(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                             weight_decay=hp["weight_decay"], max_norm=hp["max_norm"], dp_world=wl.dp_world,
+                             dp_rank=wl.dp_rank, align=wl.align, dynamic_loss_scale=wl.dynamic,
+                             init_scale=wl.init_scale, growth_interval=wl.growth_interval)
+    if wl.dp_world != 1:
+        print(json.dumps({"error": "bench times the single-rank step"}))
+        sys.exit(2)
+    S = opt.shard_numel
+    N = wl.n_elems
+    stream = torch.cuda.current_stream()
+    lay, st = opt.layout, opt.state
+
+    def one_step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        opt.pack(grads, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        opt.norm(stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        Z.zs_adamw_step(lay, opt.shard, opt.grad_dtype, opt.master, opt.m, opt.v, opt.hp, st, opt.param_ptrs, None,
+                        opt.param_dtype, stream)
+        if ev is not None:
+            ev[3].record(stream)
+        Z.zs_scaler_update(st, stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        one_step(evs[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    state = opt.read_state()
+    assert state["skipped_total"] == 0 and state["step_t"] == args.warmup + args.steps
+    pack_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    adamw_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    ms_per_step = elapsed * 1e3 / args.steps
+    adamw_bytes = 28 * S          # read g 2 + master/m/v 12, write master/m/v 12 + param 2
+    pack_bytes = 4 * N            # read 2 + write 2
+    step_bytes = pack_bytes + adamw_bytes
+    adamw_gbps = adamw_bytes / (adamw_ms * 1e-3) / 1e9
+    step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"step {ms_per_step:.3f} ms ({step_gbps:.0f} GB/s), pack {pack_ms:.3f} ms "
+        f"({pack_bytes / pack_ms / 1e6:.0f} GB/s), adamw {adamw_ms:.3f} ms ({adamw_gbps:.0f} GB/s)")
+    out = {
+        "metric": "optimizer-step elements/s and achieved HBM GB/s (% of MI355X peak)",
+        "value": S * args.steps / elapsed,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "storage": "bf16 grads and params, fp32 master/m/v; AdamW and norm arithmetic in fp64",
+        "data": "synthetic: grads N(0,1e-3) and params N(0,0.02) drawn on the GPU, random init, no dataset",
+        "config": {"workload": wl.name, "tensors": len(wl.numels), "elements": N, "dp_world": wl.dp_world,
+                   "shard_elements": S, "grad_dtype": wl.dtype, "align": wl.align},
+        "achieved_hbm_gbps": step_gbps,
+        "hbm_frac": step_gbps / HBM_PEAK_GBPS,
+        "algorithmic_bytes_per_step": step_bytes,
+        "kernels_ms": {"pack_check": pack_ms, "adamw_cast_scatter": adamw_ms,
+                       "finalize_and_scaler": ms_per_step - pack_ms - adamw_ms},
+        "roofline": {"bound": "hbm", "kernel": "k_adamw (AdamW + unscale + clip + cast + scatter)",
+                     "achieved": adamw_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": adamw_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "bytes_per_launch": adamw_bytes, "avg_launch_ms": adamw_ms},
+    }
+    opt.close()
+    del params, grads, opt
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_baseline_elems, args.cpu_baseline_steps)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

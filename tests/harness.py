@@ -1,0 +1,200 @@
+"""Parity harness: run the HIP path and the CPU oracle side by side on one workload.
+
+Inputs (parameters, per-step gradients) are drawn once on the GPU from the seeded
+workload generators and copied to the host for the oracle; no oracle input or
+expected value comes from the HIP path.  For dp_world > 1 the other ranks are
+virtual: every rank's shard is a slice of the same packed buffer (the stand-in for
+the reduce-scatter output), the GPU exchanges the ranks' local sums of squares
+through zs_unscale_check / zs_grad_norm, and the oracle takes the same partial
+sums from its own arithmetic.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+import oracle as O
+import zero_sharded_mixed_buffer_amd as Z
+from workloads import gen
+
+# Parity contract: master, m and v within a max relative error of 1e-5 after the run, the
+# relative error of an element measured against max(|oracle value|, 1e-3 * RMS of the
+# array) because an element that cancels to ~0 has no meaningful relative error.
+REL_TOL = 1e-5
+REL_FLOOR = 1e-3
+NORM_RTOL = 1e-12
+
+
+def rel_err(a: torch.Tensor, b: torch.Tensor) -> float:
+    a = a.double()
+    b = b.double()
+    if b.numel() == 0:
+        return 0.0
+    rms = float(b.pow(2).mean().sqrt())
+    den = torch.clamp(b.abs(), min=REL_FLOOR * rms) if rms > 0 else b.abs()
+    d = (a - b).abs()
+    ok = den > 0
+    if not bool(ok.all()):
+        if bool((d[~ok] != 0).any()):
+            return math.inf
+    return float((d[ok] / den[ok]).max()) if bool(ok.any()) else 0.0
+
+
+def plain_rel_err(a, b) -> float:
+    a = a.double()
+    b = b.double()
+    nz = b != 0
+    if bool((a[~nz] != 0).any()):
+        return math.inf
+    return float(((a - b).abs()[nz] / b.abs()[nz]).max()) if bool(nz.any()) else 0.0
+
+
+def bits(x: torch.Tensor) -> torch.Tensor:
+    return x.contiguous().view(torch.int16) if x.element_size() == 2 else x.contiguous().view(torch.int32)
+
+
+@dataclass
+class StepReport:
+    step: int
+    overflow_gpu: int
+    overflow_oracle: bool
+    scale_gpu: float
+    scale_oracle: float
+    norm_gpu: float = float("nan")
+    norm_oracle: float = float("nan")
+    clip_gpu: float = float("nan")
+    clip_oracle: float = float("nan")
+
+
+@dataclass
+class RunReport:
+    steps: list = field(default_factory=list)
+    master_err: float = 0.0
+    m_err: float = 0.0
+    v_err: float = 0.0
+    master_plain: float = 0.0
+    n_master_diff: int = 0
+    n_m_diff: int = 0
+    n_v_diff: int = 0
+    n_param_diff: int = 0
+
+
+def oracle_scaler(wl):
+    return O.OracleScaler(wl.init_scale, 1.0, wl.dynamic, wl.growth_interval)
+
+
+def run_parity(wl, steps=None, align=None, dp_rank=None, check_every_step=True):
+    """Run `steps` optimizer steps of workload `wl` on cuda:0 and in the oracle, checking
+    every stage each step.  Returns a RunReport; raises AssertionError on a mismatch of
+    the bit-exact quantities."""
+    steps = wl.steps if steps is None else steps
+    align = wl.align if align is None else align
+    rank = wl.dp_rank if dp_rank is None else dp_rank
+    d = wl.dp_world
+    dev = torch.device("cuda", 0)
+    dt = gen.TORCH_DTYPE[wl.dtype]
+    hp = wl.hparams
+
+    params_gpu = gen.make_params(wl, dev)
+    params_cpu = [p.cpu() for p in params_gpu]
+    opt = Z.ZeroShardedAdamW(params_gpu, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                             weight_decay=hp["weight_decay"], max_norm=hp["max_norm"], dp_world=d, dp_rank=rank,
+                             align=align, dynamic_loss_scale=wl.dynamic, init_scale=wl.init_scale,
+                             growth_interval=wl.growth_interval)
+    ref = O.OracleRank(wl.numels, d, rank, params_cpu, oracle_scaler(wl), hp, align)
+    lay = ref.layout
+    assert (opt.flat_numel, opt.shard_begin, opt.shard_numel) == (lay.flat_numel, lay.shard_begin, lay.shard_numel)
+    # Master seeding (pack with widening) is exact.
+    assert torch.equal(opt.master.cpu(), ref.master)
+
+    # Virtual ranks: layout + state of every other rank, sharing the packed buffer.
+    others = {}
+    for q in range(d):
+        if q == rank:
+            continue
+        lq = Z.zs_layout_create(wl.numels, d, q, align)
+        sq = Z.zs_state_create(lq, Z.state_host(wl.init_scale, 1.0, wl.dynamic, wl.growth_interval))
+        others[q] = (lq, sq)
+    exchange = torch.zeros(d, dtype=torch.float64, device=dev)
+    S = lay.shard_numel
+    report = RunReport()
+    try:
+        for step in range(1, steps + 1):
+            scale = ref.scaler.loss_scale
+            grads = gen.make_grads(wl, step, scale, dev)
+            grads_cpu = [g.cpu() for g in grads]
+            prev_params = [p.cpu() for p in params_gpu]
+
+            # ---- GPU path
+            opt.pack(grads)
+            if d == 1:
+                opt.norm()
+            else:
+                for q in range(d):
+                    shard_q = opt.flat[q * S:(q + 1) * S]
+                    if q == rank:
+                        opt.check(local_sumsq_out=exchange[q:q + 1])
+                    else:
+                        Z.zs_unscale_check(others[q][0], shard_q, dt, others[q][1], None, exchange[q:q + 1])
+                opt.norm(rank_sumsq=exchange)
+            st_before = opt.read_state()
+            opt.update()
+            st = opt.read_state()
+
+            # ---- oracle
+            flat_ref = O.pack(grads_cpu, lay)
+            shard_ref = O.shard_of(flat_ref, lay)
+            other = None
+            ext = False
+            if d > 1:
+                other = []
+                for q in range(d):
+                    sq = flat_ref[q * S:(q + 1) * S]
+                    other.append(O.sumsq_unscaled(sq, scale) if not O.nonfinite_any(sq) else math.inf)
+                    if q != rank:
+                        ext = ext or O.nonfinite_any(sq)
+            rec = ref.step(shard_ref, ext_overflow=ext, other_sumsq=other)
+
+            # ---- bit-exact stages: pack, flag, skip, scaler
+            assert torch.equal(bits(opt.flat.cpu()), bits(flat_ref)), f"step {step}: packed buffer differs"
+            assert st_before["overflow"] == int(rec["overflow"]), f"step {step}: overflow flag differs"
+            assert st["loss_scale"] == ref.scaler.loss_scale, f"step {step}: loss scale differs"
+            assert st["step_t"] == ref.scaler.step_t and st["growth_tracker"] == ref.scaler.growth_tracker
+            assert st["skipped_total"] == ref.scaler.skipped_total
+            r = StepReport(step, st_before["overflow"], rec["overflow"], st["loss_scale"], ref.scaler.loss_scale)
+            if not rec["overflow"]:
+                r.norm_gpu, r.norm_oracle = st_before["grad_norm"], rec["norm"]
+                r.clip_gpu, r.clip_oracle = st_before["clip_coef"], rec["clip"]
+                assert abs(r.norm_gpu - r.norm_oracle) <= NORM_RTOL * r.norm_oracle + 1e-300, \
+                    f"step {step}: norm {r.norm_gpu!r} vs {r.norm_oracle!r}"
+                assert abs(r.clip_gpu - r.clip_oracle) <= NORM_RTOL * r.clip_oracle
+            report.steps.append(r)
+
+            if check_every_step or step == steps:
+                master_gpu = opt.master.cpu()
+                params_now = [p.cpu() for p in params_gpu]
+                # Cast + scatter-back as a function of the GPU's own master: bit-exact.
+                want = prev_params if rec["overflow"] else O.unpack(master_gpu, lay, prev_params, False)
+                for i, (a, b) in enumerate(zip(params_now, want)):
+                    assert torch.equal(bits(a), bits(b)), f"step {step}: scattered params of tensor {i} differ"
+                report.master_err = rel_err(master_gpu, ref.master)
+                report.m_err = rel_err(opt.m.cpu(), ref.m)
+                report.v_err = rel_err(opt.v.cpu(), ref.v)
+                report.master_plain = plain_rel_err(master_gpu, ref.master)
+                report.n_master_diff = int((bits(master_gpu) != bits(ref.master)).sum())
+                report.n_m_diff = int((bits(opt.m.cpu()) != bits(ref.m)).sum())
+                report.n_v_diff = int((bits(opt.v.cpu()) != bits(ref.v)).sum())
+                report.n_param_diff = sum(int((bits(a) != bits(b)).sum()) for a, b in zip(params_now, ref.params))
+                assert report.master_err <= REL_TOL, f"step {step}: master rel err {report.master_err}"
+                assert report.m_err <= REL_TOL, f"step {step}: m rel err {report.m_err}"
+                assert report.v_err <= REL_TOL, f"step {step}: v rel err {report.v_err}"
+                assert report.n_param_diff <= report.n_master_diff
+    finally:
+        for lq, sq in others.values():
+            Z.zs_state_destroy(sq)
+            Z.zs_layout_destroy(lq)
+        opt.close()
+    return report

@@ -1,0 +1,324 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bar: bit-exact packed buffer, overflow flags, skip decisions, loss-scale sequence and
+cast/scatter-back (as a function of the GPU master); norm within 1e-12 relative (fp64
+on both sides); master, m, v within the 1e-5 relative-error contract of harness.py.
+"""
+
+import json
+import math
+import os
+
+import pytest
+import torch
+
+import oracle as O
+from workloads import WORKLOADS, gen
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _z():
+    import zero_sharded_mixed_buffer_amd as Z
+    Z.lib()
+    return Z
+
+
+def _log(tag, rep):
+    print(f"[parity] {tag}: master_err={rep.master_err:.3e} m_err={rep.m_err:.3e} v_err={rep.v_err:.3e} "
+          f"plain_master={rep.master_plain:.3e} diff(master,m,v,params)=({rep.n_master_diff},{rep.n_m_diff},"
+          f"{rep.n_v_diff},{rep.n_param_diff}) scales={[s.scale_gpu for s in rep.steps]} "
+          f"skips={[s.overflow_gpu for s in rep.steps]}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama_mini", "ragged_mini", "ragged_mini_a64", "qwen_mini_dp2",
+                                  "moe_mini_dp4"])
+def test_workload_parity(name):
+    from harness import run_parity
+    _z()
+    wl = WORKLOADS[name]
+    print(f"[case] {name} N={wl.n_elems} T={len(wl.numels)} d={wl.dp_world} r={wl.dp_rank} "
+          f"align={wl.align} steps={wl.steps}", flush=True)
+    rep = run_parity(wl)
+    _log(name, rep)
+    overflow_steps = sorted(wl.faults.keys())
+    assert [s.step for s in rep.steps if s.overflow_gpu] == overflow_steps
+
+
+def test_tiny_scale_sequence_matches_hand_table():
+    """fp16, S0 = 2^16, inf at step 3: skip at 3, scale halves, t = 1,2,2,3,4."""
+    from harness import run_parity
+    _z()
+    rep = run_parity(WORKLOADS["tiny"])
+    assert [s.overflow_gpu for s in rep.steps] == [0, 0, 1, 0, 0]
+    assert [s.scale_gpu for s in rep.steps] == [2.0 ** 16, 2.0 ** 16, 2.0 ** 15, 2.0 ** 15, 2.0 ** 15]
+
+
+@pytest.mark.parametrize("rank", [0, 1, 2])
+def test_dp_virtual_ranks_every_rank(rank):
+    from harness import run_parity
+    _z()
+    wl = WORKLOADS["moe_mini_dp4"]
+    rep = run_parity(wl, steps=5, dp_rank=rank)
+    _log(f"moe_mini_dp4 rank {rank}", rep)
+
+
+def test_page_sharded_sgd_example_on_gpu():
+    """The worked example of the Megatron distributed-optimizer section through the HIP path
+    (AdamW in its SGD limit, d = 2 virtual ranks): rank 0 owns [0.8, 1.6], rank 1 [2.4, 3.2]."""
+    Z = _z()
+    with open(os.path.join(GOLDEN, "sharded_sgd_example.json")) as f:
+        ex = json.load(f)
+    dev = torch.device("cuda", 0)
+    d = ex["dp_world"]
+    reduced = [sum(g[i] for g in ex["replica_gradients"]) / d for i in range(4)]
+    hp = Z.hparams(ex["lr"] * 2.0 ** 30, 0.0, 0.0, 2.0 ** 30, 0.0, 0.0)
+    owned = []
+    flat = torch.tensor(reduced, dtype=torch.float16, device=dev)
+    exch = torch.zeros(d, dtype=torch.float64, device=dev)
+    handles = []
+    for r in range(d):
+        lay = Z.zs_layout_create([4], d, r)
+        st = Z.zs_state_create(lay, Z.state_host(1.0, 1.0, False))
+        handles.append((lay, st))
+        Z.zs_unscale_check(lay, flat[r * 2:(r + 1) * 2], torch.float16, st, None, exch[r:r + 1])
+    for r in range(d):
+        lay, st = handles[r]
+        params = [torch.tensor(ex["parameters"], dtype=torch.float16, device=dev)]
+        ptrs = Z.pointer_table(params, dev)
+        master = torch.empty(2, dtype=torch.float32, device=dev)
+        m = torch.zeros(2, dtype=torch.float32, device=dev)
+        v = torch.zeros(2, dtype=torch.float32, device=dev)
+        Z.zs_pack(lay, ptrs, torch.float16, master, torch.float32, whole_flat=False)
+        Z.zs_grad_norm(lay, None, torch.float16, st, hp, exch, None)
+        Z.zs_adamw_step(lay, flat[r * 2:(r + 1) * 2], torch.float16, master, m, v, hp, st, ptrs, None,
+                        torch.float16)
+        Z.zs_scaler_update(st)
+        owned.append(master.cpu())
+        assert Z.zs_state_read(st).step_t == 1
+    for lay, st in handles:
+        Z.zs_state_destroy(st)
+        Z.zs_layout_destroy(lay)
+    assert torch.equal(owned[0], torch.tensor(ex["updated"][:2], dtype=torch.float32))
+    assert torch.equal(owned[1], torch.tensor(ex["updated"][2:], dtype=torch.float32))
+
+
+def _edge_case(numels, dtype, dp_world=1, dp_rank=0, align=1, steps=3, zero_grads=False, seed=0):
+    """Run a small hand-made tensor list through the step and the oracle."""
+    from harness import rel_err, bits
+    Z = _z()
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    params = [torch.randn(n, generator=g, device=dev).mul_(0.02).to(dtype) for n in numels]
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_norm=1.0)
+    dyn = dtype == torch.float16
+    scale = 2.0 ** 16 if dyn else 1.0
+    opt = Z.ZeroShardedAdamW(params, dp_world=dp_world, dp_rank=dp_rank, align=align,
+                             dynamic_loss_scale=dyn, init_scale=scale)
+    ref = O.OracleRank(numels, dp_world, dp_rank, [p.cpu() for p in params], O.OracleScaler(scale, 1.0, dyn), hp,
+                       align)
+    S = ref.layout.shard_numel
+    exch = torch.zeros(dp_world, dtype=torch.float64, device=dev)
+    others = [(Z.zs_layout_create(numels, dp_world, q, align)) for q in range(dp_world)]
+    ostates = [Z.zs_state_create(others[q], Z.state_host(scale, 1.0, dyn)) for q in range(dp_world)]
+    try:
+        for step in range(steps):
+            grads = [(torch.zeros(n, device=dev) if zero_grads else torch.randn(n, generator=g, device=dev))
+                     .mul_(1e-3 * ref.scaler.loss_scale).to(dtype) for n in numels]
+            opt.pack(grads)
+            if dp_world == 1:
+                opt.norm()
+            else:
+                for q in range(dp_world):
+                    if q == dp_rank:
+                        opt.check(local_sumsq_out=exch[q:q + 1])
+                    else:
+                        Z.zs_unscale_check(others[q], opt.flat[q * S:(q + 1) * S], dtype, ostates[q], None,
+                                           exch[q:q + 1])
+                opt.norm(rank_sumsq=exch)
+            opt.update()
+            flat_ref = O.pack([x.cpu() for x in grads], ref.layout)
+            other = [O.sumsq_unscaled(flat_ref[q * S:(q + 1) * S], ref.scaler.loss_scale) for q in range(dp_world)]
+            ref.step(O.shard_of(flat_ref, ref.layout), other_sumsq=other if dp_world > 1 else None)
+            assert torch.equal(bits(opt.flat.cpu()), bits(flat_ref))
+            assert rel_err(opt.master.cpu(), ref.master) <= 1e-5
+            assert rel_err(opt.m.cpu(), ref.m) <= 1e-5
+            assert rel_err(opt.v.cpu(), ref.v) <= 1e-5
+            for a, b in zip(params, ref.params):
+                assert int((bits(a.cpu()) != bits(b)).sum()) == 0 or rel_err(a.cpu().float(), b.float()) < 1e-2
+        st = opt.read_state()
+        assert st["step_t"] == ref.scaler.step_t
+        return opt, ref
+    finally:
+        for q in range(dp_world):
+            Z.zs_state_destroy(ostates[q])
+            Z.zs_layout_destroy(others[q])
+
+
+@pytest.mark.parametrize("numels,dtype,d,r,align", [
+    ([1], torch.bfloat16, 1, 0, 1),                      # a single element
+    ([0, 5, 0, 3, 0], torch.float16, 1, 0, 1),          # empty tensors in the list, ragged tail
+    ([7, 9, 4097, 1, 8191], torch.bfloat16, 3, 1, 1),   # shard starts at an odd element
+    ([7, 9, 4097, 1, 8191], torch.bfloat16, 3, 2, 1),   # last shard, tail padding
+    ([4096 * 3 + 5, 11, 2], torch.float16, 2, 1, 8),    # straddling tensor, aligned starts
+    ([1000] * 40, torch.bfloat16, 4, 3, 64),            # gaps + padding
+])
+def test_edge_case_lists(numels, dtype, d, r, align):
+    print(f"[case] edge numels={numels} d={d} r={r} align={align}", flush=True)
+    opt, _ = _edge_case(numels, dtype, d, r, align)
+    opt.close()
+
+
+def test_zero_gradients_apply_pure_decay():
+    opt, ref = _edge_case([333, 4096], torch.bfloat16, zero_grads=True, steps=4)
+    st = opt.read_state()
+    assert st["grad_norm"] == 0.0 and st["clip_coef"] == 1.0
+    assert torch.count_nonzero(opt.m) == 0 and torch.count_nonzero(opt.v) == 0
+    opt.close()
+
+
+def test_determinism_two_runs_bit_identical():
+    from harness import bits
+    Z = _z()
+    wl = WORKLOADS["ragged_mini"]
+    dev = torch.device("cuda", 0)
+    outs = []
+    for _ in range(2):
+        params = gen.make_params(wl, dev)
+        opt = Z.ZeroShardedAdamW(params, dynamic_loss_scale=False, init_scale=1.0)
+        for step in range(1, 4):
+            opt.step(gen.make_grads(wl, step, 1.0, dev, with_faults=False))
+        outs.append((opt.master.clone(), opt.m.clone(), opt.v.clone(), opt.read_state()))
+        opt.close()
+    a, b = outs
+    for x, y in zip(a[:3], b[:3]):
+        assert torch.equal(bits(x), bits(y))
+    assert a[3]["sumsq"] == b[3]["sumsq"] and a[3]["clip_coef"] == b[3]["clip_coef"]
+
+
+def test_checkpoint_resume_bit_identical():
+    """6 steps straight == 3 steps, save (state + master/m/v), restore into a new object, 3 steps."""
+    from harness import bits
+    Z = _z()
+    wl = WORKLOADS["moe_mini_dp4"]
+    wl1 = WORKLOADS["llama_mini"]
+    dev = torch.device("cuda", 0)
+    for w in (wl1,):
+        p0 = gen.make_params(w, dev)
+        a = Z.ZeroShardedAdamW([p.clone() for p in p0])
+        for s in range(1, 7):
+            a.step(gen.make_grads(w, s, 1.0, dev))
+        b = Z.ZeroShardedAdamW([p.clone() for p in p0])
+        for s in range(1, 4):
+            b.step(gen.make_grads(w, s, 1.0, dev))
+        saved = (b.read_state(), b.master.clone(), b.m.clone(), b.v.clone(), [p.clone() for p in b.params])
+        b.close()
+        c = Z.ZeroShardedAdamW(saved[4])
+        c.write_state(saved[0])
+        c.master.copy_(saved[1])
+        c.m.copy_(saved[2])
+        c.v.copy_(saved[3])
+        for s in range(4, 7):
+            c.step(gen.make_grads(w, s, 1.0, dev))
+        for x, y in ((a.master, c.master), (a.m, c.m), (a.v, c.v)):
+            assert torch.equal(bits(x), bits(y))
+        assert all(torch.equal(bits(x), bits(y)) for x, y in zip(a.params, c.params))
+        assert a.read_state()["step_t"] == c.read_state()["step_t"] == 6
+        a.close()
+        c.close()
+    del wl
+
+
+def test_unpack_whole_flat_and_shard():
+    """zs_unpack as the all-gather consumer: a model-dtype flat buffer (bit copy) and an fp32
+    shard (RNE cast) scattered into the tensors, against the oracle's unpack."""
+    from harness import bits
+    Z = _z()
+    dev = torch.device("cuda", 0)
+    wl = WORKLOADS["ragged_mini"]
+    numels = wl.numels
+    for d, r, align in ((1, 0, 1), (3, 1, 1), (4, 3, 64)):
+        lay = Z.zs_layout_create(numels, d, r, align)
+        flat_numel, sb, sn = Z.zs_layout_info(lay)
+        olay = O.plan_layout(numels, d, r, align)
+        g = torch.Generator(device=dev)
+        g.manual_seed(d * 10 + r)
+        flat = torch.randn(flat_numel, generator=g, device=dev).to(torch.bfloat16)
+        dst = [torch.zeros(n, dtype=torch.bfloat16, device=dev) for n in numels]
+        ptrs = Z.pointer_table(dst, dev)
+        Z.zs_unpack(lay, flat, torch.bfloat16, True, ptrs, torch.bfloat16)
+        want = O.unpack(flat.cpu(), olay, [x.cpu() for x in dst], True)
+        assert all(torch.equal(bits(a.cpu()), bits(b)) for a, b in zip(dst, want))
+        master = torch.randn(sn, generator=g, device=dev) * 3
+        dst2 = [torch.zeros(n, dtype=torch.float16, device=dev) for n in numels]
+        ptrs2 = Z.pointer_table(dst2, dev)
+        Z.zs_unpack(lay, master, torch.float32, False, ptrs2, torch.float16)
+        want2 = O.unpack(master.cpu(), olay, [torch.zeros(n, dtype=torch.float16) for n in numels], False)
+        assert all(torch.equal(bits(a.cpu()), bits(b)) for a, b in zip(dst2, want2))
+        # Unpacking a flat buffer with a misaligned start (a shard view) is a bit copy too.
+        shard_view = flat[sb:sb + sn]
+        dst3 = [torch.zeros(n, dtype=torch.bfloat16, device=dev) for n in numels]
+        Z.zs_unpack(lay, shard_view, torch.bfloat16, False, Z.pointer_table(dst3, dev), torch.bfloat16)
+        want3 = O.unpack(shard_view.cpu(), olay, [torch.zeros(n, dtype=torch.bfloat16) for n in numels], False)
+        assert all(torch.equal(bits(a.cpu()), bits(b)) for a, b in zip(dst3, want3))
+        Z.zs_layout_destroy(lay)
+
+
+def test_cast_rounding_ties_on_gpu():
+    """Round-to-nearest-even of the fp32 -> bf16 / fp16 casts at exact ties and overflow."""
+    from harness import bits
+    Z = _z()
+    dev = torch.device("cuda", 0)
+    vals = torch.tensor([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 1 + 2 ** -11, 1 + 3 * 2 ** -11,
+                         65519.0, 65520.0, 1e-30, -0.0, 3.0e38], dtype=torch.float32)
+    n = vals.numel()
+    for dt in (torch.bfloat16, torch.float16):
+        lay = Z.zs_layout_create([n], 1, 0)
+        dst = [torch.zeros(n, dtype=dt, device=dev)]
+        Z.zs_unpack(lay, vals.to(dev), torch.float32, False, Z.pointer_table(dst, dev), dt)
+        assert torch.equal(bits(dst[0].cpu()), bits(O.cast_to(vals, dt)))
+        Z.zs_layout_destroy(lay)
+
+
+def test_overflow_forms_nan_inf_neg_inf_and_ext_flag():
+    Z = _z()
+    dev = torch.device("cuda", 0)
+    n = 10_000
+    for dt in (torch.bfloat16, torch.float16):
+        for bad in (math.nan, math.inf, -math.inf, None):
+            lay = Z.zs_layout_create([n], 1, 0)
+            st = Z.zs_state_create(lay, Z.state_host(1.0, 1.0, False))
+            x = torch.ones(n, dtype=dt, device=dev)
+            if bad is not None:
+                x[n - 3] = bad
+            Z.zs_unscale_check(lay, x, dt, st)
+            assert Z.zs_state_read(st).overflow == (0 if bad is None else 1)
+            ext = torch.tensor([1 if bad is None else 0], dtype=torch.int32, device=dev)
+            Z.zs_unscale_check(lay, x, dt, st, ext)
+            assert Z.zs_state_read(st).overflow == 1
+            Z.zs_state_destroy(st)
+            Z.zs_layout_destroy(lay)
+
+
+def test_invalid_arguments_rejected_before_launch():
+    Z = _z()
+    dev = torch.device("cuda", 0)
+    lay = Z.zs_layout_create([100], 1, 0)
+    st = Z.zs_state_create(lay, Z.state_host(1.0, 1.0, False))
+    buf = torch.zeros(128, dtype=torch.float32, device=dev)
+    g = torch.zeros(100, dtype=torch.bfloat16, device=dev)
+    hp = Z.hparams()
+    with pytest.raises(Z.ZsError) as e:
+        Z.zs_adamw_step(lay, g, torch.bfloat16, buf[1:], buf, buf, hp, st)   # unaligned master
+    assert e.value.status == -1
+    with pytest.raises(Z.ZsError):
+        Z.zs_adamw_step(lay, g, torch.bfloat16, buf, buf, buf, Z.hparams(beta1=1.0), st)
+    with pytest.raises(Z.ZsError):
+        Z.zs_state_create(lay, Z.state_host(3.0, 1.0, True))                # scale not a power of two
+    with pytest.raises(Z.ZsError):
+        Z.zs_grad_norm(Z.zs_layout_create([100], 2, 0), None, torch.bfloat16, st, hp)  # rank_sumsq missing
+    Z.zs_state_destroy(st)
+    Z.zs_layout_destroy(lay)

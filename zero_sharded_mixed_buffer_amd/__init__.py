@@ -1,0 +1,37 @@
+"""MI355X-native per-rank ZeRO-1/2 mixed-precision optimizer step.
+
+The step runs in hand-written gfx950 HIP kernels behind the C ABI of
+include/zs.h (libzs.so, built in-tree by `python -m zero_sharded_mixed_buffer_amd.build`);
+this package is its ctypes binding plus a rank-level optimizer object.
+"""
+
+from ._abi import (  # noqa: F401
+    LIB_PATH,
+    ZS_BF16,
+    ZS_FP16,
+    ZS_FP32,
+    AdamwHParams,
+    StateHost,
+    ZsError,
+    dtype_code,
+    hparams,
+    lib,
+    state_host,
+    zs_adamw_step,
+    zs_grad_norm,
+    zs_last_error,
+    zs_layout_create,
+    zs_layout_destroy,
+    zs_layout_info,
+    zs_pack,
+    zs_plan,
+    zs_plan_segments,
+    zs_scaler_update,
+    zs_state_create,
+    zs_state_destroy,
+    zs_state_read,
+    zs_state_write,
+    zs_unpack,
+    zs_unscale_check,
+)
+from .optimizer import ZeroShardedAdamW, pointer_table  # noqa: F401

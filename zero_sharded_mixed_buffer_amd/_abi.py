@@ -1,0 +1,241 @@
+"""ctypes binding of libzs.so (include/zs.h), one Python function per C entry point.
+
+Argument marshalling only: every computation runs in the HIP library.  Pointer
+arguments accept an int (a device or host address), None (NULL) or anything
+with .data_ptr() (a torch tensor); `stream` accepts a torch stream, an int
+handle or None (the current torch stream of the current device).  A non-zero
+status raises ZsError carrying zs_last_error().  If the library is not built
+the first call raises ImportError; there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, byref, c_double, c_int32, c_int64, c_void_p
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzs.so")
+
+ZS_BF16, ZS_FP16, ZS_FP32 = 0, 1, 2
+STATUS = {0: "ZS_OK", -1: "ZS_EINVAL", -2: "ZS_EHIP", -3: "ZS_ENOMEM", -4: "ZS_EUNSUPPORTED"}
+
+
+class ZsError(RuntimeError):
+    def __init__(self, what, status, message):
+        super().__init__(f"{what} failed with {STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class AdamwHParams(ctypes.Structure):
+    _fields_ = [("lr", c_double), ("beta1", c_double), ("beta2", c_double), ("eps", c_double),
+                ("weight_decay", c_double), ("max_norm", c_double)]
+
+
+class StateHost(ctypes.Structure):
+    _fields_ = [("loss_scale", c_double), ("scale_floor", c_double), ("dynamic", c_int32),
+                ("growth_interval", c_int32), ("growth_tracker", c_int64), ("step_t", c_int64),
+                ("skipped_total", c_int64), ("overflow", c_int32), ("reserved", c_int32),
+                ("local_sumsq", c_double), ("sumsq", c_double), ("grad_norm", c_double),
+                ("clip_coef", c_double)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_ if k != "reserved"}
+
+
+_lib = None
+
+_SIGS = {
+    "zs_plan": [c_void_p, c_int32, c_int32, c_int32, c_int64, c_void_p, c_void_p, c_void_p, c_void_p],
+    "zs_plan_segments": [c_void_p, c_int32, c_int32, c_int32, c_int64, c_int32, c_void_p, c_void_p, c_void_p,
+                         c_int64, c_void_p],
+    "zs_layout_create": [c_void_p, c_int32, c_int32, c_int32, c_int64, POINTER(c_void_p)],
+    "zs_layout_info": [c_void_p, c_void_p, c_void_p, c_void_p],
+    "zs_state_create": [c_void_p, POINTER(StateHost), POINTER(c_void_p)],
+    "zs_state_read": [c_void_p, POINTER(StateHost), c_void_p],
+    "zs_state_write": [c_void_p, POINTER(StateHost), c_void_p],
+    "zs_pack": [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p],
+    "zs_unscale_check": [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p],
+    "zs_grad_norm": [c_void_p, c_void_p, c_int32, c_void_p, POINTER(AdamwHParams), c_void_p, c_void_p, c_void_p],
+    "zs_adamw_step": [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, POINTER(AdamwHParams), c_void_p,
+                      c_void_p, c_void_p, c_int32, c_void_p],
+    "zs_unpack": [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_void_p],
+    "zs_scaler_update": [c_void_p, c_void_p],
+}
+
+
+def lib():
+    """Load libzs.so (once).  Raises ImportError when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with python -m zero_sharded_mixed_buffer_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = c_int32
+        L.zs_layout_destroy.argtypes = [c_void_p]
+        L.zs_layout_destroy.restype = None
+        L.zs_state_destroy.argtypes = [c_void_p]
+        L.zs_state_destroy.restype = None
+        L.zs_last_error.argtypes = []
+        L.zs_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status, what):
+    if status != 0:
+        raise ZsError(what, status, lib().zs_last_error().decode(errors="replace"))
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if isinstance(x, ctypes.Array):
+        return ctypes.addressof(x)
+    return int(x)
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if hasattr(s, "cuda_stream"):
+        return s.cuda_stream
+    return int(s)
+
+
+def _i64_array(values):
+    return (c_int64 * len(values))(*[int(v) for v in values])
+
+
+def dtype_code(dtype):
+    """ZS_* code of a torch dtype (bfloat16, float16, float32) or of an int code."""
+    if isinstance(dtype, int):
+        return dtype
+    import torch
+    return {torch.bfloat16: ZS_BF16, torch.float16: ZS_FP16, torch.float32: ZS_FP32}[dtype]
+
+
+# ------------------------------------------------------------------------------ planning
+
+def zs_plan(numels, dp_world, dp_rank, align_elems=1):
+    """Returns (offsets, flat_numel, shard_begin, shard_numel)."""
+    n = len(numels)
+    arr = _i64_array(numels)
+    offs = (c_int64 * max(n, 1))()
+    fn, sb, sn = c_int64(), c_int64(), c_int64()
+    _check(lib().zs_plan(ctypes.addressof(arr) if n else None, n, dp_world, dp_rank, align_elems,
+                         ctypes.addressof(offs), byref(fn), byref(sb), byref(sn)), "zs_plan")
+    return list(offs)[:n], fn.value, sb.value, sn.value
+
+
+def zs_plan_segments(numels, dp_world, dp_rank, align_elems=1, whole_flat=False):
+    """Returns (seg_begin, seg_tensor, seg_local) lists of the kernels' segment map."""
+    n = len(numels)
+    arr = _i64_array(numels)
+    count = c_int64()
+    _check(lib().zs_plan_segments(ctypes.addressof(arr), n, dp_world, dp_rank, align_elems, int(bool(whole_flat)),
+                                  None, None, None, 0, byref(count)), "zs_plan_segments")
+    k = count.value
+    b, t, loc = (c_int64 * max(k, 1))(), (c_int32 * max(k, 1))(), (c_int64 * max(k, 1))()
+    _check(lib().zs_plan_segments(ctypes.addressof(arr), n, dp_world, dp_rank, align_elems, int(bool(whole_flat)),
+                                  ctypes.addressof(b), ctypes.addressof(t), ctypes.addressof(loc), k, byref(count)),
+           "zs_plan_segments")
+    return list(b)[:k], list(t)[:k], list(loc)[:k]
+
+
+# ------------------------------------------------------------------------------ handles
+
+def zs_layout_create(numels, dp_world, dp_rank, align_elems=1):
+    arr = _i64_array(numels)
+    out = c_void_p()
+    _check(lib().zs_layout_create(ctypes.addressof(arr) if len(numels) else None, len(numels), dp_world, dp_rank,
+                                  align_elems, byref(out)), "zs_layout_create")
+    return out.value
+
+
+def zs_layout_destroy(layout):
+    lib().zs_layout_destroy(layout)
+
+
+def zs_layout_info(layout):
+    """Returns (flat_numel, shard_begin, shard_numel)."""
+    a, b, c = c_int64(), c_int64(), c_int64()
+    _check(lib().zs_layout_info(layout, byref(a), byref(b), byref(c)), "zs_layout_info")
+    return a.value, b.value, c.value
+
+
+def state_host(loss_scale=1.0, scale_floor=1.0, dynamic=False, growth_interval=1000, growth_tracker=0, step_t=0,
+               skipped_total=0, clip_coef=1.0):
+    s = StateHost()
+    s.loss_scale, s.scale_floor, s.dynamic = loss_scale, scale_floor, int(bool(dynamic))
+    s.growth_interval, s.growth_tracker, s.step_t, s.skipped_total = growth_interval, growth_tracker, step_t, skipped_total
+    s.clip_coef = clip_coef
+    return s
+
+
+def zs_state_create(layout, init: StateHost):
+    out = c_void_p()
+    _check(lib().zs_state_create(layout, byref(init), byref(out)), "zs_state_create")
+    return out.value
+
+
+def zs_state_destroy(state):
+    lib().zs_state_destroy(state)
+
+
+def zs_state_read(state, stream=None) -> StateHost:
+    out = StateHost()
+    _check(lib().zs_state_read(state, byref(out), _stream(stream)), "zs_state_read")
+    return out
+
+
+def zs_state_write(state, value: StateHost, stream=None):
+    _check(lib().zs_state_write(state, byref(value), _stream(stream)), "zs_state_write")
+
+
+def hparams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_norm=1.0):
+    return AdamwHParams(lr, beta1, beta2, eps, weight_decay, max_norm)
+
+
+# ------------------------------------------------------------------------------ step calls
+
+def zs_pack(layout, src_ptrs, src_dtype, dst, dst_dtype, whole_flat=True, fuse_check=None, stream=None):
+    _check(lib().zs_pack(layout, _ptr(src_ptrs), dtype_code(src_dtype), _ptr(dst), dtype_code(dst_dtype),
+                         int(bool(whole_flat)), fuse_check, _stream(stream)), "zs_pack")
+
+
+def zs_unscale_check(layout, shard, grad_dtype, state, ext_overflow=None, local_sumsq_out=None, stream=None):
+    _check(lib().zs_unscale_check(layout, _ptr(shard), dtype_code(grad_dtype), state, _ptr(ext_overflow),
+                                  _ptr(local_sumsq_out), _stream(stream)), "zs_unscale_check")
+
+
+def zs_grad_norm(layout, shard, grad_dtype, state, hp: AdamwHParams, rank_sumsq=None, local_sumsq_out=None,
+                 stream=None):
+    _check(lib().zs_grad_norm(layout, _ptr(shard), dtype_code(grad_dtype), state, byref(hp), _ptr(rank_sumsq),
+                              _ptr(local_sumsq_out), _stream(stream)), "zs_grad_norm")
+
+
+def zs_adamw_step(layout, shard, grad_dtype, master, m, v, hp: AdamwHParams, state, param_ptrs=None,
+                  flat_param_out=None, param_dtype=ZS_BF16, stream=None):
+    _check(lib().zs_adamw_step(layout, _ptr(shard), dtype_code(grad_dtype), _ptr(master), _ptr(m), _ptr(v),
+                               byref(hp), state, _ptr(param_ptrs), _ptr(flat_param_out), dtype_code(param_dtype),
+                               _stream(stream)), "zs_adamw_step")
+
+
+def zs_unpack(layout, src, src_dtype, whole_flat, dst_ptrs, dst_dtype, honour_skip=None, stream=None):
+    _check(lib().zs_unpack(layout, _ptr(src), dtype_code(src_dtype), int(bool(whole_flat)), _ptr(dst_ptrs),
+                           dtype_code(dst_dtype), honour_skip, _stream(stream)), "zs_unpack")
+
+
+def zs_scaler_update(state, stream=None):
+    _check(lib().zs_scaler_update(state, _stream(stream)), "zs_scaler_update")
+
+
+def zs_last_error():
+    return lib().zs_last_error().decode(errors="replace")

@@ -1,0 +1,540 @@
+// Host side of the C ABI: argument validation, the flat-buffer planner, the segment maps
+// uploaded once per layout, the device state, and the launch sequence of each entry point.
+// Every step entry point only enqueues work on the caller's stream.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "zs.h"
+#include "zs_internal.h"
+
+using zs::DevMap;
+using zs::DevState;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+zs_status fail(zs_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+zs_status ok() { return ZS_OK; }
+
+zs_status hip_fail(hipError_t e, const char* what) {
+  return fail(ZS_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+bool is_pow2_double(double x) {
+  if (!(x > 0.0) || !std::isfinite(x)) return false;
+  int e = 0;
+  return std::frexp(x, &e) == 0.5;
+}
+
+int64_t round_up(int64_t x, int64_t m) { return ((x + m - 1) / m) * m; }
+
+// ---------------------------------------------------------------------------- planner
+
+struct Plan {
+  std::vector<int64_t> numels;
+  std::vector<int64_t> offsets;
+  int64_t flat_numel = 0;
+  int64_t shard_begin = 0;
+  int64_t shard_numel = 0;
+  int32_t dp_world = 1;
+  int32_t dp_rank = 0;
+  int64_t align = 1;
+};
+
+zs_status make_plan(const int64_t* numels, int32_t n, int32_t dp_world, int32_t dp_rank, int64_t align,
+                    Plan* out) {
+  if (numels == nullptr) return fail(ZS_EINVAL, "numels is NULL");
+  if (n < 1) return fail(ZS_EINVAL, "n_tensors must be >= 1 (got %d)", n);
+  if (dp_world < 1) return fail(ZS_EINVAL, "dp_world must be >= 1 (got %d)", dp_world);
+  if (dp_rank < 0 || dp_rank >= dp_world) return fail(ZS_EINVAL, "dp_rank %d outside [0, %d)", dp_rank, dp_world);
+  if (!is_pow2(align)) return fail(ZS_EINVAL, "align_elems must be a power of two (got %lld)", (long long)align);
+  Plan p;
+  p.numels.assign(numels, numels + n);
+  p.offsets.resize(n);
+  p.dp_world = dp_world;
+  p.dp_rank = dp_rank;
+  p.align = align;
+  int64_t pos = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (numels[i] < 0) return fail(ZS_EINVAL, "numels[%d] is negative", i);
+    pos = round_up(pos, align);
+    p.offsets[i] = pos;
+    pos += numels[i];
+    if (pos < 0) return fail(ZS_EINVAL, "total size overflows int64");
+  }
+  p.flat_numel = round_up(pos, int64_t(dp_world) * align);
+  p.shard_numel = p.flat_numel / dp_world;
+  p.shard_begin = int64_t(dp_rank) * p.shard_numel;
+  *out = std::move(p);
+  return ok();
+}
+
+struct HostMap {
+  std::vector<int64_t> seg_begin;  // nseg + 1
+  std::vector<int64_t> seg_local;
+  std::vector<int32_t> seg_tensor;
+  std::vector<int32_t> tile_first;  // ntiles + 1
+  int64_t len = 0;
+  int64_t ntiles = 0;
+};
+
+// Split [begin, begin + len) into maximal pieces inside one tensor or inside padding.
+HostMap build_map(const Plan& p, int64_t begin, int64_t len) {
+  HostMap m;
+  m.len = len;
+  const int64_t end = begin + len;
+  int64_t cur = begin;
+  for (size_t i = 0; i < p.numels.size(); ++i) {
+    const int64_t a = std::max(p.offsets[i], begin);
+    const int64_t b = std::min(p.offsets[i] + p.numels[i], end);
+    if (a >= b) continue;
+    if (a > cur) {
+      m.seg_begin.push_back(cur - begin);
+      m.seg_local.push_back(0);
+      m.seg_tensor.push_back(-1);
+    }
+    m.seg_begin.push_back(a - begin);
+    m.seg_local.push_back(a - p.offsets[i]);
+    m.seg_tensor.push_back(static_cast<int32_t>(i));
+    cur = b;
+  }
+  if (cur < end) {
+    m.seg_begin.push_back(cur - begin);
+    m.seg_local.push_back(0);
+    m.seg_tensor.push_back(-1);
+  }
+  const int64_t nseg = static_cast<int64_t>(m.seg_tensor.size());
+  m.seg_begin.push_back(len);
+  m.ntiles = (len + zs::kTile - 1) / zs::kTile;
+  m.tile_first.resize(m.ntiles + 1);
+  int64_t s = 0;
+  for (int64_t k = 0; k < m.ntiles; ++k) {
+    const int64_t x = k * zs::kTile;
+    while (m.seg_begin[s + 1] <= x) ++s;
+    m.tile_first[k] = static_cast<int32_t>(s);
+  }
+  m.tile_first[m.ntiles] = static_cast<int32_t>(nseg > 0 ? nseg - 1 : 0);
+  return m;
+}
+
+// One device allocation per map: seg_begin | seg_local | seg_tensor | tile_first.
+zs_status upload_map(const HostMap& h, void** mem, DevMap* out) {
+  const size_t nseg = h.seg_tensor.size();
+  const size_t b0 = 0;
+  const size_t b1 = b0 + (nseg + 1) * sizeof(int64_t);
+  const size_t b2 = b1 + std::max<size_t>(nseg, 1) * sizeof(int64_t);
+  const size_t b3 = b2 + round_up(std::max<size_t>(nseg, 1) * sizeof(int32_t), 16);
+  const size_t total = b3 + h.tile_first.size() * sizeof(int32_t);
+  void* d = nullptr;
+  hipError_t e = hipMalloc(&d, total);
+  if (e != hipSuccess) return fail(ZS_ENOMEM, "hipMalloc of %zu bytes for the segment map: %s", total, hipGetErrorString(e));
+  std::vector<unsigned char> host(total, 0);
+  std::memcpy(host.data() + b0, h.seg_begin.data(), h.seg_begin.size() * sizeof(int64_t));
+  if (nseg) {
+    std::memcpy(host.data() + b1, h.seg_local.data(), nseg * sizeof(int64_t));
+    std::memcpy(host.data() + b2, h.seg_tensor.data(), nseg * sizeof(int32_t));
+  }
+  std::memcpy(host.data() + b3, h.tile_first.data(), h.tile_first.size() * sizeof(int32_t));
+  e = hipMemcpy(d, host.data(), total, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(d);
+    return hip_fail(e, "uploading the segment map");
+  }
+  unsigned char* base = static_cast<unsigned char*>(d);
+  out->seg_begin = reinterpret_cast<const int64_t*>(base + b0);
+  out->seg_local = reinterpret_cast<const int64_t*>(base + b1);
+  out->seg_tensor = reinterpret_cast<const int32_t*>(base + b2);
+  out->tile_first = reinterpret_cast<const int32_t*>(base + b3);
+  out->len = h.len;
+  out->ntiles = h.ntiles;
+  out->nseg = static_cast<int32_t>(nseg);
+  *mem = d;
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool is_half_dtype(int dt) { return dt == ZS_BF16 || dt == ZS_FP16; }
+
+zs_status check_state_fields(const zs_state_host* s) {
+  if (!is_pow2_double(s->loss_scale)) return fail(ZS_EINVAL, "loss_scale must be a positive power of two");
+  if (!is_pow2_double(s->scale_floor)) return fail(ZS_EINVAL, "scale_floor must be a positive power of two");
+  if (s->growth_interval < 1) return fail(ZS_EINVAL, "growth_interval must be >= 1");
+  if (s->dynamic != 0 && s->dynamic != 1) return fail(ZS_EINVAL, "dynamic must be 0 or 1");
+  if (s->step_t < 0 || s->growth_tracker < 0 || s->skipped_total < 0)
+    return fail(ZS_EINVAL, "step_t, growth_tracker and skipped_total must be >= 0");
+  return ok();
+}
+
+zs_status check_hparams(const zs_adamw_hparams* hp) {
+  if (hp == nullptr) return fail(ZS_EINVAL, "hparams is NULL");
+  const double vals[6] = {hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->max_norm};
+  for (double x : vals)
+    if (!std::isfinite(x)) return fail(ZS_EINVAL, "hyper-parameters must be finite");
+  if (hp->lr < 0) return fail(ZS_EINVAL, "lr must be >= 0");
+  if (hp->beta1 < 0 || hp->beta1 >= 1 || hp->beta2 < 0 || hp->beta2 >= 1)
+    return fail(ZS_EINVAL, "betas must lie in [0, 1)");
+  if (!(hp->eps > 0)) return fail(ZS_EINVAL, "eps must be > 0");
+  if (hp->weight_decay < 0) return fail(ZS_EINVAL, "weight_decay must be >= 0");
+  return ok();
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------- opaque types
+
+struct zs_layout {
+  Plan plan;
+  int device = 0;
+  int num_cu = 0;
+  void* mem_shard = nullptr;
+  void* mem_full = nullptr;  // null when the shard is the whole buffer (dp_world == 1)
+  DevMap map_shard{};
+  DevMap map_full{};
+  int grid_stream = 0;  // workgroups of the persistent streaming kernels
+  int nparts = 0;       // partial-sum slots = workgroups of the reduction passes
+};
+
+struct zs_state {
+  DevState* dev = nullptr;
+  double* partials = nullptr;
+  int nparts = 0;
+  int device = 0;
+};
+
+namespace {
+
+zs_status check_device(int device) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (cur != device) return fail(ZS_EINVAL, "current device %d is not the layout's device %d", cur, device);
+  return ok();
+}
+
+zs_status check_layout(const zs_layout* l) {
+  if (l == nullptr) return fail(ZS_EINVAL, "layout is NULL");
+  return check_device(l->device);
+}
+
+zs_status check_state(const zs_layout* l, const zs_state* s) {
+  if (s == nullptr) return fail(ZS_EINVAL, "state is NULL");
+  if (s->device != l->device) return fail(ZS_EINVAL, "state and layout live on different devices");
+  if (s->nparts < l->nparts) return fail(ZS_EINVAL, "state was created for a smaller layout");
+  return ok();
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------- planning ABI
+
+extern "C" zs_status zs_plan(const int64_t* numels, int32_t n_tensors, int32_t dp_world, int32_t dp_rank,
+                             int64_t align_elems, int64_t* offsets_out, int64_t* flat_numel_out,
+                             int64_t* shard_begin_out, int64_t* shard_numel_out) {
+  Plan p;
+  zs_status st = make_plan(numels, n_tensors, dp_world, dp_rank, align_elems, &p);
+  if (st != ZS_OK) return st;
+  if (offsets_out) std::memcpy(offsets_out, p.offsets.data(), p.offsets.size() * sizeof(int64_t));
+  if (flat_numel_out) *flat_numel_out = p.flat_numel;
+  if (shard_begin_out) *shard_begin_out = p.shard_begin;
+  if (shard_numel_out) *shard_numel_out = p.shard_numel;
+  return ok();
+}
+
+extern "C" zs_status zs_plan_segments(const int64_t* numels, int32_t n_tensors, int32_t dp_world, int32_t dp_rank,
+                                      int64_t align_elems, int32_t whole_flat, int64_t* seg_begin,
+                                      int32_t* seg_tensor, int64_t* seg_local, int64_t capacity,
+                                      int64_t* n_segments) {
+  if (n_segments == nullptr) return fail(ZS_EINVAL, "n_segments is NULL");
+  if (capacity < 0) return fail(ZS_EINVAL, "capacity is negative");
+  Plan p;
+  zs_status st = make_plan(numels, n_tensors, dp_world, dp_rank, align_elems, &p);
+  if (st != ZS_OK) return st;
+  const HostMap m = whole_flat ? build_map(p, 0, p.flat_numel) : build_map(p, p.shard_begin, p.shard_numel);
+  const int64_t nseg = static_cast<int64_t>(m.seg_tensor.size());
+  *n_segments = nseg;
+  const int64_t k = std::min(nseg, capacity);
+  for (int64_t i = 0; i < k; ++i) {
+    if (seg_begin) seg_begin[i] = m.seg_begin[i];
+    if (seg_tensor) seg_tensor[i] = m.seg_tensor[i];
+    if (seg_local) seg_local[i] = m.seg_local[i];
+  }
+  return ok();
+}
+
+// ---------------------------------------------------------------------------- layout / state
+
+extern "C" zs_status zs_layout_create(const int64_t* numels, int32_t n_tensors, int32_t dp_world, int32_t dp_rank,
+                                      int64_t align_elems, zs_layout** out) {
+  if (out == nullptr) return fail(ZS_EINVAL, "out is NULL");
+  *out = nullptr;
+  Plan p;
+  zs_status st = make_plan(numels, n_tensors, dp_world, dp_rank, align_elems, &p);
+  if (st != ZS_OK) return st;
+  zs_layout* l = new (std::nothrow) zs_layout();
+  if (l == nullptr) return fail(ZS_ENOMEM, "host allocation of the layout failed");
+  l->plan = std::move(p);
+  hipError_t e = hipGetDevice(&l->device);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&l->num_cu, hipDeviceAttributeMultiprocessorCount, l->device);
+  if (e != hipSuccess) {
+    delete l;
+    return hip_fail(e, "querying the current device");
+  }
+  // Persistent streaming grids: enough resident workgroups per CU to keep loads in flight.
+  l->grid_stream = std::max(1, l->num_cu) * 8;
+  l->nparts = l->grid_stream;
+  const Plan& q = l->plan;
+  st = upload_map(build_map(q, q.shard_begin, q.shard_numel), &l->mem_shard, &l->map_shard);
+  if (st == ZS_OK) {
+    if (q.dp_world == 1) {
+      l->map_full = l->map_shard;
+    } else {
+      st = upload_map(build_map(q, 0, q.flat_numel), &l->mem_full, &l->map_full);
+    }
+  }
+  if (st != ZS_OK) {
+    zs_layout_destroy(l);
+    return st;
+  }
+  *out = l;
+  return ok();
+}
+
+extern "C" void zs_layout_destroy(zs_layout* l) {
+  if (l == nullptr) return;
+  if (l->mem_shard) (void)hipFree(l->mem_shard);
+  if (l->mem_full) (void)hipFree(l->mem_full);
+  delete l;
+}
+
+extern "C" zs_status zs_layout_info(const zs_layout* l, int64_t* flat_numel, int64_t* shard_begin,
+                                    int64_t* shard_numel) {
+  if (l == nullptr) return fail(ZS_EINVAL, "layout is NULL");
+  if (flat_numel) *flat_numel = l->plan.flat_numel;
+  if (shard_begin) *shard_begin = l->plan.shard_begin;
+  if (shard_numel) *shard_numel = l->plan.shard_numel;
+  return ok();
+}
+
+extern "C" zs_status zs_state_create(const zs_layout* l, const zs_state_host* init, zs_state** out) {
+  if (out == nullptr) return fail(ZS_EINVAL, "out is NULL");
+  *out = nullptr;
+  zs_status st = check_layout(l);
+  if (st != ZS_OK) return st;
+  if (init == nullptr) return fail(ZS_EINVAL, "init is NULL");
+  st = check_state_fields(init);
+  if (st != ZS_OK) return st;
+  zs_state* s = new (std::nothrow) zs_state();
+  if (s == nullptr) return fail(ZS_ENOMEM, "host allocation of the state failed");
+  s->device = l->device;
+  s->nparts = l->nparts;
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(&s->dev), sizeof(DevState));
+  if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&s->partials), sizeof(double) * std::max(1, s->nparts));
+  if (e != hipSuccess) {
+    zs_state_destroy(s);
+    return fail(ZS_ENOMEM, "hipMalloc for the state: %s", hipGetErrorString(e));
+  }
+  DevState h{};
+  h.h = *init;
+  e = hipMemcpy(s->dev, &h, sizeof h, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemset(s->partials, 0, sizeof(double) * std::max(1, s->nparts));
+  if (e != hipSuccess) {
+    zs_state_destroy(s);
+    return hip_fail(e, "initialising the state");
+  }
+  *out = s;
+  return ok();
+}
+
+extern "C" void zs_state_destroy(zs_state* s) {
+  if (s == nullptr) return;
+  if (s->dev) (void)hipFree(s->dev);
+  if (s->partials) (void)hipFree(s->partials);
+  delete s;
+}
+
+extern "C" zs_status zs_state_read(const zs_state* s, zs_state_host* out, void* stream) {
+  if (s == nullptr || out == nullptr) return fail(ZS_EINVAL, "state or out is NULL");
+  zs_status st = check_device(s->device);
+  if (st != ZS_OK) return st;
+  DevState h{};
+  hipError_t e = hipMemcpyAsync(&h, s->dev, sizeof h, hipMemcpyDeviceToHost, as_stream(stream));
+  if (e == hipSuccess) e = hipStreamSynchronize(as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "reading the state");
+  *out = h.h;
+  return ok();
+}
+
+extern "C" zs_status zs_state_write(zs_state* s, const zs_state_host* in, void* stream) {
+  if (s == nullptr || in == nullptr) return fail(ZS_EINVAL, "state or in is NULL");
+  zs_status st = check_device(s->device);
+  if (st != ZS_OK) return st;
+  st = check_state_fields(in);
+  if (st != ZS_OK) return st;
+  DevState h{};
+  h.h = *in;
+  hipError_t e = hipMemcpyAsync(s->dev, &h, sizeof h, hipMemcpyHostToDevice, as_stream(stream));
+  if (e == hipSuccess) e = hipStreamSynchronize(as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "writing the state");
+  return ok();
+}
+
+// ---------------------------------------------------------------------------- step ABI
+
+extern "C" zs_status zs_pack(const zs_layout* l, const void* src_ptrs, zs_dtype src_dtype, void* dst,
+                             zs_dtype dst_dtype, int32_t whole_flat, zs_state* fuse_check, void* stream) {
+  zs_status st = check_layout(l);
+  if (st != ZS_OK) return st;
+  if (src_ptrs == nullptr || dst == nullptr) return fail(ZS_EINVAL, "src_ptrs or dst is NULL");
+  if (!is_half_dtype(src_dtype)) return fail(ZS_EINVAL, "src_dtype must be bf16 or fp16");
+  if (dst_dtype != src_dtype && dst_dtype != ZS_FP32)
+    return fail(ZS_EUNSUPPORTED, "pack converts only to the same dtype or to fp32");
+  if (!aligned16(dst)) return fail(ZS_EINVAL, "dst must be 16-byte aligned");
+  if (fuse_check != nullptr) {
+    st = check_state(l, fuse_check);
+    if (st != ZS_OK) return st;
+    if (l->plan.dp_world != 1 || !whole_flat || dst_dtype != src_dtype)
+      return fail(ZS_EINVAL, "fuse_check needs dp_world == 1, whole_flat and a same-dtype pack");
+  }
+  const DevMap& map = whole_flat ? l->map_full : l->map_shard;
+  hipStream_t s = as_stream(stream);
+  const int grid = l->grid_stream;
+  double* parts = fuse_check ? fuse_check->partials : nullptr;
+  hipError_t e = zs::launch_pack(map, static_cast<const uint64_t*>(src_ptrs), src_dtype, dst, dst_dtype, parts,
+                                 grid, s);
+  if (e != hipSuccess) return hip_fail(e, "launching pack");
+  if (fuse_check) {
+    const int used = static_cast<int>(std::min<int64_t>(map.ntiles, grid));
+    e = zs::launch_flag_finalize(parts, used, fuse_check->dev, nullptr, zs::kFlagSet, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "launching the overflow finalize");
+  }
+  return ok();
+}
+
+extern "C" zs_status zs_unscale_check(const zs_layout* l, const void* shard, zs_dtype grad_dtype, zs_state* state,
+                                      const int32_t* ext_overflow, double* local_sumsq_out, void* stream) {
+  zs_status st = check_layout(l);
+  if (st != ZS_OK) return st;
+  st = check_state(l, state);
+  if (st != ZS_OK) return st;
+  if (shard == nullptr) return fail(ZS_EINVAL, "shard is NULL");
+  if (!is_half_dtype(grad_dtype)) return fail(ZS_EINVAL, "grad_dtype must be bf16 or fp16");
+  hipStream_t s = as_stream(stream);
+  const int64_t n = l->plan.shard_numel;
+  const int64_t ntiles = (n + zs::kTile - 1) / zs::kTile;
+  const int used = static_cast<int>(std::min<int64_t>(ntiles, l->nparts));
+  hipError_t e = zs::launch_check(shard, n, grad_dtype, state->partials, used, s);
+  if (e != hipSuccess) return hip_fail(e, "launching check");
+  e = zs::launch_flag_finalize(state->partials, used, state->dev, ext_overflow, zs::kFlagSet, local_sumsq_out, s);
+  if (e != hipSuccess) return hip_fail(e, "launching the overflow finalize");
+  return ok();
+}
+
+extern "C" zs_status zs_grad_norm(const zs_layout* l, const void* shard, zs_dtype grad_dtype, zs_state* state,
+                                  const zs_adamw_hparams* hp, const double* rank_sumsq, double* local_sumsq_out,
+                                  void* stream) {
+  zs_status st = check_layout(l);
+  if (st != ZS_OK) return st;
+  st = check_state(l, state);
+  if (st != ZS_OK) return st;
+  st = check_hparams(hp);
+  if (st != ZS_OK) return st;
+  if (l->plan.dp_world > 1 && rank_sumsq == nullptr)
+    return fail(ZS_EINVAL, "rank_sumsq is required when dp_world > 1");
+  hipStream_t s = as_stream(stream);
+  hipError_t e;
+  if (shard != nullptr) {
+    if (!is_half_dtype(grad_dtype)) return fail(ZS_EINVAL, "grad_dtype must be bf16 or fp16");
+    const int64_t n = l->plan.shard_numel;
+    const int64_t ntiles = (n + zs::kTile - 1) / zs::kTile;
+    const int used = static_cast<int>(std::min<int64_t>(ntiles, l->nparts));
+    e = zs::launch_check(shard, n, grad_dtype, state->partials, used, s);
+    if (e != hipSuccess) return hip_fail(e, "launching check");
+    e = zs::launch_flag_finalize(state->partials, used, state->dev, nullptr, zs::kFlagOr, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "launching the sum finalize");
+  }
+  e = zs::launch_norm_finalize(state->dev, rank_sumsq, l->plan.dp_world, l->plan.dp_rank, local_sumsq_out,
+                               hp->max_norm, s);
+  if (e != hipSuccess) return hip_fail(e, "launching the norm finalize");
+  return ok();
+}
+
+extern "C" zs_status zs_adamw_step(const zs_layout* l, const void* shard, zs_dtype grad_dtype, float* master,
+                                   float* m, float* v, const zs_adamw_hparams* hp, zs_state* state,
+                                   const void* param_ptrs, void* flat_param_out, zs_dtype param_dtype,
+                                   void* stream) {
+  zs_status st = check_layout(l);
+  if (st != ZS_OK) return st;
+  st = check_state(l, state);
+  if (st != ZS_OK) return st;
+  st = check_hparams(hp);
+  if (st != ZS_OK) return st;
+  if (shard == nullptr || master == nullptr || m == nullptr || v == nullptr)
+    return fail(ZS_EINVAL, "shard, master, m and v must not be NULL");
+  if (!is_half_dtype(grad_dtype) || !is_half_dtype(param_dtype))
+    return fail(ZS_EINVAL, "grad_dtype and param_dtype must be bf16 or fp16");
+  if (!aligned16(master) || !aligned16(m) || !aligned16(v)) return fail(ZS_EINVAL, "master, m, v must be 16-byte aligned");
+  if (flat_param_out != nullptr && !aligned16(flat_param_out))
+    return fail(ZS_EINVAL, "flat_param_out must be 16-byte aligned");
+  const zs::AdamwArgs a{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
+  hipError_t e = zs::launch_adamw(l->map_shard, shard, grad_dtype, master, m, v, a, state->dev,
+                                  static_cast<const uint64_t*>(param_ptrs), flat_param_out, param_dtype,
+                                  l->grid_stream, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching adamw");
+  return ok();
+}
+
+extern "C" zs_status zs_unpack(const zs_layout* l, const void* src, zs_dtype src_dtype, int32_t whole_flat,
+                               const void* dst_ptrs, zs_dtype dst_dtype, const zs_state* honour_skip,
+                               void* stream) {
+  zs_status st = check_layout(l);
+  if (st != ZS_OK) return st;
+  if (src == nullptr || dst_ptrs == nullptr) return fail(ZS_EINVAL, "src or dst_ptrs is NULL");
+  if (!is_half_dtype(dst_dtype)) return fail(ZS_EINVAL, "dst_dtype must be bf16 or fp16");
+  if (src_dtype != ZS_FP32 && src_dtype != dst_dtype)
+    return fail(ZS_EUNSUPPORTED, "unpack reads fp32 or the destination dtype");
+  if (src_dtype == ZS_FP32 && !aligned16(src)) return fail(ZS_EINVAL, "an fp32 src must be 16-byte aligned");
+  if (honour_skip != nullptr) {
+    st = check_state(l, honour_skip);
+    if (st != ZS_OK) return st;
+  }
+  const DevMap& map = whole_flat ? l->map_full : l->map_shard;
+  hipError_t e = zs::launch_unpack(map, src, src_dtype, static_cast<const uint64_t*>(dst_ptrs), dst_dtype,
+                                   honour_skip ? honour_skip->dev : nullptr, l->grid_stream, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching unpack");
+  return ok();
+}
+
+extern "C" zs_status zs_scaler_update(zs_state* state, void* stream) {
+  if (state == nullptr) return fail(ZS_EINVAL, "state is NULL");
+  zs_status st = check_device(state->device);
+  if (st != ZS_OK) return st;
+  hipError_t e = zs::launch_scaler_update(state->dev, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching the scaler update");
+  return ok();
+}
+
+extern "C" const char* zs_last_error(void) { return g_last_error.c_str(); }

@@ -1,0 +1,657 @@
+// gfx950 kernels of the per-rank ZeRO-1/2 mixed-precision optimizer step.
+//
+// All kernels stream HBM: no data is reused, so the design goals are full 16-byte
+// accesses per lane, whole-wave contiguous 1 KiB rows, enough independent loads in flight
+// per wave, and no per-tensor launches.  Tensor boundaries are resolved through a device
+// segment map (zs_internal.h): a tile of 4096 flat elements that lies inside one tensor
+// (every tile of a large tensor) takes a uniform fast path with one base pointer; tiles
+// that meet several segments look each 8-element group up by binary search over the
+// tile's few segments and fall back to 2-byte accesses only where a group straddles a
+// boundary or its tensor address is not 16-byte aligned.
+//
+// Numerics (the pages keep master weights and Adam moments in FP32 and ask for sensitive
+// reductions in higher precision - "Deep dive: Megatron", section "Precision"):
+//   - the sum of squares is accumulated in fp64 from exact fp16/bf16 -> fp64 widening;
+//   - the AdamW update is evaluated in fp64 (CDNA4 has full-rate fp64 vector ALUs and the
+//     kernel is HBM-bound) and each stored fp32 value is rounded once;
+//   - model-dtype parameters are the round-to-nearest-even cast of the new fp32 master.
+// No kernel uses atomics: every reduction has a fixed order, so results are reproducible.
+
+#include <math.h>
+
+#include "zs_internal.h"
+
+namespace zs {
+namespace {
+
+// ------------------------------------------------------------------ element conversions
+
+template <int DT>
+__device__ __forceinline__ float h2f(uint32_t b);
+template <>
+__device__ __forceinline__ float h2f<ZS_BF16>(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+template <>
+__device__ __forceinline__ float h2f<ZS_FP16>(uint32_t b) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
+}
+
+// fp32 -> 2-byte with IEEE round-to-nearest-even (gfx950 v_cvt_pk_bf16_f32 / v_cvt_f16_f32).
+template <int DT>
+__device__ __forceinline__ uint32_t f2h(float f);
+template <>
+__device__ __forceinline__ uint32_t f2h<ZS_BF16>(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+template <>
+__device__ __forceinline__ uint32_t f2h<ZS_FP16>(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+// ------------------------------------------------------------------ 8-element groups
+
+struct G16 {  // eight 2-byte values, element j in bits [16*(j&1), +16) of w[j>>1]
+  uint32_t w[4];
+  __device__ __forceinline__ uint32_t get(int j) const { return (w[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu; }
+  __device__ __forceinline__ void set(int j, uint32_t v) {
+    const int sh = (j & 1) * 16;
+    w[j >> 1] = (w[j >> 1] & ~(0xFFFFu << sh)) | ((v & 0xFFFFu) << sh);
+  }
+};
+
+__device__ __forceinline__ G16 g16_zero() { return G16{{0u, 0u, 0u, 0u}}; }
+
+__device__ __forceinline__ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+__device__ __forceinline__ G16 ld16_vec(const uint16_t* p) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  return G16{{u.x, u.y, u.z, u.w}};
+}
+__device__ __forceinline__ G16 ld16_elem(const uint16_t* p, int cnt) {
+  G16 g = g16_zero();
+  for (int j = 0; j < cnt; ++j) g.set(j, p[j]);
+  return g;
+}
+__device__ __forceinline__ void st16_vec(uint16_t* p, const G16& g) {
+  *reinterpret_cast<uint4*>(p) = make_uint4(g.w[0], g.w[1], g.w[2], g.w[3]);
+}
+__device__ __forceinline__ void st16_elem(uint16_t* p, const G16& g, int cnt) {
+  for (int j = 0; j < cnt; ++j) p[j] = static_cast<uint16_t>(g.get(j));
+}
+
+// ------------------------------------------------------------------ fixed-order reductions
+
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// Sum over the workgroup; the result is valid in thread 0.  Order: lanes by xor-butterfly,
+// then waves 0..3 in index order.
+__device__ __forceinline__ double block_sum(double x) {
+  __shared__ double red[kThreads / 64];
+  x = wave_sum(x);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  double r = 0.0;
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; ++i) r += red[i];
+  }
+  return r;
+}
+
+// ------------------------------------------------------------------ segment map walking
+
+// Largest segment index s in [lo, hi] with seg_begin[s] <= x.
+__device__ __forceinline__ int seg_find(const DevMap& mp, int lo, int hi, int64_t x) {
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (mp.seg_begin[mid] <= x)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+// Segment context of one tile.  When the whole tile lies in one segment, `base` maps a
+// range index q straight to the tensor element (base + q), or is null for padding.
+struct TileSeg {
+  int lo, hi;
+  bool uniform;
+  uint16_t* base;
+};
+
+__device__ __forceinline__ TileSeg tile_seg(const DevMap& mp, const uint64_t* ptrs, int64_t tile) {
+  TileSeg t;
+  t.lo = mp.tile_first[tile];
+  t.hi = mp.tile_first[tile + 1];
+  t.uniform = (t.lo == t.hi);
+  t.base = nullptr;
+  if (t.uniform) {
+    const int32_t tensor = mp.seg_tensor[t.lo];
+    if (tensor >= 0)
+      t.base = reinterpret_cast<uint16_t*>(ptrs[tensor]) + (mp.seg_local[t.lo] - mp.seg_begin[t.lo]);
+  }
+  return t;
+}
+
+// Pointer to the tensor element of range index q in segment s (null for padding).
+__device__ __forceinline__ uint16_t* seg_elem(const DevMap& mp, const uint64_t* ptrs, int s, int64_t q) {
+  const int32_t tensor = mp.seg_tensor[s];
+  if (tensor < 0) return nullptr;
+  return reinterpret_cast<uint16_t*>(ptrs[tensor]) + (mp.seg_local[s] + (q - mp.seg_begin[s]));
+}
+
+// Read the cnt (<= 8) elements at range indices q.. from the tensors; padding reads as 0.
+__device__ __forceinline__ G16 gather16(const DevMap& mp, const uint64_t* ptrs, const TileSeg& ts, int64_t q,
+                                        int cnt) {
+  const uint16_t* src;
+  if (ts.uniform) {
+    if (ts.base == nullptr) return g16_zero();
+    src = ts.base + q;
+  } else {
+    int s = seg_find(mp, ts.lo, ts.hi, q);
+    if (mp.seg_begin[s + 1] < q + cnt) {  // the group straddles segments
+      G16 g = g16_zero();
+      for (int j = 0; j < cnt; ++j) {
+        const int64_t e = q + j;
+        while (mp.seg_begin[s + 1] <= e) ++s;
+        const uint16_t* p = seg_elem(mp, ptrs, s, e);
+        if (p != nullptr) g.set(j, *p);
+      }
+      return g;
+    }
+    src = seg_elem(mp, ptrs, s, q);
+    if (src == nullptr) return g16_zero();
+  }
+  if (cnt == kGroup && aligned16(src)) return ld16_vec(src);
+  return ld16_elem(src, cnt);
+}
+
+// Write the cnt (<= 8) elements at range indices q.. into the tensors; padding is skipped.
+__device__ __forceinline__ void scatter16(const DevMap& mp, const uint64_t* ptrs, const TileSeg& ts, int64_t q,
+                                          int cnt, const G16& g) {
+  uint16_t* dst;
+  if (ts.uniform) {
+    if (ts.base == nullptr) return;
+    dst = ts.base + q;
+  } else {
+    int s = seg_find(mp, ts.lo, ts.hi, q);
+    if (mp.seg_begin[s + 1] < q + cnt) {
+      for (int j = 0; j < cnt; ++j) {
+        const int64_t e = q + j;
+        while (mp.seg_begin[s + 1] <= e) ++s;
+        uint16_t* p = seg_elem(mp, ptrs, s, e);
+        if (p != nullptr) *p = static_cast<uint16_t>(g.get(j));
+      }
+      return;
+    }
+    dst = seg_elem(mp, ptrs, s, q);
+    if (dst == nullptr) return;
+  }
+  if (cnt == kGroup && aligned16(dst))
+    st16_vec(dst, g);
+  else
+    st16_elem(dst, g, cnt);
+}
+
+__device__ __forceinline__ int group_count(int64_t len, int64_t q) {
+  const int64_t rem = len - q;
+  return rem >= kGroup ? kGroup : (rem > 0 ? static_cast<int>(rem) : 0);
+}
+
+template <int DT>
+__device__ __forceinline__ double sumsq8(const G16& g) {
+  double acc = 0.0;
+#pragma unroll
+  for (int j = 0; j < kGroup; ++j) {
+    const double x = static_cast<double>(h2f<DT>(g.get(j)));
+    acc += x * x;
+  }
+  return acc;
+}
+
+// ------------------------------------------------------------------ pack (+ fused check)
+
+// Gather the tensors into the flat range; padding becomes zero.  TO_F32: widen to fp32
+// (master seeding).  CHECK: also accumulate the fp64 sum of squares of the packed values
+// into partials[blockIdx.x] (a non-finite element makes that sum non-finite).
+template <int SDT, bool TO_F32, bool CHECK>
+__global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __restrict__ ptrs,
+                                                   void* __restrict__ dst, double* __restrict__ partials) {
+  double acc = 0.0;
+  for (int64_t tile = blockIdx.x; tile < mp.ntiles; tile += gridDim.x) {
+    const TileSeg ts = tile_seg(mp, ptrs, tile);
+    const int64_t base = tile * kTile;
+    G16 vals[kUnroll];
+    int cnts[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t q = base + int64_t(u * kThreads + threadIdx.x) * kGroup;
+      cnts[u] = group_count(mp.len, q);
+      vals[u] = cnts[u] > 0 ? gather16(mp, ptrs, ts, q, cnts[u]) : g16_zero();
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t q = base + int64_t(u * kThreads + threadIdx.x) * kGroup;
+      const int cnt = cnts[u];
+      if (cnt <= 0) continue;
+      if (CHECK) acc += sumsq8<SDT>(vals[u]);
+      if (TO_F32) {
+        float f[kGroup];
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) f[j] = h2f<SDT>(vals[u].get(j));
+        float* d = static_cast<float*>(dst) + q;
+        if (cnt == kGroup) {
+          reinterpret_cast<float4*>(d)[0] = make_float4(f[0], f[1], f[2], f[3]);
+          reinterpret_cast<float4*>(d)[1] = make_float4(f[4], f[5], f[6], f[7]);
+        } else {
+          for (int j = 0; j < cnt; ++j) d[j] = f[j];
+        }
+      } else {
+        uint16_t* d = static_cast<uint16_t*>(dst) + q;
+        if (cnt == kGroup)
+          st16_vec(d, vals[u]);
+        else
+          st16_elem(d, vals[u], cnt);
+      }
+    }
+  }
+  if (CHECK) {
+    const double r = block_sum(acc);
+    if (threadIdx.x == 0) partials[blockIdx.x] = r;
+  }
+}
+
+// ------------------------------------------------------------------ check (sum of squares)
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_check(const uint16_t* __restrict__ shard, int64_t n, int64_t ntiles,
+                                                    double* __restrict__ partials) {
+  const bool vec_ok = aligned16(shard);
+  double acc = 0.0;
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int64_t base = tile * kTile;
+    G16 vals[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t q = base + int64_t(u * kThreads + threadIdx.x) * kGroup;
+      const int cnt = group_count(n, q);
+      if (cnt == kGroup && vec_ok)
+        vals[u] = ld16_vec(shard + q);
+      else
+        vals[u] = ld16_elem(shard + q, cnt);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc += sumsq8<DT>(vals[u]);
+  }
+  const double r = block_sum(acc);
+  if (threadIdx.x == 0) partials[blockIdx.x] = r;
+}
+
+// ------------------------------------------------------------------ finalize kernels
+
+// One workgroup: add the block partials in a fixed order, set the overflow flag and this
+// rank's unscaled sum of squares.  Every element is finite iff the sum is finite: a finite
+// fp16/bf16 square is below 2^256 and at most 2^63 of them stay far below the fp64 range,
+// while inf or NaN anywhere propagates to the sum.
+__global__ __launch_bounds__(kThreads) void k_flag_finalize(const double* __restrict__ partials, int nparts,
+                                                            DevState* __restrict__ st,
+                                                            const int32_t* __restrict__ ext, int mode,
+                                                            double* __restrict__ local_out) {
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < nparts; i += kThreads) acc += partials[i];
+  const double raw = block_sum(acc);
+  if (threadIdx.x == 0) {
+    const bool bad = !isfinite(raw);
+    const bool other = (ext != nullptr) && (*ext != 0);
+    if (mode == kFlagSet)
+      st->h.overflow = (bad || other) ? 1 : 0;
+    else if (bad)
+      st->h.overflow = 1;
+    st->raw_sumsq = raw;
+    const double inv = 1.0 / st->h.loss_scale;  // exact: the scale is a power of two
+    const double local = (raw * inv) * inv;
+    st->h.local_sumsq = local;
+    if (local_out != nullptr) *local_out = local;
+  }
+}
+
+// One thread: global sum of squares in rank order, norm and clip coefficient.  A non-finite
+// partial from any rank (its overflow) makes the global sum non-finite and sets the flag.
+__global__ void k_norm_finalize(DevState* __restrict__ st, const double* __restrict__ rank_sumsq, int dp_world,
+                                int dp_rank, double* __restrict__ local_out, double max_norm) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  const double local = st->h.local_sumsq;
+  double ss = 0.0;
+  for (int q = 0; q < dp_world; ++q) ss += (q == dp_rank) ? local : rank_sumsq[q];
+  if (!isfinite(ss)) st->h.overflow = 1;
+  const double norm = sqrt(ss);
+  double c = 1.0;
+  if (max_norm > 0.0) {
+    const double r = max_norm / (norm + 1e-6);
+    c = (r < 1.0) ? r : 1.0;
+  }
+  st->h.sumsq = ss;
+  st->h.grad_norm = norm;
+  st->h.clip_coef = c;
+  if (local_out != nullptr) *local_out = local;
+}
+
+// One thread: commit the step in the loss scaler.
+__global__ void k_scaler_update(DevState* __restrict__ st) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  zs_state_host h = st->h;
+  if (h.overflow) {
+    h.skipped_total += 1;
+    h.growth_tracker = 0;
+    if (h.dynamic) {
+      const double halved = h.loss_scale * 0.5;
+      h.loss_scale = (halved < h.scale_floor) ? h.scale_floor : halved;
+    }
+  } else {
+    h.step_t += 1;
+    if (h.dynamic) {
+      h.growth_tracker += 1;
+      if (h.growth_tracker >= h.growth_interval) {
+        h.loss_scale *= 2.0;
+        h.growth_tracker = 0;
+      }
+    }
+  }
+  st->h = h;
+}
+
+// ------------------------------------------------------------------ AdamW + cast + scatter
+
+// Per-step scalars, evaluated in fp64 by every workgroup from the device state.
+struct StepScalars {
+  double gs, b1, omb1, b2, omb2, a, rbc2, eps, decay;
+};
+
+__device__ __forceinline__ StepScalars step_scalars(const AdamwArgs& hp, const DevState* st) {
+  StepScalars k;
+  const double t = static_cast<double>(st->h.step_t + 1);
+  k.gs = st->h.clip_coef / st->h.loss_scale;  // unscale and clip in one exact-by-construction factor
+  k.b1 = hp.beta1;
+  k.omb1 = 1.0 - hp.beta1;
+  k.b2 = hp.beta2;
+  k.omb2 = 1.0 - hp.beta2;
+  k.a = hp.lr / (1.0 - pow(hp.beta1, t));
+  k.rbc2 = 1.0 / (1.0 - pow(hp.beta2, t));
+  k.eps = hp.eps;
+  k.decay = 1.0 - hp.lr * hp.weight_decay;
+  return k;
+}
+
+// One element: returns the new (p, m, v) as fp32.
+__device__ __forceinline__ void adamw_elem(const StepScalars& k, float x, float& p, float& m, float& v) {
+#pragma clang fp contract(off)
+  const double g = static_cast<double>(x) * k.gs;
+  const float m1 = static_cast<float>(k.b1 * static_cast<double>(m) + k.omb1 * g);
+  const float v1 = static_cast<float>(k.b2 * static_cast<double>(v) + k.omb2 * (g * g));
+  const double den = sqrt(static_cast<double>(v1) * k.rbc2) + k.eps;
+  const double upd = k.a * static_cast<double>(m1) / den;
+  p = static_cast<float>(static_cast<double>(p) * k.decay - upd);
+  m = m1;
+  v = v1;
+}
+
+template <int GDT, int PDT, bool SCATTER, bool FLAT_OUT>
+__global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const uint16_t* __restrict__ shard,
+                                                    float* __restrict__ master, float* __restrict__ mom1,
+                                                    float* __restrict__ mom2, AdamwArgs hp,
+                                                    const DevState* __restrict__ st,
+                                                    const uint64_t* __restrict__ ptrs,
+                                                    uint16_t* __restrict__ flat_out) {
+  if (st->h.overflow) return;  // device-side skip: nothing changes on an overflowed step
+  const StepScalars k = step_scalars(hp, st);
+  const bool g_vec = aligned16(shard);
+  const int64_t n = mp.len;
+  for (int64_t tile = blockIdx.x; tile < mp.ntiles; tile += gridDim.x) {
+    const int64_t base = tile * kTile;
+    G16 gv[kUnroll];
+    float4 pv[kUnroll][2], mv[kUnroll][2], vv[kUnroll][2];
+    int cnts[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t q = base + int64_t(u * kThreads + threadIdx.x) * kGroup;
+      const int cnt = group_count(n, q);
+      cnts[u] = cnt;
+      if (cnt == kGroup) {
+        gv[u] = g_vec ? ld16_vec(shard + q) : ld16_elem(shard + q, kGroup);
+        pv[u][0] = reinterpret_cast<const float4*>(master + q)[0];
+        pv[u][1] = reinterpret_cast<const float4*>(master + q)[1];
+        mv[u][0] = reinterpret_cast<const float4*>(mom1 + q)[0];
+        mv[u][1] = reinterpret_cast<const float4*>(mom1 + q)[1];
+        vv[u][0] = reinterpret_cast<const float4*>(mom2 + q)[0];
+        vv[u][1] = reinterpret_cast<const float4*>(mom2 + q)[1];
+      } else if (cnt > 0) {
+        gv[u] = ld16_elem(shard + q, cnt);
+        float pt[kGroup] = {0.f}, mt[kGroup] = {0.f}, vt[kGroup] = {0.f};
+        for (int j = 0; j < cnt; ++j) {
+          pt[j] = master[q + j];
+          mt[j] = mom1[q + j];
+          vt[j] = mom2[q + j];
+        }
+        pv[u][0] = make_float4(pt[0], pt[1], pt[2], pt[3]);
+        pv[u][1] = make_float4(pt[4], pt[5], pt[6], pt[7]);
+        mv[u][0] = make_float4(mt[0], mt[1], mt[2], mt[3]);
+        mv[u][1] = make_float4(mt[4], mt[5], mt[6], mt[7]);
+        vv[u][0] = make_float4(vt[0], vt[1], vt[2], vt[3]);
+        vv[u][1] = make_float4(vt[4], vt[5], vt[6], vt[7]);
+      }
+    }
+    TileSeg ts;
+    if (SCATTER) ts = tile_seg(mp, ptrs, tile);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int cnt = cnts[u];
+      if (cnt <= 0) continue;
+      const int64_t q = base + int64_t(u * kThreads + threadIdx.x) * kGroup;
+      float p[kGroup] = {pv[u][0].x, pv[u][0].y, pv[u][0].z, pv[u][0].w,
+                         pv[u][1].x, pv[u][1].y, pv[u][1].z, pv[u][1].w};
+      float m[kGroup] = {mv[u][0].x, mv[u][0].y, mv[u][0].z, mv[u][0].w,
+                         mv[u][1].x, mv[u][1].y, mv[u][1].z, mv[u][1].w};
+      float v[kGroup] = {vv[u][0].x, vv[u][0].y, vv[u][0].z, vv[u][0].w,
+                         vv[u][1].x, vv[u][1].y, vv[u][1].z, vv[u][1].w};
+      G16 out = g16_zero();
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        adamw_elem(k, h2f<GDT>(gv[u].get(j)), p[j], m[j], v[j]);
+        out.set(j, f2h<PDT>(p[j]));
+      }
+      if (cnt == kGroup) {
+        reinterpret_cast<float4*>(master + q)[0] = make_float4(p[0], p[1], p[2], p[3]);
+        reinterpret_cast<float4*>(master + q)[1] = make_float4(p[4], p[5], p[6], p[7]);
+        reinterpret_cast<float4*>(mom1 + q)[0] = make_float4(m[0], m[1], m[2], m[3]);
+        reinterpret_cast<float4*>(mom1 + q)[1] = make_float4(m[4], m[5], m[6], m[7]);
+        reinterpret_cast<float4*>(mom2 + q)[0] = make_float4(v[0], v[1], v[2], v[3]);
+        reinterpret_cast<float4*>(mom2 + q)[1] = make_float4(v[4], v[5], v[6], v[7]);
+        if (FLAT_OUT) st16_vec(flat_out + q, out);
+      } else {
+        for (int j = 0; j < cnt; ++j) {
+          master[q + j] = p[j];
+          mom1[q + j] = m[j];
+          mom2[q + j] = v[j];
+        }
+        if (FLAT_OUT) st16_elem(flat_out + q, out, cnt);
+      }
+      if (SCATTER) scatter16(mp, ptrs, ts, q, cnt, out);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ unpack (scatter-back)
+
+// SRC_F32: the source is the fp32 master (cast RNE to DDT); otherwise a DDT flat buffer
+// (bit copy).  A set overflow flag in `skip` makes the kernel a no-op.
+template <bool SRC_F32, int DDT>
+__global__ __launch_bounds__(kThreads) void k_unpack(DevMap mp, const void* __restrict__ src,
+                                                     const DevState* __restrict__ skip,
+                                                     const uint64_t* __restrict__ ptrs) {
+  if (skip != nullptr && skip->h.overflow) return;
+  const bool vec_ok = aligned16(src);
+  for (int64_t tile = blockIdx.x; tile < mp.ntiles; tile += gridDim.x) {
+    const TileSeg ts = tile_seg(mp, ptrs, tile);
+    const int64_t base = tile * kTile;
+    G16 vals[kUnroll];
+    int cnts[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t q = base + int64_t(u * kThreads + threadIdx.x) * kGroup;
+      const int cnt = group_count(mp.len, q);
+      cnts[u] = cnt;
+      vals[u] = g16_zero();
+      if (cnt <= 0) continue;
+      if (SRC_F32) {
+        const float* s = static_cast<const float*>(src) + q;
+        float f[kGroup] = {0.f};
+        if (cnt == kGroup) {
+          const float4 a = reinterpret_cast<const float4*>(s)[0];
+          const float4 b = reinterpret_cast<const float4*>(s)[1];
+          f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+          f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+        } else {
+          for (int j = 0; j < cnt; ++j) f[j] = s[j];
+        }
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) vals[u].set(j, f2h<DDT>(f[j]));
+      } else {
+        const uint16_t* s = static_cast<const uint16_t*>(src) + q;
+        vals[u] = (cnt == kGroup && vec_ok) ? ld16_vec(s) : ld16_elem(s, cnt);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (cnts[u] <= 0) continue;
+      const int64_t q = base + int64_t(u * kThreads + threadIdx.x) * kGroup;
+      scatter16(mp, ptrs, ts, q, cnts[u], vals[u]);
+    }
+  }
+}
+
+inline int clamp_grid(int64_t ntiles, int grid) {
+  return static_cast<int>(ntiles < grid ? ntiles : grid);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ launchers
+
+hipError_t launch_pack(const DevMap& map, const uint64_t* src_ptrs, int src_dt, void* dst, int dst_dt,
+                       double* partials, int grid, hipStream_t s) {
+  if (map.ntiles == 0 || grid <= 0) return hipSuccess;
+  const int g = clamp_grid(map.ntiles, grid);
+  const dim3 G(g), B(kThreads);
+  const bool f32 = (dst_dt == ZS_FP32);
+  const bool chk = (partials != nullptr);
+  if (src_dt == ZS_BF16) {
+    if (f32)
+      hipLaunchKernelGGL((k_pack<ZS_BF16, true, false>), G, B, 0, s, map, src_ptrs, dst, partials);
+    else if (chk)
+      hipLaunchKernelGGL((k_pack<ZS_BF16, false, true>), G, B, 0, s, map, src_ptrs, dst, partials);
+    else
+      hipLaunchKernelGGL((k_pack<ZS_BF16, false, false>), G, B, 0, s, map, src_ptrs, dst, partials);
+  } else {
+    if (f32)
+      hipLaunchKernelGGL((k_pack<ZS_FP16, true, false>), G, B, 0, s, map, src_ptrs, dst, partials);
+    else if (chk)
+      hipLaunchKernelGGL((k_pack<ZS_FP16, false, true>), G, B, 0, s, map, src_ptrs, dst, partials);
+    else
+      hipLaunchKernelGGL((k_pack<ZS_FP16, false, false>), G, B, 0, s, map, src_ptrs, dst, partials);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_check(const void* shard, int64_t n, int dt, double* partials, int grid, hipStream_t s) {
+  const int64_t ntiles = (n + kTile - 1) / kTile;
+  if (ntiles == 0 || grid <= 0) return hipSuccess;
+  const int g = clamp_grid(ntiles, grid);
+  const uint16_t* p = static_cast<const uint16_t*>(shard);
+  if (dt == ZS_BF16)
+    hipLaunchKernelGGL((k_check<ZS_BF16>), dim3(g), dim3(kThreads), 0, s, p, n, ntiles, partials);
+  else
+    hipLaunchKernelGGL((k_check<ZS_FP16>), dim3(g), dim3(kThreads), 0, s, p, n, ntiles, partials);
+  return hipGetLastError();
+}
+
+hipError_t launch_flag_finalize(const double* partials, int nparts, DevState* st, const int32_t* ext, int mode,
+                                double* local_out, hipStream_t s) {
+  hipLaunchKernelGGL(k_flag_finalize, dim3(1), dim3(kThreads), 0, s, partials, nparts, st, ext, mode, local_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_finalize(DevState* st, const double* rank_sumsq, int dp_world, int dp_rank,
+                                double* local_out, double max_norm, hipStream_t s) {
+  hipLaunchKernelGGL(k_norm_finalize, dim3(1), dim3(64), 0, s, st, rank_sumsq, dp_world, dp_rank, local_out,
+                     max_norm);
+  return hipGetLastError();
+}
+
+hipError_t launch_scaler_update(DevState* st, hipStream_t s) {
+  hipLaunchKernelGGL(k_scaler_update, dim3(1), dim3(64), 0, s, st);
+  return hipGetLastError();
+}
+
+template <int GDT, int PDT>
+static void adamw_dispatch(const dim3& G, hipStream_t s, const DevMap& map, const uint16_t* shard, float* master,
+                           float* m, float* v, const AdamwArgs& hp, const DevState* st, const uint64_t* ptrs,
+                           uint16_t* flat_out) {
+  const dim3 B(kThreads);
+  if (ptrs != nullptr && flat_out != nullptr)
+    hipLaunchKernelGGL((k_adamw<GDT, PDT, true, true>), G, B, 0, s, map, shard, master, m, v, hp, st, ptrs,
+                       flat_out);
+  else if (ptrs != nullptr)
+    hipLaunchKernelGGL((k_adamw<GDT, PDT, true, false>), G, B, 0, s, map, shard, master, m, v, hp, st, ptrs,
+                       flat_out);
+  else if (flat_out != nullptr)
+    hipLaunchKernelGGL((k_adamw<GDT, PDT, false, true>), G, B, 0, s, map, shard, master, m, v, hp, st, ptrs,
+                       flat_out);
+  else
+    hipLaunchKernelGGL((k_adamw<GDT, PDT, false, false>), G, B, 0, s, map, shard, master, m, v, hp, st, ptrs,
+                       flat_out);
+}
+
+hipError_t launch_adamw(const DevMap& map, const void* shard, int grad_dt, float* master, float* m, float* v,
+                        const AdamwArgs& hp, const DevState* st, const uint64_t* param_ptrs, void* flat_out,
+                        int param_dt, int grid, hipStream_t s) {
+  if (map.ntiles == 0 || grid <= 0) return hipSuccess;
+  const dim3 G(clamp_grid(map.ntiles, grid));
+  const uint16_t* g = static_cast<const uint16_t*>(shard);
+  uint16_t* fo = static_cast<uint16_t*>(flat_out);
+  if (grad_dt == ZS_BF16 && param_dt == ZS_BF16)
+    adamw_dispatch<ZS_BF16, ZS_BF16>(G, s, map, g, master, m, v, hp, st, param_ptrs, fo);
+  else if (grad_dt == ZS_FP16 && param_dt == ZS_FP16)
+    adamw_dispatch<ZS_FP16, ZS_FP16>(G, s, map, g, master, m, v, hp, st, param_ptrs, fo);
+  else if (grad_dt == ZS_BF16)
+    adamw_dispatch<ZS_BF16, ZS_FP16>(G, s, map, g, master, m, v, hp, st, param_ptrs, fo);
+  else
+    adamw_dispatch<ZS_FP16, ZS_BF16>(G, s, map, g, master, m, v, hp, st, param_ptrs, fo);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack(const DevMap& map, const void* src, int src_dt, const uint64_t* dst_ptrs, int dst_dt,
+                         const DevState* skip, int grid, hipStream_t s) {
+  if (map.ntiles == 0 || grid <= 0) return hipSuccess;
+  const dim3 G(clamp_grid(map.ntiles, grid)), B(kThreads);
+  const bool f32 = (src_dt == ZS_FP32);
+  if (dst_dt == ZS_BF16) {
+    if (f32)
+      hipLaunchKernelGGL((k_unpack<true, ZS_BF16>), G, B, 0, s, map, src, skip, dst_ptrs);
+    else
+      hipLaunchKernelGGL((k_unpack<false, ZS_BF16>), G, B, 0, s, map, src, skip, dst_ptrs);
+  } else {
+    if (f32)
+      hipLaunchKernelGGL((k_unpack<true, ZS_FP16>), G, B, 0, s, map, src, skip, dst_ptrs);
+    else
+      hipLaunchKernelGGL((k_unpack<false, ZS_FP16>), G, B, 0, s, map, src, skip, dst_ptrs);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace zs

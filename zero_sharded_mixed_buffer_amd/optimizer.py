@@ -1,0 +1,130 @@
+"""A rank-level optimizer object over the C ABI.
+
+ZeroShardedAdamW owns the buffers of one data-parallel rank (flat gradient
+buffer, fp32 master / m / v of its shard, device pointer tables) and issues the
+step as a fixed sequence of ABI calls on one stream:
+
+    zs_pack -> zs_unscale_check -> zs_grad_norm -> zs_adamw_step -> zs_scaler_update
+    (dp_world == 1: the check is fused into the pack pass)
+
+It makes no decisions of its own and never synchronises; the skip on overflow,
+the clip and the scaler all happen on the device.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _abi as A
+
+
+def pointer_table(tensors, device):
+    """Device int64 array of the tensors' data pointers (the ABI's pointer tables)."""
+    for t in tensors:
+        if t.numel() and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
+
+
+class ZeroShardedAdamW:
+    def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, max_norm=1.0,
+                 dp_world=1, dp_rank=0, align=1, dynamic_loss_scale=None, init_scale=None, scale_floor=1.0,
+                 growth_interval=1000, grad_dtype=None):
+        params = list(params)
+        if not params:
+            raise ValueError("empty parameter list")
+        self.device = params[0].device
+        self.param_dtype = params[0].dtype
+        self.grad_dtype = grad_dtype or self.param_dtype
+        if dynamic_loss_scale is None:
+            dynamic_loss_scale = self.grad_dtype == torch.float16
+        if init_scale is None:
+            init_scale = 2.0 ** 16 if dynamic_loss_scale else 1.0
+        self.params = params
+        self.numels = [p.numel() for p in params]
+        self.hp = A.hparams(lr, betas[0], betas[1], eps, weight_decay, max_norm)
+        self.dp_world, self.dp_rank = dp_world, dp_rank
+        with torch.cuda.device(self.device):
+            self.layout = A.zs_layout_create(self.numels, dp_world, dp_rank, align)
+            self.flat_numel, self.shard_begin, self.shard_numel = A.zs_layout_info(self.layout)
+            self.state = A.zs_state_create(self.layout, A.state_host(init_scale, scale_floor, dynamic_loss_scale,
+                                                                     growth_interval))
+        dev = self.device
+        self.flat = torch.zeros(self.flat_numel, dtype=self.grad_dtype, device=dev)
+        self.master = torch.empty(self.shard_numel, dtype=torch.float32, device=dev)
+        self.m = torch.zeros(self.shard_numel, dtype=torch.float32, device=dev)
+        self.v = torch.zeros(self.shard_numel, dtype=torch.float32, device=dev)
+        self.param_ptrs = pointer_table(params, dev)
+        self.local_sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
+        self._grad_key = None
+        self._grad_ptrs = None
+        A.zs_pack(self.layout, self.param_ptrs, self.param_dtype, self.master, torch.float32, whole_flat=False)
+
+    @property
+    def shard(self):
+        """This rank's partition of the flat gradient buffer (a view)."""
+        return self.flat[self.shard_begin:self.shard_begin + self.shard_numel]
+
+    def _grad_table(self, grads):
+        key = tuple(g.data_ptr() for g in grads)
+        if key != self._grad_key:
+            if len(grads) != len(self.numels) or any(g.numel() != n for g, n in zip(grads, self.numels)):
+                raise ValueError("gradients must match the parameter list")
+            self._grad_ptrs = pointer_table(grads, self.device)
+            self._grad_key = key
+        return self._grad_ptrs
+
+    def pack(self, grads, stream=None):
+        """Pack the per-parameter gradients into the flat buffer (fused with the overflow check
+        and sum of squares when there is one rank)."""
+        fuse = self.state if self.dp_world == 1 else None
+        A.zs_pack(self.layout, self._grad_table(grads), self.grad_dtype, self.flat, self.grad_dtype,
+                  whole_flat=True, fuse_check=fuse, stream=stream)
+
+    def check(self, ext_overflow=None, local_sumsq_out=None, stream=None):
+        """Overflow flag and local sum of squares of the shard (after the reduce-scatter);
+        local_sumsq_out (a device double) receives the value to exchange with the other ranks."""
+        A.zs_unscale_check(self.layout, self.shard, self.grad_dtype, self.state, ext_overflow,
+                           local_sumsq_out if local_sumsq_out is not None else self.local_sumsq, stream=stream)
+
+    def norm(self, rank_sumsq=None, stream=None):
+        """Global norm and clip coefficient; rank_sumsq: device array of every rank's local sum
+        of squares in rank order (required when dp_world > 1)."""
+        A.zs_grad_norm(self.layout, None, self.grad_dtype, self.state, self.hp, rank_sumsq, None, stream=stream)
+
+    def update(self, scatter=True, flat_param_out=None, stream=None):
+        A.zs_adamw_step(self.layout, self.shard, self.grad_dtype, self.master, self.m, self.v, self.hp, self.state,
+                        self.param_ptrs if scatter else None, flat_param_out, self.param_dtype, stream=stream)
+        A.zs_scaler_update(self.state, stream=stream)
+
+    def step(self, grads, stream=None):
+        """Whole single-rank step (dp_world == 1)."""
+        if self.dp_world != 1:
+            raise ValueError("step() is the single-rank sequence; call pack/check/norm/update with the "
+                             "other ranks' flag and partial sums for dp_world > 1")
+        self.pack(grads, stream)
+        self.norm(stream=stream)
+        self.update(stream=stream)
+
+    def read_state(self, stream=None):
+        return A.zs_state_read(self.state, stream).as_dict()
+
+    def write_state(self, values: dict, stream=None):
+        s = A.zs_state_read(self.state, stream)
+        for k, v in values.items():
+            setattr(s, k, v)
+        A.zs_state_write(self.state, s, stream)
+
+    def close(self):
+        if getattr(self, "state", None):
+            A.zs_state_destroy(self.state)
+            self.state = None
+        if getattr(self, "layout", None):
+            A.zs_layout_destroy(self.layout)
+            self.layout = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
