@@ -140,9 +140,15 @@ def run_parity(wl, steps=None, align=None, dp_rank=None, check_every_step=True):
                     else:
                         Z.zs_unscale_check(others[q][0], shard_q, dt, others[q][1], None, exchange[q:q + 1])
                 opt.norm(rank_sumsq=exchange)
+                # The virtual ranks run the same protocol, so their scalers stay in step.
+                for lq, sq in others.values():
+                    Z.zs_grad_norm(lq, None, dt, sq, opt.hp, exchange, None)
+                    Z.zs_scaler_update(sq)
             st_before = opt.read_state()
             opt.update()
             st = opt.read_state()
+            for lq, sq in others.values():
+                assert Z.zs_state_read(sq).loss_scale == st["loss_scale"]
 
             # ---- oracle
             flat_ref = O.pack(grads_cpu, lay)

@@ -139,6 +139,10 @@ def _edge_case(numels, dtype, dp_world=1, dp_rank=0, align=1, steps=3, zero_grad
                         Z.zs_unscale_check(others[q], opt.flat[q * S:(q + 1) * S], dtype, ostates[q], None,
                                            exch[q:q + 1])
                 opt.norm(rank_sumsq=exch)
+                for q in range(dp_world):
+                    if q != dp_rank:
+                        Z.zs_grad_norm(others[q], None, dtype, ostates[q], opt.hp, exch, None)
+                        Z.zs_scaler_update(ostates[q])
             opt.update()
             flat_ref = O.pack([x.cpu() for x in grads], ref.layout)
             other = [O.sumsq_unscaled(flat_ref[q * S:(q + 1) * S], ref.scaler.loss_scale) for q in range(dp_world)]
