@@ -52,6 +52,31 @@ def cpu_baseline(wl, n_elems, steps):
                       f"step time ({per_step:.2f} s)"}
 
 
+def ceilings(torch, gib=4, reps=5):
+    """Practical HBM yardsticks on the same GPU: torch's device-to-device copy (read + write
+    of `gib` GiB each) and a triad a = b + 2c over three `gib` GiB fp32 buffers."""
+    n = gib * (1 << 30) // 4
+    a = torch.empty(n, dtype=torch.float32, device="cuda")
+    b = torch.ones(n, dtype=torch.float32, device="cuda")
+    c = torch.ones(n, dtype=torch.float32, device="cuda")
+    res = {}
+    for name, fn, nbytes in (("copy", lambda: a.copy_(b), 2 * 4 * n),
+                             ("triad", lambda: torch.add(b, c, alpha=2.0, out=a), 3 * 4 * n)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name] = {"gbps": nbytes / (ms * 1e-3) / 1e9, "ms": ms, "bytes": nbytes}
+    del a, b, c
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -61,6 +86,8 @@ def main():
     ap.add_argument("--cpu-baseline-elems", type=int, default=1 << 27)
     ap.add_argument("--cpu-baseline-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="also time a device-to-device copy and a triad (torch kernels) as bandwidth yardsticks")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -163,6 +190,9 @@ def main():
     opt.close()
     del params, grads, opt
     torch.cuda.empty_cache()
+    if args.ceilings:
+        out["ceilings"] = ceilings(torch)
+        log(f"ceilings: {out['ceilings']}")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_baseline_elems, args.cpu_baseline_steps)

@@ -84,6 +84,8 @@ zs_status make_plan(const int64_t* numels, int32_t n, int32_t dp_world, int32_t 
     if (pos < 0) return fail(ZS_EINVAL, "total size overflows int64");
   }
   p.flat_numel = round_up(pos, int64_t(dp_world) * align);
+  if (p.flat_numel / zs::kPackBlock >= (int64_t(1) << 31))
+    return fail(ZS_EINVAL, "flat buffer of %lld elements exceeds the supported 2^42", (long long)p.flat_numel);
   p.shard_numel = p.flat_numel / dp_world;
   p.shard_begin = int64_t(dp_rank) * p.shard_numel;
   *out = std::move(p);
@@ -212,14 +214,13 @@ struct zs_layout {
   void* mem_full = nullptr;  // null when the shard is the whole buffer (dp_world == 1)
   DevMap map_shard{};
   DevMap map_full{};
-  int grid_stream = 0;  // workgroups of the persistent streaming kernels
-  int nparts = 0;       // partial-sum slots = workgroups of the reduction passes
+  int64_t nparts = 0;  // partial-sum slots: workgroups of the largest pack / check pass
 };
 
 struct zs_state {
   DevState* dev = nullptr;
-  double* partials = nullptr;
-  int nparts = 0;
+  double* partials = nullptr;  // nparts slots, then kLevel2 second-level slots
+  int64_t nparts = 0;
   int device = 0;
 };
 
@@ -303,10 +304,8 @@ extern "C" zs_status zs_layout_create(const int64_t* numels, int32_t n_tensors, 
     delete l;
     return hip_fail(e, "querying the current device");
   }
-  // Persistent streaming grids: enough resident workgroups per CU to keep loads in flight.
-  l->grid_stream = std::max(1, l->num_cu) * 8;
-  l->nparts = l->grid_stream;
   const Plan& q = l->plan;
+  l->nparts = std::max<int64_t>(1, std::max(zs::reduction_blocks(q.flat_numel), zs::reduction_blocks(q.shard_numel)));
   st = upload_map(build_map(q, q.shard_begin, q.shard_numel), &l->mem_shard, &l->map_shard);
   if (st == ZS_OK) {
     if (q.dp_world == 1) {
@@ -352,7 +351,8 @@ extern "C" zs_status zs_state_create(const zs_layout* l, const zs_state_host* in
   s->device = l->device;
   s->nparts = l->nparts;
   hipError_t e = hipMalloc(reinterpret_cast<void**>(&s->dev), sizeof(DevState));
-  if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&s->partials), sizeof(double) * std::max(1, s->nparts));
+  const size_t part_bytes = sizeof(double) * static_cast<size_t>(s->nparts + zs::kLevel2);
+  if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&s->partials), part_bytes);
   if (e != hipSuccess) {
     zs_state_destroy(s);
     return fail(ZS_ENOMEM, "hipMalloc for the state: %s", hipGetErrorString(e));
@@ -360,7 +360,7 @@ extern "C" zs_status zs_state_create(const zs_layout* l, const zs_state_host* in
   DevState h{};
   h.h = *init;
   e = hipMemcpy(s->dev, &h, sizeof h, hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemset(s->partials, 0, sizeof(double) * std::max(1, s->nparts));
+  if (e == hipSuccess) e = hipMemset(s->partials, 0, part_bytes);
   if (e != hipSuccess) {
     zs_state_destroy(s);
     return hip_fail(e, "initialising the state");
@@ -421,14 +421,13 @@ extern "C" zs_status zs_pack(const zs_layout* l, const void* src_ptrs, zs_dtype 
   }
   const DevMap& map = whole_flat ? l->map_full : l->map_shard;
   hipStream_t s = as_stream(stream);
-  const int grid = l->grid_stream;
   double* parts = fuse_check ? fuse_check->partials : nullptr;
-  hipError_t e = zs::launch_pack(map, static_cast<const uint64_t*>(src_ptrs), src_dtype, dst, dst_dtype, parts,
-                                 grid, s);
+  hipError_t e = zs::launch_pack(map, static_cast<const uint64_t*>(src_ptrs), src_dtype, dst, dst_dtype, parts, s);
   if (e != hipSuccess) return hip_fail(e, "launching pack");
   if (fuse_check) {
-    const int used = static_cast<int>(std::min<int64_t>(map.ntiles, grid));
-    e = zs::launch_flag_finalize(parts, used, fuse_check->dev, nullptr, zs::kFlagSet, nullptr, s);
+    const int64_t used = zs::reduction_blocks(map.len);
+    e = zs::launch_reduce_finalize(parts, used, parts + fuse_check->nparts, fuse_check->dev, nullptr, zs::kFlagSet,
+                                   nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "launching the overflow finalize");
   }
   return ok();
@@ -444,11 +443,10 @@ extern "C" zs_status zs_unscale_check(const zs_layout* l, const void* shard, zs_
   if (!is_half_dtype(grad_dtype)) return fail(ZS_EINVAL, "grad_dtype must be bf16 or fp16");
   hipStream_t s = as_stream(stream);
   const int64_t n = l->plan.shard_numel;
-  const int64_t ntiles = (n + zs::kTile - 1) / zs::kTile;
-  const int used = static_cast<int>(std::min<int64_t>(ntiles, l->nparts));
-  hipError_t e = zs::launch_check(shard, n, grad_dtype, state->partials, used, s);
+  hipError_t e = zs::launch_check(shard, n, grad_dtype, state->partials, s);
   if (e != hipSuccess) return hip_fail(e, "launching check");
-  e = zs::launch_flag_finalize(state->partials, used, state->dev, ext_overflow, zs::kFlagSet, local_sumsq_out, s);
+  e = zs::launch_reduce_finalize(state->partials, zs::reduction_blocks(n), state->partials + state->nparts,
+                                 state->dev, ext_overflow, zs::kFlagSet, local_sumsq_out, s);
   if (e != hipSuccess) return hip_fail(e, "launching the overflow finalize");
   return ok();
 }
@@ -469,11 +467,10 @@ extern "C" zs_status zs_grad_norm(const zs_layout* l, const void* shard, zs_dtyp
   if (shard != nullptr) {
     if (!is_half_dtype(grad_dtype)) return fail(ZS_EINVAL, "grad_dtype must be bf16 or fp16");
     const int64_t n = l->plan.shard_numel;
-    const int64_t ntiles = (n + zs::kTile - 1) / zs::kTile;
-    const int used = static_cast<int>(std::min<int64_t>(ntiles, l->nparts));
-    e = zs::launch_check(shard, n, grad_dtype, state->partials, used, s);
+    e = zs::launch_check(shard, n, grad_dtype, state->partials, s);
     if (e != hipSuccess) return hip_fail(e, "launching check");
-    e = zs::launch_flag_finalize(state->partials, used, state->dev, nullptr, zs::kFlagOr, nullptr, s);
+    e = zs::launch_reduce_finalize(state->partials, zs::reduction_blocks(n), state->partials + state->nparts,
+                                   state->dev, nullptr, zs::kFlagOr, nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "launching the sum finalize");
   }
   e = zs::launch_norm_finalize(state->dev, rank_sumsq, l->plan.dp_world, l->plan.dp_rank, local_sumsq_out,
@@ -502,7 +499,7 @@ extern "C" zs_status zs_adamw_step(const zs_layout* l, const void* shard, zs_dty
   const zs::AdamwArgs a{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
   hipError_t e = zs::launch_adamw(l->map_shard, shard, grad_dtype, master, m, v, a, state->dev,
                                   static_cast<const uint64_t*>(param_ptrs), flat_param_out, param_dtype,
-                                  l->grid_stream, as_stream(stream));
+                                  as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "launching adamw");
   return ok();
 }
@@ -523,7 +520,7 @@ extern "C" zs_status zs_unpack(const zs_layout* l, const void* src, zs_dtype src
   }
   const DevMap& map = whole_flat ? l->map_full : l->map_shard;
   hipError_t e = zs::launch_unpack(map, src, src_dtype, static_cast<const uint64_t*>(dst_ptrs), dst_dtype,
-                                   honour_skip ? honour_skip->dev : nullptr, l->grid_stream, as_stream(stream));
+                                   honour_skip ? honour_skip->dev : nullptr, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "launching unpack");
   return ok();
 }

@@ -9,14 +9,22 @@
 
 namespace zs {
 
-// Streaming-kernel geometry: 256 threads (four wave64s) per workgroup, each thread owns a
-// group of 8 consecutive flat elements (one 16-byte load of 2-byte data, two of fp32) and
-// kUnroll groups per tile, so a tile is 4096 flat elements and a wave touches 1 KiB of
-// 2-byte data per group row.
+// Streaming-kernel geometry.  Every streaming kernel launches one workgroup of 256 threads
+// (four wave64s) per unit of work - no persistent grid-stride loops, which measured slower
+// on MI355X for these pure streams.  A thread owns groups of 8 consecutive flat elements
+// (one 16-byte access of 2-byte data, two of fp32).  The AdamW and unpack kernels take
+// kUnroll groups per thread, i.e. one 4096-element tile per workgroup; the pack and check
+// passes take one group per thread, i.e. half a tile (kPackBlock) per workgroup, and leave
+// one fp64 partial sum per workgroup.
 constexpr int kThreads = 256;
 constexpr int kGroup = 8;
 constexpr int kUnroll = 2;
 constexpr int64_t kTile = int64_t(kThreads) * kGroup * kUnroll;
+constexpr int64_t kPackBlock = int64_t(kThreads) * kGroup;
+constexpr int kLevel2 = 1024;  // first-level partial-sum workgroups of the two-level reduction
+
+// Workgroups (and partial sums) of a pack or check pass over len elements.
+inline int64_t reduction_blocks(int64_t len) { return (len + kPackBlock - 1) / kPackBlock; }
 
 // Segment map of one flat range (a rank's shard or the whole buffer), in device memory.
 // Segment i covers range-relative [seg_begin[i], seg_begin[i+1]) and lies inside tensor
@@ -49,18 +57,21 @@ struct AdamwArgs {
 enum FlagMode : int { kFlagSet = 0, kFlagOr = 1 };
 
 // Launchers (zs_kernels.hip).  Each enqueues on `s` and returns the launch status.
+// launch_pack / launch_check write reduction_blocks(len) partial sums when partials != null;
+// launch_reduce_finalize folds n partials (via level2 scratch of kLevel2 doubles when n is
+// large) into the state's flag and local sum of squares.
 hipError_t launch_pack(const DevMap& map, const uint64_t* src_ptrs, int src_dt, void* dst, int dst_dt,
-                       double* partials, int grid, hipStream_t s);
-hipError_t launch_check(const void* shard, int64_t n, int dt, double* partials, int grid, hipStream_t s);
-hipError_t launch_flag_finalize(const double* partials, int nparts, DevState* st, const int32_t* ext, int mode,
-                                double* local_out, hipStream_t s);
+                       double* partials, hipStream_t s);
+hipError_t launch_check(const void* shard, int64_t n, int dt, double* partials, hipStream_t s);
+hipError_t launch_reduce_finalize(const double* partials, int64_t nparts, double* level2, DevState* st,
+                                  const int32_t* ext, int mode, double* local_out, hipStream_t s);
 hipError_t launch_norm_finalize(DevState* st, const double* rank_sumsq, int dp_world, int dp_rank,
                                 double* local_out, double max_norm, hipStream_t s);
 hipError_t launch_adamw(const DevMap& map, const void* shard, int grad_dt, float* master, float* m, float* v,
                         const AdamwArgs& hp, const DevState* st, const uint64_t* param_ptrs, void* flat_out,
-                        int param_dt, int grid, hipStream_t s);
+                        int param_dt, hipStream_t s);
 hipError_t launch_unpack(const DevMap& map, const void* src, int src_dt, const uint64_t* dst_ptrs, int dst_dt,
-                         const DevState* skip, int grid, hipStream_t s);
+                         const DevState* skip, hipStream_t s);
 hipError_t launch_scaler_update(DevState* st, hipStream_t s);
 
 }  // namespace zs

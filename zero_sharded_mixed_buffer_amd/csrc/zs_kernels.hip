@@ -2,7 +2,9 @@
 //
 // All kernels stream HBM: no data is reused, so the design goals are full 16-byte
 // accesses per lane, whole-wave contiguous 1 KiB rows, enough independent loads in flight
-// per wave, and no per-tensor launches.  Tensor boundaries are resolved through a device
+// per wave, one short-lived workgroup per unit of work (the hardware dispatcher keeps
+// every CU full and the tail short), non-temporal stores for data nobody re-reads soon,
+// and no per-tensor launches.  Tensor boundaries are resolved through a device
 // segment map (zs_internal.h): a tile of 4096 flat elements that lies inside one tensor
 // (every tile of a large tensor) takes a uniform fast path with one base pointer; tiles
 // that meet several segments look each 8-element group up by binary search over the
@@ -64,8 +66,19 @@ __device__ __forceinline__ G16 g16_zero() { return G16{{0u, 0u, 0u, 0u}}; }
 
 __device__ __forceinline__ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// 16-byte accesses of the streamed arrays; every bulk load and store goes through these.
+// Stores are non-temporal: the written streams are read again only by the next pass or
+// the next step, long after they would have left the caches.
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4u ld_v4u(const void* p) { return *reinterpret_cast<const v4u*>(p); }
+__device__ __forceinline__ void st_v4u(void* p, v4u x) { __builtin_nontemporal_store(x, reinterpret_cast<v4u*>(p)); }
+__device__ __forceinline__ v4f ld_v4f(const float* p) { return *reinterpret_cast<const v4f*>(p); }
+__device__ __forceinline__ void st_v4f(float* p, v4f x) { __builtin_nontemporal_store(x, reinterpret_cast<v4f*>(p)); }
+
 __device__ __forceinline__ G16 ld16_vec(const uint16_t* p) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const v4u u = ld_v4u(p);
   return G16{{u.x, u.y, u.z, u.w}};
 }
 __device__ __forceinline__ G16 ld16_elem(const uint16_t* p, int cnt) {
@@ -74,7 +87,7 @@ __device__ __forceinline__ G16 ld16_elem(const uint16_t* p, int cnt) {
   return g;
 }
 __device__ __forceinline__ void st16_vec(uint16_t* p, const G16& g) {
-  *reinterpret_cast<uint4*>(p) = make_uint4(g.w[0], g.w[1], g.w[2], g.w[3]);
+  st_v4u(p, v4u{g.w[0], g.w[1], g.w[2], g.w[3]});
 }
 __device__ __forceinline__ void st16_elem(uint16_t* p, const G16& g, int cnt) {
   for (int j = 0; j < cnt; ++j) p[j] = static_cast<uint16_t>(g.get(j));
@@ -217,48 +230,38 @@ __device__ __forceinline__ double sumsq8(const G16& g) {
 
 // ------------------------------------------------------------------ pack (+ fused check)
 
-// Gather the tensors into the flat range; padding becomes zero.  TO_F32: widen to fp32
-// (master seeding).  CHECK: also accumulate the fp64 sum of squares of the packed values
-// into partials[blockIdx.x] (a non-finite element makes that sum non-finite).
+// Gather the tensors into the flat range; padding becomes zero.  One group per thread, one
+// kPackBlock-element block per workgroup.  TO_F32: widen to fp32 (master seeding).  CHECK:
+// also write the fp64 sum of squares of this block's packed values to partials[blockIdx.x]
+// (a non-finite element makes that sum non-finite).
 template <int SDT, bool TO_F32, bool CHECK>
 __global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __restrict__ ptrs,
                                                    void* __restrict__ dst, double* __restrict__ partials) {
+  const int64_t block_base = int64_t(blockIdx.x) * kPackBlock;
+  const TileSeg ts = tile_seg(mp, ptrs, block_base / kTile);
+  const int64_t q = block_base + int64_t(threadIdx.x) * kGroup;
+  const int cnt = group_count(mp.len, q);
   double acc = 0.0;
-  for (int64_t tile = blockIdx.x; tile < mp.ntiles; tile += gridDim.x) {
-    const TileSeg ts = tile_seg(mp, ptrs, tile);
-    const int64_t base = tile * kTile;
-    G16 vals[kUnroll];
-    int cnts[kUnroll];
+  if (cnt > 0) {
+    const G16 vals = gather16(mp, ptrs, ts, q, cnt);
+    if (CHECK) acc = sumsq8<SDT>(vals);
+    if (TO_F32) {
+      float f[kGroup];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t q = base + int64_t(u * kThreads + threadIdx.x) * kGroup;
-      cnts[u] = group_count(mp.len, q);
-      vals[u] = cnts[u] > 0 ? gather16(mp, ptrs, ts, q, cnts[u]) : g16_zero();
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t q = base + int64_t(u * kThreads + threadIdx.x) * kGroup;
-      const int cnt = cnts[u];
-      if (cnt <= 0) continue;
-      if (CHECK) acc += sumsq8<SDT>(vals[u]);
-      if (TO_F32) {
-        float f[kGroup];
-#pragma unroll
-        for (int j = 0; j < kGroup; ++j) f[j] = h2f<SDT>(vals[u].get(j));
-        float* d = static_cast<float*>(dst) + q;
-        if (cnt == kGroup) {
-          reinterpret_cast<float4*>(d)[0] = make_float4(f[0], f[1], f[2], f[3]);
-          reinterpret_cast<float4*>(d)[1] = make_float4(f[4], f[5], f[6], f[7]);
-        } else {
-          for (int j = 0; j < cnt; ++j) d[j] = f[j];
-        }
+      for (int j = 0; j < kGroup; ++j) f[j] = h2f<SDT>(vals.get(j));
+      float* d = static_cast<float*>(dst) + q;
+      if (cnt == kGroup) {
+        st_v4f(d, v4f{f[0], f[1], f[2], f[3]});
+        st_v4f(d + 4, v4f{f[4], f[5], f[6], f[7]});
       } else {
-        uint16_t* d = static_cast<uint16_t*>(dst) + q;
-        if (cnt == kGroup)
-          st16_vec(d, vals[u]);
-        else
-          st16_elem(d, vals[u], cnt);
+        for (int j = 0; j < cnt; ++j) d[j] = f[j];
       }
+    } else {
+      uint16_t* d = static_cast<uint16_t*>(dst) + q;
+      if (cnt == kGroup)
+        st16_vec(d, vals);
+      else
+        st16_elem(d, vals, cnt);
     }
   }
   if (CHECK) {
@@ -270,27 +273,29 @@ __global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __
 // ------------------------------------------------------------------ check (sum of squares)
 
 template <int DT>
-__global__ __launch_bounds__(kThreads) void k_check(const uint16_t* __restrict__ shard, int64_t n, int64_t ntiles,
+__global__ __launch_bounds__(kThreads) void k_check(const uint16_t* __restrict__ shard, int64_t n,
                                                     double* __restrict__ partials) {
-  const bool vec_ok = aligned16(shard);
+  const int64_t q = int64_t(blockIdx.x) * kPackBlock + int64_t(threadIdx.x) * kGroup;
+  const int cnt = group_count(n, q);
   double acc = 0.0;
-  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int64_t base = tile * kTile;
-    G16 vals[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t q = base + int64_t(u * kThreads + threadIdx.x) * kGroup;
-      const int cnt = group_count(n, q);
-      if (cnt == kGroup && vec_ok)
-        vals[u] = ld16_vec(shard + q);
-      else
-        vals[u] = ld16_elem(shard + q, cnt);
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) acc += sumsq8<DT>(vals[u]);
+  if (cnt > 0) {
+    const G16 vals = (cnt == kGroup && aligned16(shard)) ? ld16_vec(shard + q) : ld16_elem(shard + q, cnt);
+    acc = sumsq8<DT>(vals);
   }
   const double r = block_sum(acc);
   if (threadIdx.x == 0) partials[blockIdx.x] = r;
+}
+
+// First level of the fixed-order reduction of many partial sums: workgroup b adds
+// partials [b*per, min((b+1)*per, n)) and writes level2[b].
+__global__ __launch_bounds__(kThreads) void k_partial_reduce(const double* __restrict__ partials, int64_t n,
+                                                             int64_t per, double* __restrict__ level2) {
+  const int64_t b0 = int64_t(blockIdx.x) * per;
+  const int64_t b1 = (b0 + per < n) ? b0 + per : n;
+  double acc = 0.0;
+  for (int64_t i = b0 + threadIdx.x; i < b1; i += kThreads) acc += partials[i];
+  const double r = block_sum(acc);
+  if (threadIdx.x == 0) level2[blockIdx.x] = r;
 }
 
 // ------------------------------------------------------------------ finalize kernels
@@ -299,12 +304,12 @@ __global__ __launch_bounds__(kThreads) void k_check(const uint16_t* __restrict__
 // rank's unscaled sum of squares.  Every element is finite iff the sum is finite: a finite
 // fp16/bf16 square is below 2^256 and at most 2^63 of them stay far below the fp64 range,
 // while inf or NaN anywhere propagates to the sum.
-__global__ __launch_bounds__(kThreads) void k_flag_finalize(const double* __restrict__ partials, int nparts,
+__global__ __launch_bounds__(kThreads) void k_flag_finalize(const double* __restrict__ partials, int64_t nparts,
                                                             DevState* __restrict__ st,
                                                             const int32_t* __restrict__ ext, int mode,
                                                             double* __restrict__ local_out) {
   double acc = 0.0;
-  for (int i = threadIdx.x; i < nparts; i += kThreads) acc += partials[i];
+  for (int64_t i = threadIdx.x; i < nparts; i += kThreads) acc += partials[i];
   const double raw = block_sum(acc);
   if (threadIdx.x == 0) {
     const bool bad = !isfinite(raw);
@@ -412,10 +417,11 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const uint16_t* _
   const StepScalars k = step_scalars(hp, st);
   const bool g_vec = aligned16(shard);
   const int64_t n = mp.len;
-  for (int64_t tile = blockIdx.x; tile < mp.ntiles; tile += gridDim.x) {
+  const int64_t tile = blockIdx.x;
+  {
     const int64_t base = tile * kTile;
     G16 gv[kUnroll];
-    float4 pv[kUnroll][2], mv[kUnroll][2], vv[kUnroll][2];
+    v4f pv[kUnroll][2], mv[kUnroll][2], vv[kUnroll][2];
     int cnts[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -424,13 +430,13 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const uint16_t* _
       cnts[u] = cnt;
       if (cnt == kGroup) {
         gv[u] = g_vec ? ld16_vec(shard + q) : ld16_elem(shard + q, kGroup);
-        pv[u][0] = reinterpret_cast<const float4*>(master + q)[0];
-        pv[u][1] = reinterpret_cast<const float4*>(master + q)[1];
-        mv[u][0] = reinterpret_cast<const float4*>(mom1 + q)[0];
-        mv[u][1] = reinterpret_cast<const float4*>(mom1 + q)[1];
-        vv[u][0] = reinterpret_cast<const float4*>(mom2 + q)[0];
-        vv[u][1] = reinterpret_cast<const float4*>(mom2 + q)[1];
-      } else if (cnt > 0) {
+        pv[u][0] = ld_v4f(master + q);
+        pv[u][1] = ld_v4f(master + q + 4);
+        mv[u][0] = ld_v4f(mom1 + q);
+        mv[u][1] = ld_v4f(mom1 + q + 4);
+        vv[u][0] = ld_v4f(mom2 + q);
+        vv[u][1] = ld_v4f(mom2 + q + 4);
+      } else {
         gv[u] = ld16_elem(shard + q, cnt);
         float pt[kGroup] = {0.f}, mt[kGroup] = {0.f}, vt[kGroup] = {0.f};
         for (int j = 0; j < cnt; ++j) {
@@ -438,12 +444,12 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const uint16_t* _
           mt[j] = mom1[q + j];
           vt[j] = mom2[q + j];
         }
-        pv[u][0] = make_float4(pt[0], pt[1], pt[2], pt[3]);
-        pv[u][1] = make_float4(pt[4], pt[5], pt[6], pt[7]);
-        mv[u][0] = make_float4(mt[0], mt[1], mt[2], mt[3]);
-        mv[u][1] = make_float4(mt[4], mt[5], mt[6], mt[7]);
-        vv[u][0] = make_float4(vt[0], vt[1], vt[2], vt[3]);
-        vv[u][1] = make_float4(vt[4], vt[5], vt[6], vt[7]);
+        pv[u][0] = v4f{pt[0], pt[1], pt[2], pt[3]};
+        pv[u][1] = v4f{pt[4], pt[5], pt[6], pt[7]};
+        mv[u][0] = v4f{mt[0], mt[1], mt[2], mt[3]};
+        mv[u][1] = v4f{mt[4], mt[5], mt[6], mt[7]};
+        vv[u][0] = v4f{vt[0], vt[1], vt[2], vt[3]};
+        vv[u][1] = v4f{vt[4], vt[5], vt[6], vt[7]};
       }
     }
     TileSeg ts;
@@ -453,12 +459,16 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const uint16_t* _
       const int cnt = cnts[u];
       if (cnt <= 0) continue;
       const int64_t q = base + int64_t(u * kThreads + threadIdx.x) * kGroup;
-      float p[kGroup] = {pv[u][0].x, pv[u][0].y, pv[u][0].z, pv[u][0].w,
-                         pv[u][1].x, pv[u][1].y, pv[u][1].z, pv[u][1].w};
-      float m[kGroup] = {mv[u][0].x, mv[u][0].y, mv[u][0].z, mv[u][0].w,
-                         mv[u][1].x, mv[u][1].y, mv[u][1].z, mv[u][1].w};
-      float v[kGroup] = {vv[u][0].x, vv[u][0].y, vv[u][0].z, vv[u][0].w,
-                         vv[u][1].x, vv[u][1].y, vv[u][1].z, vv[u][1].w};
+      float p[kGroup], m[kGroup], v[kGroup];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[j] = pv[u][0][j];
+        p[j + 4] = pv[u][1][j];
+        m[j] = mv[u][0][j];
+        m[j + 4] = mv[u][1][j];
+        v[j] = vv[u][0][j];
+        v[j + 4] = vv[u][1][j];
+      }
       G16 out = g16_zero();
 #pragma unroll
       for (int j = 0; j < kGroup; ++j) {
@@ -466,12 +476,12 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const uint16_t* _
         out.set(j, f2h<PDT>(p[j]));
       }
       if (cnt == kGroup) {
-        reinterpret_cast<float4*>(master + q)[0] = make_float4(p[0], p[1], p[2], p[3]);
-        reinterpret_cast<float4*>(master + q)[1] = make_float4(p[4], p[5], p[6], p[7]);
-        reinterpret_cast<float4*>(mom1 + q)[0] = make_float4(m[0], m[1], m[2], m[3]);
-        reinterpret_cast<float4*>(mom1 + q)[1] = make_float4(m[4], m[5], m[6], m[7]);
-        reinterpret_cast<float4*>(mom2 + q)[0] = make_float4(v[0], v[1], v[2], v[3]);
-        reinterpret_cast<float4*>(mom2 + q)[1] = make_float4(v[4], v[5], v[6], v[7]);
+        st_v4f(master + q, v4f{p[0], p[1], p[2], p[3]});
+        st_v4f(master + q + 4, v4f{p[4], p[5], p[6], p[7]});
+        st_v4f(mom1 + q, v4f{m[0], m[1], m[2], m[3]});
+        st_v4f(mom1 + q + 4, v4f{m[4], m[5], m[6], m[7]});
+        st_v4f(mom2 + q, v4f{v[0], v[1], v[2], v[3]});
+        st_v4f(mom2 + q + 4, v4f{v[4], v[5], v[6], v[7]});
         if (FLAT_OUT) st16_vec(flat_out + q, out);
       } else {
         for (int j = 0; j < cnt; ++j) {
@@ -496,7 +506,8 @@ __global__ __launch_bounds__(kThreads) void k_unpack(DevMap mp, const void* __re
                                                      const uint64_t* __restrict__ ptrs) {
   if (skip != nullptr && skip->h.overflow) return;
   const bool vec_ok = aligned16(src);
-  for (int64_t tile = blockIdx.x; tile < mp.ntiles; tile += gridDim.x) {
+  const int64_t tile = blockIdx.x;
+  {
     const TileSeg ts = tile_seg(mp, ptrs, tile);
     const int64_t base = tile * kTile;
     G16 vals[kUnroll];
@@ -512,8 +523,8 @@ __global__ __launch_bounds__(kThreads) void k_unpack(DevMap mp, const void* __re
         const float* s = static_cast<const float*>(src) + q;
         float f[kGroup] = {0.f};
         if (cnt == kGroup) {
-          const float4 a = reinterpret_cast<const float4*>(s)[0];
-          const float4 b = reinterpret_cast<const float4*>(s)[1];
+          const v4f a = ld_v4f(s);
+          const v4f b = ld_v4f(s + 4);
           f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
           f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
         } else {
@@ -535,19 +546,15 @@ __global__ __launch_bounds__(kThreads) void k_unpack(DevMap mp, const void* __re
   }
 }
 
-inline int clamp_grid(int64_t ntiles, int grid) {
-  return static_cast<int>(ntiles < grid ? ntiles : grid);
-}
-
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
 
 hipError_t launch_pack(const DevMap& map, const uint64_t* src_ptrs, int src_dt, void* dst, int dst_dt,
-                       double* partials, int grid, hipStream_t s) {
-  if (map.ntiles == 0 || grid <= 0) return hipSuccess;
-  const int g = clamp_grid(map.ntiles, grid);
-  const dim3 G(g), B(kThreads);
+                       double* partials, hipStream_t s) {
+  const int64_t nb = reduction_blocks(map.len);
+  if (nb == 0) return hipSuccess;
+  const dim3 G(static_cast<unsigned>(nb)), B(kThreads);
   const bool f32 = (dst_dt == ZS_FP32);
   const bool chk = (partials != nullptr);
   if (src_dt == ZS_BF16) {
@@ -568,20 +575,33 @@ hipError_t launch_pack(const DevMap& map, const uint64_t* src_ptrs, int src_dt, 
   return hipGetLastError();
 }
 
-hipError_t launch_check(const void* shard, int64_t n, int dt, double* partials, int grid, hipStream_t s) {
-  const int64_t ntiles = (n + kTile - 1) / kTile;
-  if (ntiles == 0 || grid <= 0) return hipSuccess;
-  const int g = clamp_grid(ntiles, grid);
+hipError_t launch_check(const void* shard, int64_t n, int dt, double* partials, hipStream_t s) {
+  const int64_t nb = reduction_blocks(n);
+  if (nb == 0) return hipSuccess;
   const uint16_t* p = static_cast<const uint16_t*>(shard);
+  const dim3 G(static_cast<unsigned>(nb)), B(kThreads);
   if (dt == ZS_BF16)
-    hipLaunchKernelGGL((k_check<ZS_BF16>), dim3(g), dim3(kThreads), 0, s, p, n, ntiles, partials);
+    hipLaunchKernelGGL((k_check<ZS_BF16>), G, B, 0, s, p, n, partials);
   else
-    hipLaunchKernelGGL((k_check<ZS_FP16>), dim3(g), dim3(kThreads), 0, s, p, n, ntiles, partials);
+    hipLaunchKernelGGL((k_check<ZS_FP16>), G, B, 0, s, p, n, partials);
   return hipGetLastError();
 }
 
-hipError_t launch_flag_finalize(const double* partials, int nparts, DevState* st, const int32_t* ext, int mode,
-                                double* local_out, hipStream_t s) {
+hipError_t launch_reduce_finalize(const double* partials, int64_t nparts, double* level2, DevState* st,
+                                  const int32_t* ext, int mode, double* local_out, hipStream_t s) {
+  // Up to 16 partials per thread go straight to the single finalize workgroup; more are
+  // first folded by up to kLevel2 workgroups, each over a contiguous range, in fixed order.
+  if (nparts > int64_t(kThreads) * 16) {
+    const int64_t per0 = (nparts + kLevel2 - 1) / kLevel2;
+    const int64_t per = per0 < int64_t(kThreads) * 4 ? int64_t(kThreads) * 4 : per0;
+    const int64_t nb = (nparts + per - 1) / per;
+    hipLaunchKernelGGL(k_partial_reduce, dim3(static_cast<unsigned>(nb)), dim3(kThreads), 0, s, partials, nparts,
+                       per, level2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    partials = level2;
+    nparts = nb;
+  }
   hipLaunchKernelGGL(k_flag_finalize, dim3(1), dim3(kThreads), 0, s, partials, nparts, st, ext, mode, local_out);
   return hipGetLastError();
 }
@@ -619,9 +639,9 @@ static void adamw_dispatch(const dim3& G, hipStream_t s, const DevMap& map, cons
 
 hipError_t launch_adamw(const DevMap& map, const void* shard, int grad_dt, float* master, float* m, float* v,
                         const AdamwArgs& hp, const DevState* st, const uint64_t* param_ptrs, void* flat_out,
-                        int param_dt, int grid, hipStream_t s) {
-  if (map.ntiles == 0 || grid <= 0) return hipSuccess;
-  const dim3 G(clamp_grid(map.ntiles, grid));
+                        int param_dt, hipStream_t s) {
+  if (map.ntiles == 0) return hipSuccess;
+  const dim3 G(static_cast<unsigned>(map.ntiles));
   const uint16_t* g = static_cast<const uint16_t*>(shard);
   uint16_t* fo = static_cast<uint16_t*>(flat_out);
   if (grad_dt == ZS_BF16 && param_dt == ZS_BF16)
@@ -636,9 +656,9 @@ hipError_t launch_adamw(const DevMap& map, const void* shard, int grad_dt, float
 }
 
 hipError_t launch_unpack(const DevMap& map, const void* src, int src_dt, const uint64_t* dst_ptrs, int dst_dt,
-                         const DevState* skip, int grid, hipStream_t s) {
-  if (map.ntiles == 0 || grid <= 0) return hipSuccess;
-  const dim3 G(clamp_grid(map.ntiles, grid)), B(kThreads);
+                         const DevState* skip, hipStream_t s) {
+  if (map.ntiles == 0) return hipSuccess;
+  const dim3 G(static_cast<unsigned>(map.ntiles)), B(kThreads);
   const bool f32 = (src_dt == ZS_FP32);
   if (dst_dt == ZS_BF16) {
     if (f32)
