@@ -12,6 +12,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -50,6 +51,31 @@ def cpu_baseline(wl, n_elems, steps):
             "sample": f"{steps} whole oracle steps (pack, flag, norm, AdamW, cast, scaler) on a {n_elems}-element "
                       f"single-tensor slice with the workload's distributions; elements/s = slice size / mean "
                       f"step time ({per_step:.2f} s)"}
+
+
+def kernel_source_sha256():
+    h = hashlib.sha256()
+    for f in ("zero_sharded_mixed_buffer_amd/csrc/zs_kernels.hip", "zero_sharded_mixed_buffer_amd/csrc/zs_internal.h"):
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel="k_adamw"):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary, scaled by the copy-kernel calibration recorded there; None when there is no
+    summary for this workload or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"k_adamw_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        text = fh.read()
+    if "```json" not in text:
+        return None
+    summary = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    if summary.get("source_sha256") != kernel_source_sha256():
+        return None
+    return summary["kernels"][kernel]["traffic_bytes"]
 
 
 def ceilings(torch, gib=4, reps=5):
@@ -159,6 +185,7 @@ def main():
     step_bytes = pack_bytes + adamw_bytes
     adamw_gbps = adamw_bytes / (adamw_ms * 1e-3) / 1e9
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    traffic = measured_traffic(wl.name)
     log(f"step {ms_per_step:.3f} ms ({step_gbps:.0f} GB/s), pack {pack_ms:.3f} ms "
         f"({pack_bytes / pack_ms / 1e6:.0f} GB/s), adamw {adamw_ms:.3f} ms ({adamw_gbps:.0f} GB/s)")
     out = {
@@ -184,8 +211,9 @@ def main():
                        "finalize_and_scaler": ms_per_step - pack_ms - adamw_ms},
         "roofline": {"bound": "hbm", "kernel": "k_adamw (AdamW + unscale + clip + cast + scatter)",
                      "achieved": adamw_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": adamw_gbps / HBM_PEAK_GBPS, "traffic": None,
-                     "bytes_per_launch": adamw_bytes, "avg_launch_ms": adamw_ms},
+                     "frac": adamw_gbps / HBM_PEAK_GBPS, "traffic": traffic,
+                     "bytes_per_launch": adamw_bytes, "avg_launch_ms": adamw_ms,
+                     "traffic_over_algorithmic": None if traffic is None else traffic / adamw_bytes},
     }
     opt.close()
     del params, grads, opt
