@@ -86,6 +86,165 @@ def oracle_scaler(wl):
     return O.OracleScaler(wl.init_scale, 1.0, wl.dynamic, wl.growth_interval)
 
 
+def sample_windows(lay, width=1 << 16, n_random=24, seed=0):
+    """Deterministic shard windows [a, b) (shard-relative): the first and last `width`
+    elements, windows across the first and last four tensor boundaries inside the shard,
+    and n_random seeded ones."""
+    import random
+    S = lay.shard_numel
+    lo, hi = lay.shard_begin, lay.shard_begin + S
+    w = min(width, S)
+    starts = {0, S - w}
+    inside = [off for off in lay.offsets if lo < off < hi]
+    for off in inside[:4] + inside[-4:]:
+        starts.add(min(max(off - lo - w // 2, 0), S - w))
+    rng = random.Random(seed)
+    for _ in range(n_random):
+        starts.add(rng.randrange(0, S - w + 1))
+    return sorted((a, a + w) for a in starts)
+
+
+def _window_values(tensors_cpu, lay, a, b, dtype):
+    """Oracle pack of shard window [a, b): the flat values there, zeros in padding."""
+    out = torch.zeros(b - a, dtype=dtype)
+    lo = lay.shard_begin + a
+    hi = lay.shard_begin + b
+    for t, off, n in zip(tensors_cpu, lay.offsets, lay.numels):
+        x, y = max(off, lo), min(off + n, hi)
+        if x < y:
+            out[x - lo:y - lo] = t.view(-1)[x - off:y - off]
+    return out
+
+
+def run_parity_sampled(wl, steps=None, log=print):
+    """Full-size parity on sampled outputs.  The GPU runs the whole step at the workload's
+    real size in the same launch configuration as bench.py; the oracle computes every
+    step's flag, scaler and global norm from all gradients (streamed to the host one
+    tensor at a time) and the AdamW state only on sampled shard windows, which are
+    compared element by element (master, m, v, params, packed buffer)."""
+    steps = wl.steps if steps is None else steps
+    d, rank, align = wl.dp_world, wl.dp_rank, wl.align
+    dev = torch.device("cuda", 0)
+    dt = gen.TORCH_DTYPE[wl.dtype]
+    hp = wl.hparams
+    lay = O.plan_layout(wl.numels, d, rank, align)
+    S = lay.shard_numel
+    wins = sample_windows(lay, seed=wl.seed)
+    params = gen.make_params(wl, dev)
+    params_cpu0 = [p.cpu() for p in params]
+    opt = Z.ZeroShardedAdamW(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                             weight_decay=hp["weight_decay"], max_norm=hp["max_norm"], dp_world=d, dp_rank=rank,
+                             align=align, dynamic_loss_scale=wl.dynamic, init_scale=wl.init_scale,
+                             growth_interval=wl.growth_interval)
+    scaler = oracle_scaler(wl)
+    # Oracle state on the windows only.
+    ref = {}
+    for a, b in wins:
+        p = _window_values(params_cpu0, lay, a, b, torch.float32)
+        ref[(a, b)] = [p, torch.zeros_like(p), torch.zeros_like(p)]
+    del params_cpu0
+    others = {}
+    for q in range(d):
+        if q != rank:
+            lq = Z.zs_layout_create(wl.numels, d, q, align)
+            others[q] = (lq, Z.zs_state_create(lq, Z.state_host(wl.init_scale, 1.0, wl.dynamic, wl.growth_interval)))
+    exchange = torch.zeros(d, dtype=torch.float64, device=dev)
+    # Tensor pieces overlapping each window, found once: tensor index -> [(window, x, y)].
+    import bisect
+    overlaps = {}
+    for (a, b) in wins:
+        lo, hi = lay.shard_begin + a, lay.shard_begin + b
+        i = max(bisect.bisect_right(lay.offsets, lo) - 1, 0)
+        while i < len(lay.offsets) and lay.offsets[i] < hi:
+            x, y = max(lay.offsets[i], lo), min(lay.offsets[i] + lay.numels[i], hi)
+            if x < y:
+                overlaps.setdefault(i, []).append(((a, b), x, y))
+            i += 1
+    worst = dict(master=0.0, m=0.0, v=0.0)
+    ndiff = dict(master=0, m=0, v=0, params=0)
+    try:
+        for step in range(1, steps + 1):
+            scale = scaler.loss_scale
+            grads = gen.make_grads(wl, step, scale, dev)
+            opt.pack(grads)
+            if d == 1:
+                opt.norm()
+            else:
+                for q in range(d):
+                    if q == rank:
+                        opt.check(local_sumsq_out=exchange[q:q + 1])
+                    else:
+                        Z.zs_unscale_check(others[q][0], opt.flat[q * S:(q + 1) * S], dt, others[q][1], None,
+                                           exchange[q:q + 1])
+                opt.norm(rank_sumsq=exchange)
+                for lq, sq in others.values():
+                    Z.zs_grad_norm(lq, None, dt, sq, opt.hp, exchange, None)
+                    Z.zs_scaler_update(sq)
+            st_before = opt.read_state()
+            opt.update()
+            st = opt.read_state()
+
+            # Oracle: flag and global norm over every gradient element, one tensor at a time.
+            overflow = False
+            parts = []
+            win_x = {w: torch.zeros(w[1] - w[0], dtype=dt) for w in wins}
+            for i, (g, off, n) in enumerate(zip(grads, lay.offsets, lay.numels)):
+                gc = g.cpu()
+                if O.nonfinite_any(gc):
+                    overflow = True
+                else:
+                    parts.append(O.sumsq_unscaled(gc, scale))
+                for (a, b), x, y in overlaps.get(i, ()):
+                    lo = lay.shard_begin + a
+                    win_x[(a, b)][x - lo:y - lo] = gc.view(-1)[x - off:y - off]
+                del gc
+            assert st_before["overflow"] == int(overflow), f"step {step}: overflow flag differs"
+            if not overflow:
+                ss = O.global_sumsq(parts)
+                norm, c = O.clip_coefficient(ss, hp["max_norm"])
+                assert abs(st_before["grad_norm"] - norm) <= NORM_RTOL * norm, \
+                    f"step {step}: norm {st_before['grad_norm']!r} vs {norm!r}"
+                assert abs(st_before["clip_coef"] - c) <= NORM_RTOL * c
+                t = scaler.step_t + 1
+            scaler = O.scaler_update(scaler, overflow)
+            assert st["loss_scale"] == scaler.loss_scale and st["step_t"] == scaler.step_t
+            assert st["growth_tracker"] == scaler.growth_tracker and st["skipped_total"] == scaler.skipped_total
+            flat_gpu = opt.flat
+            master_gpu, m_gpu, v_gpu = opt.master, opt.m, opt.v
+            for (a, b) in wins:
+                xw = win_x[(a, b)]
+                assert torch.equal(bits(flat_gpu[lay.shard_begin + a:lay.shard_begin + b].cpu()), bits(xw)), \
+                    f"step {step}: packed window {a} differs"
+                st_ref = ref[(a, b)]
+                if not overflow:
+                    ref[(a, b)] = list(O.adamw_update(st_ref[0], st_ref[1], st_ref[2], xw, scale, c, t, hp))
+                pm = master_gpu[a:b].cpu()
+                for name, got, want in (("master", pm, ref[(a, b)][0]), ("m", m_gpu[a:b].cpu(), ref[(a, b)][1]),
+                                        ("v", v_gpu[a:b].cpu(), ref[(a, b)][2])):
+                    ndiff[name] += int((bits(got) != bits(want)).sum())
+                    worst[name] = max(worst[name], rel_err(got, want) if want.abs().max() > 0 else 0.0)
+            log(f"[fullsize] {wl.name} step {step}: overflow={int(overflow)} scale={st['loss_scale']} "
+                f"norm={st_before['grad_norm']:.9g} worst={worst} ndiff={ndiff}")
+        # Parameters at the windows: the cast of the GPU master, bit-exact (unpack as a function).
+        for i, pieces in overlaps.items():
+            p, off = params[i], lay.offsets[i]
+            for (a, b), x, y in pieces:
+                lo = lay.shard_begin + a
+                pm = opt.master[x - lay.shard_begin:y - lay.shard_begin].cpu()
+                got = p.view(-1)[x - off:y - off].cpu()
+                want = O.cast_to(pm, p.dtype)
+                assert torch.equal(bits(got), bits(want)), f"params of window {a} differ"
+                ndiff["params"] += int((bits(got) != bits(O.cast_to(ref[(a, b)][0][x - lo:y - lo], p.dtype))).sum())
+        for k in ("master", "m", "v"):
+            assert worst[k] <= REL_TOL, f"{k} relative error {worst[k]}"
+        return worst, ndiff, wins
+    finally:
+        for lq, sq in others.values():
+            Z.zs_state_destroy(sq)
+            Z.zs_layout_destroy(lq)
+        opt.close()
+
+
 def run_parity(wl, steps=None, align=None, dp_rank=None, check_every_step=True):
     """Run `steps` optimizer steps of workload `wl` on cuda:0 and in the oracle, checking
     every stage each step.  Returns a RunReport; raises AssertionError on a mismatch of

@@ -1,0 +1,138 @@
+"""The pins catch plausible mistakes: each test plants one mistake in the oracle (on the CPU,
+by monkeypatching) and checks that at least one pin of test_oracle_pins.py then fails."""
+
+import math
+
+import pytest
+import torch
+
+import oracle
+import oracle.zs_oracle as Z
+import test_oracle_pins as P
+
+
+def _patch(monkeypatch, name, fn):
+    monkeypatch.setattr(Z, name, fn)
+    monkeypatch.setattr(oracle, name, fn)
+
+
+def _fails(*tests):
+    """True when at least one of the pin functions raises AssertionError."""
+    for t in tests:
+        try:
+            t()
+        except AssertionError:
+            return True
+    return False
+
+
+ADAMW_PINS = (P.test_adamw_closed_form_constant_gradient, P.test_adamw_zero_gradient_is_pure_decoupled_decay,
+              P.test_adamw_eps_added_after_the_root, P.test_page_sharded_sgd_example_through_adamw_limit,
+              lambda: P.test_adamw_matches_torch_optim_adamw_step_by_step(0))
+
+
+def _adamw_variant(kind):
+    def f(master, m, v, x, loss_scale, clip, t, hp):
+        lr, b1, b2, eps, wd = hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"]
+        g = x.double() / loss_scale * clip
+        p = master.double()
+        if kind == "coupled_decay":
+            g = g + wd * p
+        m_t = (b1 * m.double() + (1 - b1) * g).float()
+        v_t = ((b1 if kind == "beta1_for_v" else b2) * v.double() + (1 - b2) * g * g).float()
+        tt = t + 1 if kind == "t_off_by_one" else t
+        m_hat = m_t.double() / (1 if kind == "no_bias_correction" else (1 - b1 ** tt))
+        v_hat = v_t.double() / (1 if kind == "no_bias_correction" else (1 - b2 ** tt))
+        den = (v_hat + eps).sqrt() if kind == "eps_inside_root" else v_hat.sqrt() + eps
+        decay = 1.0 if kind == "coupled_decay" else (1 - lr * wd)
+        step = lr * m_hat / den
+        p_t = (p * decay + step) if kind == "wrong_sign" else (p * decay - step)
+        return p_t.float(), m_t, v_t
+    return f
+
+
+@pytest.mark.parametrize("kind", ["no_bias_correction", "eps_inside_root", "coupled_decay", "wrong_sign",
+                                  "beta1_for_v", "t_off_by_one"])
+def test_adamw_mistakes_are_caught(monkeypatch, kind):
+    _patch(monkeypatch, "adamw_update", _adamw_variant(kind))
+    assert _fails(*ADAMW_PINS), kind
+
+
+def test_norm_without_unscale_is_caught(monkeypatch):
+    _patch(monkeypatch, "sumsq_unscaled", lambda x, s: float((x.double() ** 2).sum()) if x.numel() else 0.0)
+    assert _fails(P.test_sumsq_matches_exact_rationals, P.test_sumsq_special_cases_and_invariants)
+
+
+@pytest.mark.parametrize("kind", ["no_eps", "no_min"])
+def test_clip_mistakes_are_caught(monkeypatch, kind):
+    def f(ss, max_norm):
+        n = math.sqrt(ss)
+        if max_norm <= 0:
+            return n, 1.0
+        if kind == "no_eps":
+            return n, min(1.0, max_norm / n) if n > 0 else 1.0
+        return n, max_norm / (n + 1e-6)
+    _patch(monkeypatch, "clip_coefficient", f)
+    assert _fails(P.test_clip_coefficient_matches_clip_grad_norm)
+
+
+def test_overflow_only_inf_is_caught(monkeypatch):
+    def f(x):
+        if x.numel() == 0:
+            return False
+        return bool(torch.isinf(x.float()).any())
+    _patch(monkeypatch, "nonfinite_any", f)
+    assert _fails(lambda: P.test_nonfinite_flag_exhaustive(torch.float16),
+                  lambda: P.test_nonfinite_flag_exhaustive(torch.bfloat16))
+
+
+def test_truncating_cast_is_caught(monkeypatch):
+    def f(x, dtype):
+        # round toward zero: clear the dropped mantissa bits before rounding
+        bits = x.float().contiguous().view(torch.int32)
+        keep = 16 if dtype == torch.bfloat16 else 13
+        return (bits & ~((1 << keep) - 1)).view(torch.float32).to(dtype)
+    _patch(monkeypatch, "cast_to", f)
+    assert _fails(P.test_cast_ties_round_to_even)
+
+
+def test_layout_mistake_is_caught(monkeypatch):
+    real = Z.plan_layout
+
+    def f(numels, dp_world, dp_rank, align=1):
+        lay = real(numels, dp_world, dp_rank, align)
+        # pad only the tail to dp_world (forgetting the per-tensor alignment)
+        pos = 0
+        offs = []
+        for n in numels:
+            offs.append(pos)
+            pos += n
+        lay.offsets = offs
+        return lay
+    _patch(monkeypatch, "plan_layout", f)
+    assert _fails(lambda: P.test_layout_pack_unpack_roundtrip(8, 2), lambda: P.test_layout_pack_unpack_roundtrip(64, 3))
+
+
+@pytest.mark.parametrize("kind", ["grow_late", "no_reset_on_overflow", "no_floor", "t_counts_skips"])
+def test_scaler_mistakes_are_caught(monkeypatch, kind):
+    def f(s, overflow):
+        s = Z.OracleScaler(**s.__dict__)
+        if overflow:
+            s.skipped_total += 1
+            if kind != "no_reset_on_overflow":
+                s.growth_tracker = 0
+            if kind == "t_counts_skips":
+                s.step_t += 1
+            if s.dynamic:
+                s.loss_scale = s.loss_scale / 2.0 if kind == "no_floor" else max(s.loss_scale / 2.0, s.scale_floor)
+        else:
+            s.step_t += 1
+            if s.dynamic:
+                s.growth_tracker += 1
+                if s.growth_tracker == s.growth_interval + (1 if kind == "grow_late" else 0):
+                    s.loss_scale *= 2.0
+                    s.growth_tracker = 0
+        return s
+    _patch(monkeypatch, "scaler_update", f)
+    assert _fails(P.test_scaler_tiny_config_sequence, P.test_scaler_growth_and_backoff_sequence,
+                  P.test_scaler_floor_and_static, P.test_scaler_doubles_once_per_window), kind
