@@ -12,15 +12,15 @@ namespace zs {
 // Streaming-kernel geometry.  Every streaming kernel launches one workgroup of 256 threads
 // (four wave64s) per unit of work - no persistent grid-stride loops, which measured slower
 // on MI355X for these pure streams.  A thread owns groups of 8 consecutive flat elements
-// (one 16-byte access of 2-byte data, two of fp32).  The AdamW and unpack kernels take
-// kUnroll groups per thread, i.e. one 4096-element tile per workgroup; the pack and check
-// passes take one group per thread, i.e. half a tile (kPackBlock) per workgroup, and leave
-// one fp64 partial sum per workgroup.
+// (one 16-byte access of 2-byte data, two of fp32), and every kernel covers one
+// 4096-element tile per workgroup: kUnroll groups per thread in the unpack kernel, two in
+// the pack and check passes (kPackBlock, which also leave one fp64 partial sum per
+// workgroup), and the same elements regrouped as four-element quads in the AdamW kernel.
 constexpr int kThreads = 256;
 constexpr int kGroup = 8;
 constexpr int kUnroll = 2;
 constexpr int64_t kTile = int64_t(kThreads) * kGroup * kUnroll;
-constexpr int64_t kPackBlock = int64_t(kThreads) * kGroup;
+constexpr int64_t kPackBlock = int64_t(kThreads) * kGroup * 2;
 constexpr int kLevel2 = 1024;  // first-level partial-sum workgroups of the two-level reduction
 
 // Workgroups (and partial sums) of a pack or check pass over len elements.

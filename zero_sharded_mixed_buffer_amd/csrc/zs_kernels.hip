@@ -65,6 +65,7 @@ struct G16 {  // eight 2-byte values, element j in bits [16*(j&1), +16) of w[j>>
 __device__ __forceinline__ G16 g16_zero() { return G16{{0u, 0u, 0u, 0u}}; }
 
 __device__ __forceinline__ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+__device__ __forceinline__ bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
 // 16-byte accesses of the streamed arrays; every bulk load and store goes through these.
 // Stores are non-temporal: the written streams are read again only by the next pass or
@@ -76,6 +77,10 @@ __device__ __forceinline__ v4u ld_v4u(const void* p) { return *reinterpret_cast<
 __device__ __forceinline__ void st_v4u(void* p, v4u x) { __builtin_nontemporal_store(x, reinterpret_cast<v4u*>(p)); }
 __device__ __forceinline__ v4f ld_v4f(const float* p) { return *reinterpret_cast<const v4f*>(p); }
 __device__ __forceinline__ void st_v4f(float* p, v4f x) { __builtin_nontemporal_store(x, reinterpret_cast<v4f*>(p)); }
+
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ v2u ld_v2u(const void* p) { return *reinterpret_cast<const v2u*>(p); }
+__device__ __forceinline__ void st_v2u(void* p, v2u x) { __builtin_nontemporal_store(x, reinterpret_cast<v2u*>(p)); }
 
 __device__ __forceinline__ G16 ld16_vec(const uint16_t* p) {
   const v4u u = ld_v4u(p);
@@ -185,16 +190,18 @@ __device__ __forceinline__ G16 gather16(const DevMap& mp, const uint64_t* ptrs, 
   return ld16_elem(src, cnt);
 }
 
-// Write the cnt (<= 8) elements at range indices q.. into the tensors; padding is skipped.
-__device__ __forceinline__ void scatter16(const DevMap& mp, const uint64_t* ptrs, const TileSeg& ts, int64_t q,
-                                          int cnt, const G16& g) {
+// Write the cnt (<= W) elements at range indices q.. into the tensors; padding is skipped.
+// W = 8: one 16-byte store when the destination allows it; W = 4: one 8-byte store.
+template <int W>
+__device__ __forceinline__ void scatter(const DevMap& mp, const uint64_t* ptrs, const TileSeg& ts, int64_t q,
+                                        int cnt, const G16& g) {
   uint16_t* dst;
   if (ts.uniform) {
     if (ts.base == nullptr) return;
     dst = ts.base + q;
   } else {
     int s = seg_find(mp, ts.lo, ts.hi, q);
-    if (mp.seg_begin[s + 1] < q + cnt) {
+    if (mp.seg_begin[s + 1] < q + cnt) {  // the group straddles segments
       for (int j = 0; j < cnt; ++j) {
         const int64_t e = q + j;
         while (mp.seg_begin[s + 1] <= e) ++s;
@@ -206,8 +213,10 @@ __device__ __forceinline__ void scatter16(const DevMap& mp, const uint64_t* ptrs
     dst = seg_elem(mp, ptrs, s, q);
     if (dst == nullptr) return;
   }
-  if (cnt == kGroup && aligned16(dst))
+  if (W == 8 && cnt == 8 && aligned16(dst))
     st16_vec(dst, g);
+  else if (W == 4 && cnt == 4 && aligned8(dst))
+    st_v2u(dst, v2u{g.w[0], g.w[1]});
   else
     st16_elem(dst, g, cnt);
 }
@@ -230,25 +239,35 @@ __device__ __forceinline__ double sumsq8(const G16& g) {
 
 // ------------------------------------------------------------------ pack (+ fused check)
 
-// Gather the tensors into the flat range; padding becomes zero.  One group per thread, one
-// kPackBlock-element block per workgroup.  TO_F32: widen to fp32 (master seeding).  CHECK:
+// Gather the tensors into the flat range; padding becomes zero.  kPackBlock elements per
+// workgroup (one 8-element group per thread).  TO_F32: widen to fp32 (master seeding).  CHECK:
 // also write the fp64 sum of squares of this block's packed values to partials[blockIdx.x]
 // (a non-finite element makes that sum non-finite).
 template <int SDT, bool TO_F32, bool CHECK>
 __global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __restrict__ ptrs,
                                                    void* __restrict__ dst, double* __restrict__ partials) {
+  constexpr int kPackGroups = int(kPackBlock / (int64_t(kThreads) * kGroup));
   const int64_t block_base = int64_t(blockIdx.x) * kPackBlock;
   const TileSeg ts = tile_seg(mp, ptrs, block_base / kTile);
-  const int64_t q = block_base + int64_t(threadIdx.x) * kGroup;
-  const int cnt = group_count(mp.len, q);
+  G16 vals[kPackGroups];
+  int cnts[kPackGroups];
+#pragma unroll
+  for (int u = 0; u < kPackGroups; ++u) {
+    const int64_t q = block_base + int64_t(u * kThreads + threadIdx.x) * kGroup;
+    cnts[u] = group_count(mp.len, q);
+    vals[u] = cnts[u] > 0 ? gather16(mp, ptrs, ts, q, cnts[u]) : g16_zero();
+  }
   double acc = 0.0;
-  if (cnt > 0) {
-    const G16 vals = gather16(mp, ptrs, ts, q, cnt);
-    if (CHECK) acc = sumsq8<SDT>(vals);
+#pragma unroll
+  for (int u = 0; u < kPackGroups; ++u) {
+    const int cnt = cnts[u];
+    if (cnt <= 0) continue;
+    const int64_t q = block_base + int64_t(u * kThreads + threadIdx.x) * kGroup;
+    if (CHECK) acc += sumsq8<SDT>(vals[u]);
     if (TO_F32) {
       float f[kGroup];
 #pragma unroll
-      for (int j = 0; j < kGroup; ++j) f[j] = h2f<SDT>(vals.get(j));
+      for (int j = 0; j < kGroup; ++j) f[j] = h2f<SDT>(vals[u].get(j));
       float* d = static_cast<float*>(dst) + q;
       if (cnt == kGroup) {
         st_v4f(d, v4f{f[0], f[1], f[2], f[3]});
@@ -259,9 +278,9 @@ __global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __
     } else {
       uint16_t* d = static_cast<uint16_t*>(dst) + q;
       if (cnt == kGroup)
-        st16_vec(d, vals);
+        st16_vec(d, vals[u]);
       else
-        st16_elem(d, vals, cnt);
+        st16_elem(d, vals[u], cnt);
     }
   }
   if (CHECK) {
@@ -275,13 +294,18 @@ __global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_check(const uint16_t* __restrict__ shard, int64_t n,
                                                     double* __restrict__ partials) {
-  const int64_t q = int64_t(blockIdx.x) * kPackBlock + int64_t(threadIdx.x) * kGroup;
-  const int cnt = group_count(n, q);
-  double acc = 0.0;
-  if (cnt > 0) {
-    const G16 vals = (cnt == kGroup && aligned16(shard)) ? ld16_vec(shard + q) : ld16_elem(shard + q, cnt);
-    acc = sumsq8<DT>(vals);
+  constexpr int kPackGroups = int(kPackBlock / (int64_t(kThreads) * kGroup));
+  const bool vec_ok = aligned16(shard);
+  G16 vals[kPackGroups];
+#pragma unroll
+  for (int u = 0; u < kPackGroups; ++u) {
+    const int64_t q = int64_t(blockIdx.x) * kPackBlock + int64_t(u * kThreads + threadIdx.x) * kGroup;
+    const int cnt = group_count(n, q);
+    vals[u] = (cnt == kGroup && vec_ok) ? ld16_vec(shard + q) : ld16_elem(shard + q, cnt);
   }
+  double acc = 0.0;
+#pragma unroll
+  for (int u = 0; u < kPackGroups; ++u) acc += sumsq8<DT>(vals[u]);
   const double r = block_sum(acc);
   if (threadIdx.x == 0) partials[blockIdx.x] = r;
 }
@@ -406,6 +430,15 @@ __device__ __forceinline__ void adamw_elem(const StepScalars& k, float x, float&
   v = v1;
 }
 
+// Quad layout: a workgroup owns one 4096-element tile; thread t handles the four-element
+// quads starting at base + u*1024 + 4t for u < 4.  Every wave-wide access of the fp32
+// arrays is then one contiguous 1 KiB row (16 bytes per lane) and every access of the
+// 2-byte arrays a contiguous 512-byte row (8 bytes per lane), so each instruction covers
+// whole cache lines; with the 8-element layout a 16-byte fp32 access per lane left every
+// line half-written by two instructions, which the non-temporal write path turned into
+// 6 % extra HBM write traffic.
+constexpr int kQuadsPerThread = int(kTile / (int64_t(kThreads) * 4));
+
 template <int GDT, int PDT, bool SCATTER, bool FLAT_OUT>
 __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const uint16_t* __restrict__ shard,
                                                     float* __restrict__ master, float* __restrict__ mom1,
@@ -415,84 +448,76 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const uint16_t* _
                                                     uint16_t* __restrict__ flat_out) {
   if (st->h.overflow) return;  // device-side skip: nothing changes on an overflowed step
   const StepScalars k = step_scalars(hp, st);
-  const bool g_vec = aligned16(shard);
+  const bool g_vec = aligned8(shard);
   const int64_t n = mp.len;
   const int64_t tile = blockIdx.x;
-  {
-    const int64_t base = tile * kTile;
-    G16 gv[kUnroll];
-    v4f pv[kUnroll][2], mv[kUnroll][2], vv[kUnroll][2];
-    int cnts[kUnroll];
+  const int64_t base = tile * kTile;
+  G16 gv[kQuadsPerThread];
+  v4f pv[kQuadsPerThread], mv[kQuadsPerThread], vv[kQuadsPerThread];
+  int cnts[kQuadsPerThread];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t q = base + int64_t(u * kThreads + threadIdx.x) * kGroup;
-      const int cnt = group_count(n, q);
-      cnts[u] = cnt;
-      if (cnt == kGroup) {
-        gv[u] = g_vec ? ld16_vec(shard + q) : ld16_elem(shard + q, kGroup);
-        pv[u][0] = ld_v4f(master + q);
-        pv[u][1] = ld_v4f(master + q + 4);
-        mv[u][0] = ld_v4f(mom1 + q);
-        mv[u][1] = ld_v4f(mom1 + q + 4);
-        vv[u][0] = ld_v4f(mom2 + q);
-        vv[u][1] = ld_v4f(mom2 + q + 4);
+  for (int u = 0; u < kQuadsPerThread; ++u) {
+    const int64_t q = base + int64_t(u) * (kThreads * 4) + int64_t(threadIdx.x) * 4;
+    const int64_t rem = n - q;
+    const int cnt = rem >= 4 ? 4 : (rem > 0 ? static_cast<int>(rem) : 0);
+    cnts[u] = cnt;
+    if (cnt == 4) {
+      if (g_vec) {
+        const v2u x = ld_v2u(shard + q);
+        gv[u] = G16{{x.x, x.y, 0u, 0u}};
       } else {
-        gv[u] = ld16_elem(shard + q, cnt);
-        float pt[kGroup] = {0.f}, mt[kGroup] = {0.f}, vt[kGroup] = {0.f};
-        for (int j = 0; j < cnt; ++j) {
-          pt[j] = master[q + j];
-          mt[j] = mom1[q + j];
-          vt[j] = mom2[q + j];
-        }
-        pv[u][0] = v4f{pt[0], pt[1], pt[2], pt[3]};
-        pv[u][1] = v4f{pt[4], pt[5], pt[6], pt[7]};
-        mv[u][0] = v4f{mt[0], mt[1], mt[2], mt[3]};
-        mv[u][1] = v4f{mt[4], mt[5], mt[6], mt[7]};
-        vv[u][0] = v4f{vt[0], vt[1], vt[2], vt[3]};
-        vv[u][1] = v4f{vt[4], vt[5], vt[6], vt[7]};
+        gv[u] = ld16_elem(shard + q, 4);
       }
+      pv[u] = ld_v4f(master + q);
+      mv[u] = ld_v4f(mom1 + q);
+      vv[u] = ld_v4f(mom2 + q);
+    } else {
+      gv[u] = ld16_elem(shard + q, cnt);
+      float pt[4] = {0.f, 0.f, 0.f, 0.f}, mt[4] = {0.f, 0.f, 0.f, 0.f}, vt[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < cnt; ++j) {
+        pt[j] = master[q + j];
+        mt[j] = mom1[q + j];
+        vt[j] = mom2[q + j];
+      }
+      pv[u] = v4f{pt[0], pt[1], pt[2], pt[3]};
+      mv[u] = v4f{mt[0], mt[1], mt[2], mt[3]};
+      vv[u] = v4f{vt[0], vt[1], vt[2], vt[3]};
     }
-    TileSeg ts;
-    if (SCATTER) ts = tile_seg(mp, ptrs, tile);
+  }
+  TileSeg ts;
+  if (SCATTER) ts = tile_seg(mp, ptrs, tile);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int cnt = cnts[u];
-      if (cnt <= 0) continue;
-      const int64_t q = base + int64_t(u * kThreads + threadIdx.x) * kGroup;
-      float p[kGroup], m[kGroup], v[kGroup];
+  for (int u = 0; u < kQuadsPerThread; ++u) {
+    const int cnt = cnts[u];
+    if (cnt <= 0) continue;
+    const int64_t q = base + int64_t(u) * (kThreads * 4) + int64_t(threadIdx.x) * 4;
+    float p[4], m[4], v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        p[j] = pv[u][0][j];
-        p[j + 4] = pv[u][1][j];
-        m[j] = mv[u][0][j];
-        m[j + 4] = mv[u][1][j];
-        v[j] = vv[u][0][j];
-        v[j + 4] = vv[u][1][j];
-      }
-      G16 out = g16_zero();
-#pragma unroll
-      for (int j = 0; j < kGroup; ++j) {
-        adamw_elem(k, h2f<GDT>(gv[u].get(j)), p[j], m[j], v[j]);
-        out.set(j, f2h<PDT>(p[j]));
-      }
-      if (cnt == kGroup) {
-        st_v4f(master + q, v4f{p[0], p[1], p[2], p[3]});
-        st_v4f(master + q + 4, v4f{p[4], p[5], p[6], p[7]});
-        st_v4f(mom1 + q, v4f{m[0], m[1], m[2], m[3]});
-        st_v4f(mom1 + q + 4, v4f{m[4], m[5], m[6], m[7]});
-        st_v4f(mom2 + q, v4f{v[0], v[1], v[2], v[3]});
-        st_v4f(mom2 + q + 4, v4f{v[4], v[5], v[6], v[7]});
-        if (FLAT_OUT) st16_vec(flat_out + q, out);
-      } else {
-        for (int j = 0; j < cnt; ++j) {
-          master[q + j] = p[j];
-          mom1[q + j] = m[j];
-          mom2[q + j] = v[j];
-        }
-        if (FLAT_OUT) st16_elem(flat_out + q, out, cnt);
-      }
-      if (SCATTER) scatter16(mp, ptrs, ts, q, cnt, out);
+    for (int j = 0; j < 4; ++j) {
+      p[j] = pv[u][j];
+      m[j] = mv[u][j];
+      v[j] = vv[u][j];
     }
+    G16 out = g16_zero();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      adamw_elem(k, h2f<GDT>(gv[u].get(j)), p[j], m[j], v[j]);
+      out.set(j, f2h<PDT>(p[j]));
+    }
+    if (cnt == 4) {
+      st_v4f(master + q, v4f{p[0], p[1], p[2], p[3]});
+      st_v4f(mom1 + q, v4f{m[0], m[1], m[2], m[3]});
+      st_v4f(mom2 + q, v4f{v[0], v[1], v[2], v[3]});
+      if (FLAT_OUT) st_v2u(flat_out + q, v2u{out.w[0], out.w[1]});
+    } else {
+      for (int j = 0; j < cnt; ++j) {
+        master[q + j] = p[j];
+        mom1[q + j] = m[j];
+        mom2[q + j] = v[j];
+      }
+      if (FLAT_OUT) st16_elem(flat_out + q, out, cnt);
+    }
+    if (SCATTER) scatter<4>(mp, ptrs, ts, q, cnt, out);
   }
 }
 
@@ -541,7 +566,7 @@ __global__ __launch_bounds__(kThreads) void k_unpack(DevMap mp, const void* __re
     for (int u = 0; u < kUnroll; ++u) {
       if (cnts[u] <= 0) continue;
       const int64_t q = base + int64_t(u * kThreads + threadIdx.x) * kGroup;
-      scatter16(mp, ptrs, ts, q, cnts[u], vals[u]);
+      scatter<kGroup>(mp, ptrs, ts, q, cnts[u], vals[u]);
     }
   }
 }
