@@ -67,19 +67,20 @@ __device__ __forceinline__ G16 g16_zero() { return G16{{0u, 0u, 0u, 0u}}; }
 __device__ __forceinline__ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 __device__ __forceinline__ bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
-// 16-byte accesses of the streamed arrays; every bulk load and store goes through these.
-// Stores are non-temporal: the written streams are read again only by the next pass or
-// the next step, long after they would have left the caches.
+// 16-byte (and 8-byte) accesses of the streamed arrays; every bulk load and store goes
+// through these.  All are non-temporal: every byte is touched once per pass, and the
+// streams are read again only by the next pass or the next step, long after they would
+// have left the caches.
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ v4u ld_v4u(const void* p) { return *reinterpret_cast<const v4u*>(p); }
+__device__ __forceinline__ v4u ld_v4u(const void* p) { return __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p)); }
 __device__ __forceinline__ void st_v4u(void* p, v4u x) { __builtin_nontemporal_store(x, reinterpret_cast<v4u*>(p)); }
-__device__ __forceinline__ v4f ld_v4f(const float* p) { return *reinterpret_cast<const v4f*>(p); }
+__device__ __forceinline__ v4f ld_v4f(const float* p) { return __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p)); }
 __device__ __forceinline__ void st_v4f(float* p, v4f x) { __builtin_nontemporal_store(x, reinterpret_cast<v4f*>(p)); }
 
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ v2u ld_v2u(const void* p) { return *reinterpret_cast<const v2u*>(p); }
+__device__ __forceinline__ v2u ld_v2u(const void* p) { return __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p)); }
 __device__ __forceinline__ void st_v2u(void* p, v2u x) { __builtin_nontemporal_store(x, reinterpret_cast<v2u*>(p)); }
 
 __device__ __forceinline__ G16 ld16_vec(const uint16_t* p) {
@@ -221,6 +222,9 @@ __device__ __forceinline__ void scatter(const DevMap& mp, const uint64_t* ptrs, 
     st16_elem(dst, g, cnt);
 }
 
+// Work unit (tile or pack block) of this workgroup.
+__device__ __forceinline__ int64_t work_unit() { return blockIdx.x; }
+
 __device__ __forceinline__ int group_count(int64_t len, int64_t q) {
   const int64_t rem = len - q;
   return rem >= kGroup ? kGroup : (rem > 0 ? static_cast<int>(rem) : 0);
@@ -247,7 +251,7 @@ template <int SDT, bool TO_F32, bool CHECK>
 __global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __restrict__ ptrs,
                                                    void* __restrict__ dst, double* __restrict__ partials) {
   constexpr int kPackGroups = int(kPackBlock / (int64_t(kThreads) * kGroup));
-  const int64_t block_base = int64_t(blockIdx.x) * kPackBlock;
+  const int64_t block_base = work_unit() * kPackBlock;
   const TileSeg ts = tile_seg(mp, ptrs, block_base / kTile);
   G16 vals[kPackGroups];
   int cnts[kPackGroups];
@@ -299,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void k_check(const uint16_t* __restrict__
   G16 vals[kPackGroups];
 #pragma unroll
   for (int u = 0; u < kPackGroups; ++u) {
-    const int64_t q = int64_t(blockIdx.x) * kPackBlock + int64_t(u * kThreads + threadIdx.x) * kGroup;
+    const int64_t q = work_unit() * kPackBlock + int64_t(u * kThreads + threadIdx.x) * kGroup;
     const int cnt = group_count(n, q);
     vals[u] = (cnt == kGroup && vec_ok) ? ld16_vec(shard + q) : ld16_elem(shard + q, cnt);
   }
@@ -450,7 +454,7 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const uint16_t* _
   const StepScalars k = step_scalars(hp, st);
   const bool g_vec = aligned8(shard);
   const int64_t n = mp.len;
-  const int64_t tile = blockIdx.x;
+  const int64_t tile = work_unit();
   const int64_t base = tile * kTile;
   G16 gv[kQuadsPerThread];
   v4f pv[kQuadsPerThread], mv[kQuadsPerThread], vv[kQuadsPerThread];
@@ -531,7 +535,7 @@ __global__ __launch_bounds__(kThreads) void k_unpack(DevMap mp, const void* __re
                                                      const uint64_t* __restrict__ ptrs) {
   if (skip != nullptr && skip->h.overflow) return;
   const bool vec_ok = aligned16(src);
-  const int64_t tile = blockIdx.x;
+  const int64_t tile = work_unit();
   {
     const TileSeg ts = tile_seg(mp, ptrs, tile);
     const int64_t base = tile * kTile;
