@@ -326,3 +326,91 @@ def test_invalid_arguments_rejected_before_launch():
         Z.zs_grad_norm(Z.zs_layout_create([100], 2, 0), None, torch.bfloat16, st, hp)  # rank_sumsq missing
     Z.zs_state_destroy(st)
     Z.zs_layout_destroy(lay)
+
+
+@pytest.mark.parametrize("grad_dt,param_dt", [(torch.bfloat16, torch.bfloat16), (torch.float16, torch.float16),
+                                              (torch.bfloat16, torch.float16), (torch.float16, torch.bfloat16)])
+@pytest.mark.parametrize("scatter,flat_out", [(True, True), (False, True), (False, False)])
+def test_adamw_output_variants(grad_dt, param_dt, scatter, flat_out):
+    """Every AdamW entry-point variant (fused scatter, flat parameter shard for the all-gather,
+    state only) and mixed gradient / parameter dtypes, against the oracle."""
+    from harness import bits, rel_err
+    Z = _z()
+    dev = torch.device("cuda", 0)
+    numels = [1000, 7, 4096 * 2 + 3, 129, 64]
+    d, r, align = 3, 1, 1
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    params = [torch.randn(n, generator=g, device=dev).mul_(0.02).to(param_dt) for n in numels]
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_norm=1.0)
+    lay = Z.zs_layout_create(numels, d, r, align)
+    flat_numel, sb, sn = Z.zs_layout_info(lay)
+    st = Z.zs_state_create(lay, Z.state_host(1.0, 1.0, False))
+    olay = O.plan_layout(numels, d, r, align)
+    master = torch.empty(sn, dtype=torch.float32, device=dev)
+    Z.zs_pack(lay, Z.pointer_table(params, dev), param_dt, master, torch.float32, whole_flat=False)
+    m = torch.zeros_like(master)
+    v = torch.zeros_like(master)
+    ref_master = O.shard_of(O.pack([p.cpu() for p in params], olay, torch.float32), olay).clone()
+    assert torch.equal(master.cpu(), ref_master)
+    ref_m, ref_v = torch.zeros(sn), torch.zeros(sn)
+    ref_params = [p.cpu() for p in params]
+    flat_param = torch.zeros(sn, dtype=param_dt, device=dev) if flat_out else None
+    ptrs = Z.pointer_table(params, dev)
+    for step in range(1, 4):
+        grads = [torch.randn(n, generator=g, device=dev).mul_(1e-3).to(grad_dt) for n in numels]
+        flat = torch.zeros(flat_numel, dtype=grad_dt, device=dev)
+        Z.zs_pack(lay, Z.pointer_table(grads, dev), grad_dt, flat, grad_dt, whole_flat=True)
+        exch = torch.zeros(d, dtype=torch.float64, device=dev)
+        flat_ref = O.pack([x.cpu() for x in grads], olay)
+        for q in range(d):
+            exch[q] = O.sumsq_unscaled(flat_ref[q * sn:(q + 1) * sn], 1.0)   # other ranks' partials
+        shard = flat[sb:sb + sn]
+        Z.zs_unscale_check(lay, shard, grad_dt, st)
+        Z.zs_grad_norm(lay, None, grad_dt, st, Z.hparams(**hp), exch, None)
+        Z.zs_adamw_step(lay, shard, grad_dt, master, m, v, Z.hparams(**hp), st, ptrs if scatter else None,
+                        flat_param, param_dt)
+        Z.zs_scaler_update(st)
+        norm, c = O.clip_coefficient(O.global_sumsq([float(x) for x in exch.cpu()]), hp["max_norm"])
+        ref_master, ref_m, ref_v = O.adamw_update(ref_master, ref_m, ref_v, O.shard_of(flat_ref, olay), 1.0, c,
+                                                  step, hp)
+        assert rel_err(master.cpu(), ref_master) <= 1e-5 and rel_err(m.cpu(), ref_m) <= 1e-5
+        assert rel_err(v.cpu(), ref_v) <= 1e-5
+        if scatter:
+            ref_params = O.unpack(master.cpu(), olay, ref_params, False)
+            assert all(torch.equal(bits(a.cpu()), bits(b)) for a, b in zip(params, ref_params))
+        else:
+            assert all(torch.equal(bits(a.cpu()), bits(b)) for a, b in zip(params, ref_params))  # untouched
+        if flat_out:
+            assert torch.equal(bits(flat_param.cpu()), bits(O.cast_to(master.cpu(), param_dt)))
+    Z.zs_state_destroy(st)
+    Z.zs_layout_destroy(lay)
+
+
+def test_grad_norm_recompute_path_matches_check_path():
+    """zs_grad_norm with a shard argument (sum recomputed there) equals zs_unscale_check followed
+    by zs_grad_norm(NULL); a non-finite element seen only by the recompute still sets the flag."""
+    Z = _z()
+    dev = torch.device("cuda", 0)
+    n = 100_003
+    lay = Z.zs_layout_create([n], 1, 0)
+    s1 = Z.zs_state_create(lay, Z.state_host(2.0 ** 4, 1.0, True))
+    s2 = Z.zs_state_create(lay, Z.state_host(2.0 ** 4, 1.0, True))
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    x = torch.randn(n, generator=g, device=dev).mul_(16.0).to(torch.float16)
+    hp = Z.hparams(max_norm=0.5)
+    Z.zs_unscale_check(lay, x, torch.float16, s1)
+    Z.zs_grad_norm(lay, None, torch.float16, s1, hp)
+    Z.zs_grad_norm(lay, x, torch.float16, s2, hp)
+    a, b = Z.zs_state_read(s1), Z.zs_state_read(s2)
+    assert a.sumsq == b.sumsq and a.grad_norm == b.grad_norm and a.clip_coef == b.clip_coef and not a.overflow
+    want = O.sumsq_unscaled(x.cpu(), 2.0 ** 4)
+    assert abs(a.sumsq - want) <= 1e-12 * want
+    assert a.clip_coef == O.clip_coefficient(a.sumsq, 0.5)[1]
+    x[n // 3] = math.nan
+    Z.zs_grad_norm(lay, x, torch.float16, s2, hp)
+    assert Z.zs_state_read(s2).overflow == 1
+    Z.zs_state_destroy(s1)
+    Z.zs_state_destroy(s2)
+    Z.zs_layout_destroy(lay)
