@@ -89,14 +89,18 @@ __device__ __forceinline__ G16 ld16_vec(const uint16_t* p) {
 }
 __device__ __forceinline__ G16 ld16_elem(const uint16_t* p, int cnt) {
   G16 g = g16_zero();
-  for (int j = 0; j < cnt; ++j) g.set(j, p[j]);
+#pragma unroll
+  for (int j = 0; j < kGroup; ++j)
+    if (j < cnt) g.set(j, p[j]);
   return g;
 }
 __device__ __forceinline__ void st16_vec(uint16_t* p, const G16& g) {
   st_v4u(p, v4u{g.w[0], g.w[1], g.w[2], g.w[3]});
 }
 __device__ __forceinline__ void st16_elem(uint16_t* p, const G16& g, int cnt) {
-  for (int j = 0; j < cnt; ++j) p[j] = static_cast<uint16_t>(g.get(j));
+#pragma unroll
+  for (int j = 0; j < kGroup; ++j)
+    if (j < cnt) p[j] = static_cast<uint16_t>(g.get(j));
 }
 
 // ------------------------------------------------------------------ fixed-order reductions
@@ -142,6 +146,7 @@ struct TileSeg {
   int lo, hi;
   bool uniform;
   uint16_t* base;
+  int64_t seg_b, seg_e;  // range-relative bounds of the segment (uniform tiles)
 };
 
 __device__ __forceinline__ TileSeg tile_seg(const DevMap& mp, const uint64_t* ptrs, int64_t tile) {
@@ -150,12 +155,45 @@ __device__ __forceinline__ TileSeg tile_seg(const DevMap& mp, const uint64_t* pt
   t.hi = mp.tile_first[tile + 1];
   t.uniform = (t.lo == t.hi);
   t.base = nullptr;
+  t.seg_b = mp.seg_begin[t.lo];
+  t.seg_e = mp.seg_begin[t.lo + 1];
   if (t.uniform) {
     const int32_t tensor = mp.seg_tensor[t.lo];
-    if (tensor >= 0)
-      t.base = reinterpret_cast<uint16_t*>(ptrs[tensor]) + (mp.seg_local[t.lo] - mp.seg_begin[t.lo]);
+    if (tensor >= 0) t.base = reinterpret_cast<uint16_t*>(ptrs[tensor]) + (mp.seg_local[t.lo] - t.seg_b);
   }
   return t;
+}
+
+// Elements delta .. delta+7 of the 16-element sequence a | b (a first), delta in 1..7:
+// a funnel shift of 2-byte lanes across two aligned 16-byte chunks (v_alignbyte for odd
+// shifts).  delta is uniform across the workgroup.
+template <int D>
+__device__ __forceinline__ G16 funnel16_at(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3, uint32_t x4,
+                                           uint32_t x5, uint32_t x6, uint32_t x7) {
+  const uint32_t x[8] = {x0, x1, x2, x3, x4, x5, x6, x7};
+  constexpr int w = D >> 1;
+  G16 r;
+  if constexpr ((D & 1) == 0) {
+    r.w[0] = x[w]; r.w[1] = x[w + 1]; r.w[2] = x[w + 2]; r.w[3] = x[w + 3];
+  } else {
+    r.w[0] = __builtin_amdgcn_alignbyte(x[w + 1], x[w], 2);
+    r.w[1] = __builtin_amdgcn_alignbyte(x[w + 2], x[w + 1], 2);
+    r.w[2] = __builtin_amdgcn_alignbyte(x[w + 3], x[w + 2], 2);
+    r.w[3] = __builtin_amdgcn_alignbyte(x[w + 4], x[w + 3], 2);
+  }
+  return r;
+}
+
+__device__ __forceinline__ G16 funnel16(const v4u a, const v4u b, int delta) {
+  switch (delta) {
+    case 1: return funnel16_at<1>(a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w);
+    case 2: return funnel16_at<2>(a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w);
+    case 3: return funnel16_at<3>(a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w);
+    case 4: return funnel16_at<4>(a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w);
+    case 5: return funnel16_at<5>(a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w);
+    case 6: return funnel16_at<6>(a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w);
+    default: return funnel16_at<7>(a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w);
+  }
 }
 
 // Pointer to the tensor element of range index q in segment s (null for padding).
@@ -176,7 +214,9 @@ __device__ __forceinline__ G16 gather16(const DevMap& mp, const uint64_t* ptrs, 
     int s = seg_find(mp, ts.lo, ts.hi, q);
     if (mp.seg_begin[s + 1] < q + cnt) {  // the group straddles segments
       G16 g = g16_zero();
-      for (int j = 0; j < cnt; ++j) {
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        if (j >= cnt) break;
         const int64_t e = q + j;
         while (mp.seg_begin[s + 1] <= e) ++s;
         const uint16_t* p = seg_elem(mp, ptrs, s, e);
@@ -203,7 +243,9 @@ __device__ __forceinline__ void scatter(const DevMap& mp, const uint64_t* ptrs, 
   } else {
     int s = seg_find(mp, ts.lo, ts.hi, q);
     if (mp.seg_begin[s + 1] < q + cnt) {  // the group straddles segments
-      for (int j = 0; j < cnt; ++j) {
+#pragma unroll
+      for (int j = 0; j < W; ++j) {
+        if (j >= cnt) break;
         const int64_t e = q + j;
         while (mp.seg_begin[s + 1] <= e) ++s;
         uint16_t* p = seg_elem(mp, ptrs, s, e);
@@ -251,15 +293,34 @@ template <int SDT, bool TO_F32, bool CHECK>
 __global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __restrict__ ptrs,
                                                    void* __restrict__ dst, double* __restrict__ partials) {
   constexpr int kPackGroups = int(kPackBlock / (int64_t(kThreads) * kGroup));
+  constexpr int kChunks = int(kPackBlock / kGroup);  // 16-byte chunks of one block
+  __shared__ v4u stage[kChunks + 1];
   const int64_t block_base = work_unit() * kPackBlock;
   const TileSeg ts = tile_seg(mp, ptrs, block_base / kTile);
   G16 vals[kPackGroups];
   int cnts[kPackGroups];
+  // A full block inside one tensor whose source address is not 16-byte aligned: load the
+  // aligned chunks that cover it (all inside the tensor segment) through LDS and shift.
+  const int delta = (ts.base != nullptr) ? int((reinterpret_cast<uintptr_t>(ts.base + block_base) >> 1) & 7) : 0;
+  const bool staged = ts.uniform && ts.base != nullptr && delta != 0 && block_base + kPackBlock <= mp.len &&
+                      block_base - delta >= ts.seg_b && block_base - delta + kPackBlock + kGroup <= ts.seg_e;
+  if (staged) {
+    const v4u* chunk = reinterpret_cast<const v4u*>(ts.base + (block_base - delta));
+    for (int i = threadIdx.x; i <= kChunks; i += kThreads) stage[i] = ld_v4u(chunk + i);
+    __syncthreads();
 #pragma unroll
-  for (int u = 0; u < kPackGroups; ++u) {
-    const int64_t q = block_base + int64_t(u * kThreads + threadIdx.x) * kGroup;
-    cnts[u] = group_count(mp.len, q);
-    vals[u] = cnts[u] > 0 ? gather16(mp, ptrs, ts, q, cnts[u]) : g16_zero();
+    for (int u = 0; u < kPackGroups; ++u) {
+      const int k = u * kThreads + threadIdx.x;
+      cnts[u] = kGroup;
+      vals[u] = funnel16(stage[k], stage[k + 1], delta);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kPackGroups; ++u) {
+      const int64_t q = block_base + int64_t(u * kThreads + threadIdx.x) * kGroup;
+      cnts[u] = group_count(mp.len, q);
+      vals[u] = cnts[u] > 0 ? gather16(mp, ptrs, ts, q, cnts[u]) : g16_zero();
+    }
   }
   double acc = 0.0;
 #pragma unroll
@@ -277,7 +338,9 @@ __global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __
         st_v4f(d, v4f{f[0], f[1], f[2], f[3]});
         st_v4f(d + 4, v4f{f[4], f[5], f[6], f[7]});
       } else {
-        for (int j = 0; j < cnt; ++j) d[j] = f[j];
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j)
+          if (j < cnt) d[j] = f[j];
       }
     } else {
       uint16_t* d = static_cast<uint16_t*>(dst) + q;
@@ -478,10 +541,13 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const uint16_t* _
     } else {
       gv[u] = ld16_elem(shard + q, cnt);
       float pt[4] = {0.f, 0.f, 0.f, 0.f}, mt[4] = {0.f, 0.f, 0.f, 0.f}, vt[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int j = 0; j < cnt; ++j) {
-        pt[j] = master[q + j];
-        mt[j] = mom1[q + j];
-        vt[j] = mom2[q + j];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j < cnt) {
+          pt[j] = master[q + j];
+          mt[j] = mom1[q + j];
+          vt[j] = mom2[q + j];
+        }
       }
       pv[u] = v4f{pt[0], pt[1], pt[2], pt[3]};
       mv[u] = v4f{mt[0], mt[1], mt[2], mt[3]};
@@ -514,10 +580,13 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const uint16_t* _
       st_v4f(mom2 + q, v4f{v[0], v[1], v[2], v[3]});
       if (FLAT_OUT) st_v2u(flat_out + q, v2u{out.w[0], out.w[1]});
     } else {
-      for (int j = 0; j < cnt; ++j) {
-        master[q + j] = p[j];
-        mom1[q + j] = m[j];
-        mom2[q + j] = v[j];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j < cnt) {
+          master[q + j] = p[j];
+          mom1[q + j] = m[j];
+          mom2[q + j] = v[j];
+        }
       }
       if (FLAT_OUT) st16_elem(flat_out + q, out, cnt);
     }
@@ -557,7 +626,9 @@ __global__ __launch_bounds__(kThreads) void k_unpack(DevMap mp, const void* __re
           f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
           f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
         } else {
-          for (int j = 0; j < cnt; ++j) f[j] = s[j];
+#pragma unroll
+          for (int j = 0; j < kGroup; ++j)
+            if (j < cnt) f[j] = s[j];
         }
 #pragma unroll
         for (int j = 0; j < kGroup; ++j) vals[u].set(j, f2h<DDT>(f[j]));
