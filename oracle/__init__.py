@@ -8,6 +8,7 @@ does and shares no code with it.
 from .zs_oracle import (  # noqa: F401
     OracleLayout,
     OracleScaler,
+    accumulate,
     adamw_update,
     cast_to,
     clip_coefficient,

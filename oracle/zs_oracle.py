@@ -40,7 +40,7 @@ from dataclasses import dataclass
 
 import torch
 
-_EXP_MASK = {torch.float16: 0x7C00, torch.bfloat16: 0x7F80}
+_EXP_MASK = {torch.float16: 0x7C00, torch.bfloat16: 0x7F80, torch.float32: 0x7F800000}
 
 
 # ----------------------------------------------------------------------------------------------
@@ -103,6 +103,20 @@ def pack(tensors, layout: OracleLayout, dtype=None) -> torch.Tensor:
     return flat
 
 
+def accumulate(acc: torch.Tensor, tensors, layout: OracleLayout) -> torch.Tensor:
+    """Gradient accumulation over micro-steps into the flat buffer: acc + pack(tensors),
+    elementwise, rounded once to the buffer's dtype (fp32, or the model dtype).  The
+    optimizer steps only at the accumulation boundary ([BOOK] "Initializing a DeepSpeed
+    Engine": gradient reduction is accumulation-aware; gradient_accumulation_steps in the
+    DeepSpeed configs).  READING: each micro-step's sum is rounded once, to nearest even,
+    into the buffer's dtype.  It is evaluated in fp64 here; fp64 carries more than twice
+    the significand bits of fp32, bf16 and fp16 plus two, so rounding through fp64 equals
+    rounding the exact sum once.  The first micro-step of a window is a plain pack (with
+    widening to fp32 if wanted)."""
+    packed = pack(tensors, layout, acc.dtype)
+    return (acc.double() + packed.double()).to(acc.dtype)
+
+
 def shard_of(flat: torch.Tensor, layout: OracleLayout) -> torch.Tensor:
     """This rank's contiguous partition of the flat buffer [MEG]."""
     return flat[layout.shard_begin:layout.shard_begin + layout.shard_numel]
@@ -138,11 +152,15 @@ def cast_to(x: torch.Tensor, dtype) -> torch.Tensor:
 
 def nonfinite_any(x: torch.Tensor) -> bool:
     """True when any element is +inf, -inf or NaN, decided on the raw bits: the exponent
-    field is all ones.  READING: applied to bf16 as well as fp16."""
+    field is all ones.  READING: applied to bf16 as well as fp16 (and to an fp32
+    accumulation buffer)."""
     if x.numel() == 0:
         return False
     mask = _EXP_MASK[x.dtype]
-    bits = x.contiguous().view(torch.int16).to(torch.int32) & 0xFFFF
+    if x.dtype == torch.float32:
+        bits = x.contiguous().view(torch.int32).to(torch.int64) & 0xFFFFFFFF
+    else:
+        bits = x.contiguous().view(torch.int16).to(torch.int32) & 0xFFFF
     return bool(((bits & mask) == mask).any())
 
 

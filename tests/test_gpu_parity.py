@@ -414,3 +414,92 @@ def test_grad_norm_recompute_path_matches_check_path():
     Z.zs_state_destroy(s1)
     Z.zs_state_destroy(s2)
     Z.zs_layout_destroy(lay)
+
+
+@pytest.mark.parametrize("grad_dt", [torch.bfloat16, torch.float16])
+def test_no_write_outside_buffers_with_guard_regions(grad_dt):
+    """Poisoned guard regions: every tensor is a view at an odd element offset inside one big
+    canary-filled buffer, and the flat buffer and fp32 shards carry canaries on both sides.
+    After pack, check, norm, AdamW with scatter and flat output, unpack of the whole buffer
+    and of the shard, every canary is untouched and the results still match the oracle."""
+    from harness import bits
+    Z = _z()
+    dev = torch.device("cuda", 0)
+    gen_ = torch.Generator(device=dev)
+    gen_.manual_seed(11)
+    numels = [4096 * 3 + 5, 1, 17, 4096, 8191, 3, 12345, 64]
+    G = 37                                     # guard elements between and around tensors
+    CAN16 = -12345                             # canary bit pattern for 2-byte buffers
+    CAN32 = 0x7F7FBEEF
+
+    def carve(dtype, base_dtype_fill):
+        total = sum(numels) + G * (len(numels) + 1)
+        big = torch.full((total,), 0, dtype=torch.int16, device=dev)
+        big.fill_(base_dtype_fill)
+        views, off = [], G
+        for n in numels:
+            views.append(big[off:off + n].view(dtype))
+            off += n + G
+        return big, views
+
+    gbig, grads = carve(grad_dt, CAN16)
+    pbig, params = carve(grad_dt, CAN16)
+    for p in params:
+        p.copy_(torch.randn(p.numel(), generator=gen_, device=dev).mul_(0.02).to(grad_dt))
+    for g in grads:
+        g.copy_(torch.randn(g.numel(), generator=gen_, device=dev).mul_(1e-3).to(grad_dt))
+    d, r = 2, 1
+    lay = Z.zs_layout_create(numels, d, r, 1)
+    flat_numel, sb, sn = Z.zs_layout_info(lay)
+    olay = O.plan_layout(numels, d, r, 1)
+    st = Z.zs_state_create(lay, Z.state_host(1.0, 1.0, False))
+    fl_big = torch.full((flat_numel + 2 * 64,), CAN16, dtype=torch.int16, device=dev)
+    flat = fl_big[64:64 + flat_numel].view(grad_dt)
+    f32 = lambda: torch.full((sn + 2 * 64,), CAN32, dtype=torch.int32, device=dev)
+    mbig, m1big, v1big, fobig = f32(), f32(), f32(), torch.full((sn + 2 * 64,), CAN16, dtype=torch.int16, device=dev)
+    master, m, v = mbig[64:64 + sn].view(torch.float32), m1big[64:64 + sn].view(torch.float32), v1big[64:64 + sn].view(torch.float32)
+    flat_param = fobig[64:64 + sn].view(grad_dt)
+    m.zero_()
+    v.zero_()
+    pp, gp = Z.pointer_table(params, dev), Z.pointer_table(grads, dev)
+    params_before = [p.cpu() for p in params]
+    Z.zs_pack(lay, pp, grad_dt, master, torch.float32, whole_flat=False)
+    Z.zs_pack(lay, gp, grad_dt, flat, grad_dt, whole_flat=True)
+    exch = torch.zeros(d, dtype=torch.float64, device=dev)
+    for q in range(d):
+        lq = Z.zs_layout_create(numels, d, q, 1)
+        sq = Z.zs_state_create(lq, Z.state_host(1.0, 1.0, False))
+        Z.zs_unscale_check(lq, flat[q * sn:(q + 1) * sn], grad_dt, sq, None, exch[q:q + 1])
+        Z.zs_state_destroy(sq)
+        Z.zs_layout_destroy(lq)
+    shard = flat[sb:sb + sn]
+    Z.zs_unscale_check(lay, shard, grad_dt, st)
+    hp = Z.hparams()
+    Z.zs_grad_norm(lay, None, grad_dt, st, hp, exch, None)
+    Z.zs_adamw_step(lay, shard, grad_dt, master, m, v, hp, st, pp, flat_param, grad_dt)
+    Z.zs_unpack(lay, flat_param, grad_dt, False, pp, grad_dt)
+    Z.zs_unpack(lay, flat, grad_dt, True, gp, grad_dt)
+    Z.zs_scaler_update(st)
+    torch.cuda.synchronize()
+
+    def guards_ok(big, n_lead, n_body, can):
+        b = big.cpu()
+        return bool((b[:n_lead] == can).all()) and bool((b[n_lead + n_body:] == can).all())
+    assert guards_ok(fl_big, 64, flat_numel, CAN16)
+    for big in (mbig, m1big, v1big):
+        assert guards_ok(big, 64, sn, CAN32)
+    assert guards_ok(fobig, 64, sn, CAN16)
+    for big in (gbig, pbig):
+        b = big.cpu()
+        off = 0
+        for n in numels:
+            assert bool((b[off:off + G] == CAN16).all())
+            off += G + n
+        assert bool((b[off:] == CAN16).all())
+    # Results still right: packed buffer bit-exact, params = cast of the new master.
+    flat_ref = O.pack([x.cpu() for x in grads], olay)
+    assert torch.equal(bits(flat.cpu()), bits(flat_ref))
+    want = O.unpack(master.cpu(), olay, params_before, False)
+    assert all(torch.equal(bits(a.cpu()), bits(b)) for a, b in zip(params, want))
+    Z.zs_state_destroy(st)
+    Z.zs_layout_destroy(lay)

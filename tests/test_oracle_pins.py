@@ -425,3 +425,66 @@ def test_dp_split_equals_single_rank_when_unclipped():
             if a < b:
                 merged[a - owned.offsets[i]:b - owned.offsets[i]] = r.params[i][a - owned.offsets[i]:b - owned.offsets[i]]
         assert torch.equal(merged, single.params[i])
+
+
+# ------------------------------------------------------------------------------------------
+# Gradient accumulation into the flat buffer (the step before the path)
+# ------------------------------------------------------------------------------------------
+
+def test_accumulate_fp32_matches_exact_sums():
+    from fractions import Fraction as F
+    gen = torch.Generator().manual_seed(21)
+    numels = [37, 100, 5]
+    lay = O.plan_layout(numels, 1, 0)
+    micro = [[(torch.randn(n, generator=gen) * 10 ** k).to(torch.bfloat16) for n in numels] for k in (-3, 0, 2, -1)]
+    acc = O.pack(micro[0], lay, torch.float32)
+    for m in micro[1:]:
+        acc = O.accumulate(acc, m, lay)
+    flat = [O.pack(m, lay, torch.float32) for m in micro]
+    for i in range(lay.flat_numel):
+        # sequential fp32 accumulation: each step is the exact sum rounded once to fp32
+        x = flat[0][i].item()
+        for f in flat[1:]:
+            x = float(torch.tensor(float(F(x) + F(f[i].item())), dtype=torch.float32))
+        assert acc[i].item() == x
+
+
+def test_accumulate_model_dtype_rounds_to_nearest_even():
+    lay = O.plan_layout([4], 1, 0)
+    acc = torch.tensor([1.0, 1.0, 1.0 + 2 ** -7, 256.0], dtype=torch.bfloat16)
+    g = [torch.tensor([2 ** -8, 3 * 2 ** -8, 2 ** -8, 1.0], dtype=torch.bfloat16)]
+    out = O.accumulate(acc, g, lay)
+    # 1 + 2^-8 is a tie -> 1.0 (even); 1 + 3*2^-8 -> 1 + 2^-6; (1 + 2^-7) + 2^-8 is a tie -> 1 + 2^-6
+    # (even mantissa); 256 + 1 is a tie between 256 and 258 -> 256.
+    assert out.float().tolist() == [1.0, 1.0 + 2 ** -6, 1.0 + 2 ** -6, 256.0]
+
+
+def test_accumulate_then_step_equals_step_on_summed_gradient():
+    """G micro-steps accumulated in fp32 then one step == one step on the exactly summed
+    gradient, when every partial sum is exact (small integers)."""
+    numels = [64, 3]
+    lay = O.plan_layout(numels, 1, 0)
+    micro = [[torch.full((n,), float(k + 1), dtype=torch.float16) for n in numels] for k in range(4)]
+    acc = O.pack(micro[0], lay, torch.float32)
+    for m in micro[1:]:
+        acc = O.accumulate(acc, m, lay)
+    assert torch.equal(acc, torch.full((67,), 10.0))
+    hp = dict(HP)
+    r1 = O.OracleRank(numels, 1, 0, [torch.zeros(n, dtype=torch.float16) for n in numels],
+                      O.OracleScaler(1.0, dynamic=False), hp)
+    r2 = O.OracleRank(numels, 1, 0, [torch.zeros(n, dtype=torch.float16) for n in numels],
+                      O.OracleScaler(1.0, dynamic=False), hp)
+    r1.step(acc)
+    r2.step(torch.full((67,), 10.0, dtype=torch.float16))
+    assert torch.equal(r1.master, r2.master) and torch.equal(r1.v, r2.v)
+
+
+def test_nonfinite_flag_fp32_accumulator():
+    x = torch.zeros(10)
+    assert O.nonfinite_any(x) is False
+    for v in (math.inf, -math.inf, math.nan):
+        y = x.clone()
+        y[3] = v
+        assert O.nonfinite_any(y) is True
+    big = torch.tensor([3.4e38, -3.4e38, 1e-45])
+    assert O.nonfinite_any(big) is False
