@@ -144,21 +144,33 @@ zs_status zs_state_write(zs_state* state, const zs_state_host* in, void* stream)
  *   dst: whole_flat != 0 -> the flat buffer, flat_numel elements; whole_flat == 0 -> this
  *        rank's shard only, shard_numel elements.  Padding elements are written as zero.
  *   dst_dtype == src_dtype: bit copy (the gradient buffer); dst_dtype == ZS_FP32: exact
- *        widening (seeding the fp32 master from the model-dtype parameters).
+ *        widening (seeding the fp32 master from the model-dtype parameters, or the first
+ *        micro-step of an fp32 gradient-accumulation buffer).
  *   fuse_check: NULL, or a state to receive this pass's overflow flag and sum of squares
- *        (exactly what zs_unscale_check(dst) would compute with no other ranks); allowed
- *        only with dp_world == 1, whole_flat != 0 and dst_dtype == src_dtype.
+ *        of the packed values (what zs_unscale_check(dst) would compute with no other
+ *        ranks, up to summation order); allowed only with dp_world == 1 and whole_flat.
  * Errors: ZS_EINVAL on NULL pointers, unaligned dst, src_dtype not bf16/fp16, a disallowed
  * fuse_check; ZS_EUNSUPPORTED for other dtype pairs. */
 zs_status zs_pack(const zs_layout* layout, const void* src_ptrs, zs_dtype src_dtype, void* dst,
                   zs_dtype dst_dtype, int32_t whole_flat, zs_state* fuse_check, void* stream);
 
+/* Gradient accumulation across micro-steps: acc += pack(src), element by element, each sum
+ * rounded once (to nearest even) to acc_dtype; the optimizer steps only at the boundary
+ * ("Initializing a DeepSpeed Engine": accumulation-aware backward and step;
+ * gradient_accumulation_steps in the DeepSpeed configs).  acc_dtype is src_dtype or ZS_FP32
+ * (an fp32 main-gradient buffer, as in the Megatron distributed optimizer's ledger); the
+ * first micro-step of a window is a plain zs_pack into the same buffer.  Arguments, layout
+ * and errors as zs_pack; fuse_check receives the flag and sum of squares of the updated
+ * buffer, so the last micro-step can carry the check at dp_world == 1. */
+zs_status zs_pack_accumulate(const zs_layout* layout, const void* src_ptrs, zs_dtype src_dtype, void* acc,
+                             zs_dtype acc_dtype, int32_t whole_flat, zs_state* fuse_check, void* stream);
+
 /* Overflow check of this rank's gradient shard (the reduce-scatter output; one GPU: the
  * rank's slice of its packed buffer).  Sets state.overflow = (any element of `shard` is
  * +inf, -inf or NaN) OR (*ext_overflow != 0), and records the shard's sum of squares of the
  * unscaled gradient for zs_grad_norm ("nano-deepspeed", section 2: FP16 dynamic loss scaling).
- *   shard: device pointer to shard_numel elements of grad_dtype (bf16/fp16), any element
- *          alignment.
+ *   shard: device pointer to shard_numel elements of grad_dtype (bf16, fp16, or fp32 for
+ *          an fp32 accumulation buffer), aligned to its element size.
  *   ext_overflow: NULL or a device int32 holding the OR of the other ranks' flags.
  *   local_sumsq_out: NULL or a device double receiving this rank's sum of squares, the
  *          value the ranks exchange before zs_grad_norm (non-finite iff this shard holds a
@@ -194,14 +206,15 @@ zs_status zs_grad_norm(const zs_layout* layout, const void* shard, zs_dtype grad
  * evaluated in fp64 and rounded once to fp32 per stored value; the model-dtype parameter is
  * the round-to-nearest-even cast of the new fp32 master.  If state.overflow is set the call
  * changes nothing (device-side skip).  Does not advance step_t: zs_scaler_update does.
- *   shard: grad shard, shard_numel elements of grad_dtype.  master / m / v: device fp32
- *          arrays of shard_numel elements, updated in place.
+ *   shard: grad shard, shard_numel elements of grad_dtype (bf16, fp16 or fp32), aligned to
+ *          its element size.  master / m / v: device fp32 arrays of shard_numel elements,
+ *          updated in place.
  *   param_ptrs: NULL, or the device table of the n_tensors parameter tensors (param_dtype);
  *          the elements this rank owns are overwritten with the cast master.
  *   flat_param_out: NULL, or a device buffer of shard_numel param_dtype elements receiving
  *          the cast master in flat order (the all-gather input).
  * Errors: ZS_EINVAL on NULL required pointers, unaligned fp32 arrays / flat_param_out,
- * invalid hyper-parameters, param_dtype not bf16/fp16. */
+ * invalid hyper-parameters, grad_dtype not bf16/fp16/fp32, param_dtype not bf16/fp16. */
 zs_status zs_adamw_step(const zs_layout* layout, const void* shard, zs_dtype grad_dtype, float* master, float* m,
                         float* v, const zs_adamw_hparams* hp, zs_state* state, const void* param_ptrs,
                         void* flat_param_out, zs_dtype param_dtype, void* stream);

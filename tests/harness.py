@@ -363,3 +363,93 @@ def run_parity(wl, steps=None, align=None, dp_rank=None, check_every_step=True):
             Z.zs_layout_destroy(lq)
         opt.close()
     return report
+
+
+def run_parity_accumulation(wl, micro_steps, accum_dtype, steps=None, dp_rank=None):
+    """Gradient accumulation: `micro_steps` gradient lists per step are packed into the flat
+    buffer (first) and added to it (the rest, the last one fused with the check at dp 1),
+    in accum_dtype (fp32 or the model dtype); then the step.  Checks the accumulated buffer
+    bit-exactly against the oracle's accumulate() and the state against the 1e-5 contract."""
+    steps = wl.steps if steps is None else steps
+    rank = wl.dp_rank if dp_rank is None else dp_rank
+    d, align = wl.dp_world, wl.align
+    dev = torch.device("cuda", 0)
+    dt = gen.TORCH_DTYPE[wl.dtype]
+    hp = wl.hparams
+    params = gen.make_params(wl, dev)
+    opt = Z.ZeroShardedAdamW(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                             weight_decay=hp["weight_decay"], max_norm=hp["max_norm"], dp_world=d, dp_rank=rank,
+                             align=align, dynamic_loss_scale=wl.dynamic, init_scale=wl.init_scale,
+                             growth_interval=wl.growth_interval, accum_dtype=accum_dtype)
+    ref = O.OracleRank(wl.numels, d, rank, [p.cpu() for p in params], oracle_scaler(wl), hp, align)
+    lay = ref.layout
+    S = lay.shard_numel
+    others = {}
+    for q in range(d):
+        if q != rank:
+            lq = Z.zs_layout_create(wl.numels, d, q, align)
+            others[q] = (lq, Z.zs_state_create(lq, Z.state_host(wl.init_scale, 1.0, wl.dynamic, wl.growth_interval)))
+    exchange = torch.zeros(d, dtype=torch.float64, device=dev)
+    flags = []
+    try:
+        for step in range(1, steps + 1):
+            scale = ref.scaler.loss_scale
+            micro = [gen.make_grads(wl, step * 100 + k, scale, dev, with_faults=False) for k in range(micro_steps)]
+            for t, kk, val in wl.faults.get(step, []):   # the step's faults land on its last micro-step
+                micro[-1][t].view(-1)[kk] = val
+            for k, g in enumerate(micro):
+                opt.pack(g, accumulate=k > 0, last=k == micro_steps - 1)
+            if d == 1:
+                opt.norm()
+            else:
+                for q in range(d):
+                    if q == rank:
+                        opt.check(local_sumsq_out=exchange[q:q + 1])
+                    else:
+                        Z.zs_unscale_check(others[q][0], opt.flat[q * S:(q + 1) * S], opt.grad_dtype, others[q][1],
+                                           None, exchange[q:q + 1])
+                opt.norm(rank_sumsq=exchange)
+                for lq, sq in others.values():
+                    Z.zs_grad_norm(lq, None, opt.grad_dtype, sq, opt.hp, exchange, None)
+                    Z.zs_scaler_update(sq)
+            st_before = opt.read_state()
+            opt.update()
+            st = opt.read_state()
+            acc = O.pack([g.cpu() for g in micro[0]], lay, accum_dtype)
+            for g in micro[1:]:
+                acc = O.accumulate(acc, [x.cpu() for x in g], lay)
+            got_acc = opt.flat.cpu()
+            # Bit-exact, except that NaN payloads and signs are not part of the contract: any
+            # NaN in the buffer skips the step, and the oracle's own casts (torch's CPU
+            # kernels) do not fix one NaN encoding.
+            differ = (bits(got_acc) != bits(acc)) & ~(torch.isnan(got_acc.float()) & torch.isnan(acc.float()))
+            if bool(differ.any()):
+                bad = differ.nonzero().flatten()[:8].tolist()
+                raise AssertionError(f"step {step}: accumulated buffer differs at {len(bad)}+ positions, e.g. "
+                                     f"{[(i, hex(int(bits(got_acc)[i]) & 0xFFFFFFFF), hex(int(bits(acc)[i]) & 0xFFFFFFFF)) for i in bad]}")
+            other, ext = None, False
+            if d > 1:
+                other = []
+                for q in range(d):
+                    sq_ = acc[q * S:(q + 1) * S]
+                    bad = O.nonfinite_any(sq_)
+                    other.append(math.inf if bad else O.sumsq_unscaled(sq_, scale))
+                    ext = ext or (bad and q != rank)
+            rec = ref.step(O.shard_of(acc, lay), ext_overflow=ext, other_sumsq=other)
+            assert st_before["overflow"] == int(rec["overflow"]), f"step {step}: overflow differs"
+            assert st["loss_scale"] == ref.scaler.loss_scale and st["step_t"] == ref.scaler.step_t
+            if not rec["overflow"]:
+                assert abs(st_before["grad_norm"] - rec["norm"]) <= NORM_RTOL * rec["norm"]
+            assert rel_err(opt.master.cpu(), ref.master) <= REL_TOL
+            assert rel_err(opt.m.cpu(), ref.m) <= REL_TOL
+            assert rel_err(opt.v.cpu(), ref.v) <= REL_TOL
+            want = ref.params
+            ndiff = sum(int((bits(a.cpu()) != bits(b)).sum()) for a, b in zip(params, want))
+            assert ndiff <= int((bits(opt.master.cpu()) != bits(ref.master)).sum())
+            flags.append(int(rec["overflow"]))
+        return flags
+    finally:
+        for lq, sq in others.values():
+            Z.zs_state_destroy(sq)
+            Z.zs_layout_destroy(lq)
+        opt.close()

@@ -503,3 +503,19 @@ def test_no_write_outside_buffers_with_guard_regions(grad_dt):
     assert all(torch.equal(bits(a.cpu()), bits(b)) for a, b in zip(params, want))
     Z.zs_state_destroy(st)
     Z.zs_layout_destroy(lay)
+
+
+@pytest.mark.parametrize("name,accum", [("llama_mini", torch.float32), ("ragged_mini", torch.float32),
+                                        ("ragged_mini", None), ("moe_mini_dp4", torch.float32),
+                                        ("tiny", None), ("qwen_mini_dp2", None)])
+def test_gradient_accumulation_parity(name, accum):
+    """Gradient accumulation fused into the pack (3 micro-steps per step), in an fp32 buffer
+    or in the model dtype, against the oracle's accumulate(); injected faults land on the
+    last micro-step and must still skip the step."""
+    from harness import run_parity_accumulation
+    _z()
+    wl = WORKLOADS[name]
+    acc_dt = accum if accum is not None else gen.TORCH_DTYPE[wl.dtype]
+    print(f"[case] accumulation {name} accum={acc_dt}", flush=True)
+    flags = run_parity_accumulation(wl, 3, acc_dt, steps=min(wl.steps, 6))
+    assert [i + 1 for i, f in enumerate(flags) if f] == [s for s in sorted(wl.faults) if s <= min(wl.steps, 6)]

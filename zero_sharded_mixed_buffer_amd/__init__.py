@@ -24,6 +24,7 @@ from ._abi import (  # noqa: F401
     zs_layout_destroy,
     zs_layout_info,
     zs_pack,
+    zs_pack_accumulate,
     zs_plan,
     zs_plan_segments,
     zs_scaler_update,

@@ -55,6 +55,7 @@ _SIGS = {
     "zs_state_read": [c_void_p, POINTER(StateHost), c_void_p],
     "zs_state_write": [c_void_p, POINTER(StateHost), c_void_p],
     "zs_pack": [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p],
+    "zs_pack_accumulate": [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p],
     "zs_unscale_check": [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p],
     "zs_grad_norm": [c_void_p, c_void_p, c_int32, c_void_p, POINTER(AdamwHParams), c_void_p, c_void_p, c_void_p],
     "zs_adamw_step": [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, POINTER(AdamwHParams), c_void_p,
@@ -208,6 +209,11 @@ def hparams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_no
 def zs_pack(layout, src_ptrs, src_dtype, dst, dst_dtype, whole_flat=True, fuse_check=None, stream=None):
     _check(lib().zs_pack(layout, _ptr(src_ptrs), dtype_code(src_dtype), _ptr(dst), dtype_code(dst_dtype),
                          int(bool(whole_flat)), fuse_check, _stream(stream)), "zs_pack")
+
+
+def zs_pack_accumulate(layout, src_ptrs, src_dtype, acc, acc_dtype, whole_flat=True, fuse_check=None, stream=None):
+    _check(lib().zs_pack_accumulate(layout, _ptr(src_ptrs), dtype_code(src_dtype), _ptr(acc), dtype_code(acc_dtype),
+                                    int(bool(whole_flat)), fuse_check, _stream(stream)), "zs_pack_accumulate")
 
 
 def zs_unscale_check(layout, shard, grad_dtype, state, ext_overflow=None, local_sumsq_out=None, stream=None):

@@ -178,6 +178,10 @@ zs_status upload_map(const HostMap& h, void** mem, DevMap* out) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool is_half_dtype(int dt) { return dt == ZS_BF16 || dt == ZS_FP16; }
+bool is_grad_dtype(int dt) { return dt == ZS_BF16 || dt == ZS_FP16 || dt == ZS_FP32; }
+bool grad_aligned(const void* p, int dt) {
+  return (reinterpret_cast<uintptr_t>(p) & (dt == ZS_FP32 ? 3u : 1u)) == 0;
+}
 
 zs_status check_state_fields(const zs_state_host* s) {
   if (!is_pow2_double(s->loss_scale)) return fail(ZS_EINVAL, "loss_scale must be a positive power of two");
@@ -404,25 +408,28 @@ extern "C" zs_status zs_state_write(zs_state* s, const zs_state_host* in, void* 
 
 // ---------------------------------------------------------------------------- step ABI
 
-extern "C" zs_status zs_pack(const zs_layout* l, const void* src_ptrs, zs_dtype src_dtype, void* dst,
-                             zs_dtype dst_dtype, int32_t whole_flat, zs_state* fuse_check, void* stream) {
+namespace {
+
+zs_status pack_common(const zs_layout* l, const void* src_ptrs, zs_dtype src_dtype, void* dst, zs_dtype dst_dtype,
+                      int32_t whole_flat, bool accumulate, zs_state* fuse_check, void* stream, const char* what) {
   zs_status st = check_layout(l);
   if (st != ZS_OK) return st;
-  if (src_ptrs == nullptr || dst == nullptr) return fail(ZS_EINVAL, "src_ptrs or dst is NULL");
-  if (!is_half_dtype(src_dtype)) return fail(ZS_EINVAL, "src_dtype must be bf16 or fp16");
+  if (src_ptrs == nullptr || dst == nullptr) return fail(ZS_EINVAL, "%s: src_ptrs or dst is NULL", what);
+  if (!is_half_dtype(src_dtype)) return fail(ZS_EINVAL, "%s: src_dtype must be bf16 or fp16", what);
   if (dst_dtype != src_dtype && dst_dtype != ZS_FP32)
-    return fail(ZS_EUNSUPPORTED, "pack converts only to the same dtype or to fp32");
-  if (!aligned16(dst)) return fail(ZS_EINVAL, "dst must be 16-byte aligned");
+    return fail(ZS_EUNSUPPORTED, "%s: the buffer must have the source dtype or fp32", what);
+  if (!aligned16(dst)) return fail(ZS_EINVAL, "%s: the flat buffer must be 16-byte aligned", what);
   if (fuse_check != nullptr) {
     st = check_state(l, fuse_check);
     if (st != ZS_OK) return st;
-    if (l->plan.dp_world != 1 || !whole_flat || dst_dtype != src_dtype)
-      return fail(ZS_EINVAL, "fuse_check needs dp_world == 1, whole_flat and a same-dtype pack");
+    if (l->plan.dp_world != 1 || !whole_flat)
+      return fail(ZS_EINVAL, "%s: fuse_check needs dp_world == 1 and the whole flat buffer", what);
   }
   const DevMap& map = whole_flat ? l->map_full : l->map_shard;
   hipStream_t s = as_stream(stream);
   double* parts = fuse_check ? fuse_check->partials : nullptr;
-  hipError_t e = zs::launch_pack(map, static_cast<const uint64_t*>(src_ptrs), src_dtype, dst, dst_dtype, parts, s);
+  hipError_t e = zs::launch_pack(map, static_cast<const uint64_t*>(src_ptrs), src_dtype, dst, dst_dtype, accumulate,
+                                 parts, s);
   if (e != hipSuccess) return hip_fail(e, "launching pack");
   if (fuse_check) {
     const int64_t used = zs::reduction_blocks(map.len);
@@ -433,6 +440,19 @@ extern "C" zs_status zs_pack(const zs_layout* l, const void* src_ptrs, zs_dtype 
   return ok();
 }
 
+}  // namespace
+
+extern "C" zs_status zs_pack(const zs_layout* l, const void* src_ptrs, zs_dtype src_dtype, void* dst,
+                             zs_dtype dst_dtype, int32_t whole_flat, zs_state* fuse_check, void* stream) {
+  return pack_common(l, src_ptrs, src_dtype, dst, dst_dtype, whole_flat, false, fuse_check, stream, "zs_pack");
+}
+
+extern "C" zs_status zs_pack_accumulate(const zs_layout* l, const void* src_ptrs, zs_dtype src_dtype, void* acc,
+                                        zs_dtype acc_dtype, int32_t whole_flat, zs_state* fuse_check, void* stream) {
+  return pack_common(l, src_ptrs, src_dtype, acc, acc_dtype, whole_flat, true, fuse_check, stream,
+                     "zs_pack_accumulate");
+}
+
 extern "C" zs_status zs_unscale_check(const zs_layout* l, const void* shard, zs_dtype grad_dtype, zs_state* state,
                                       const int32_t* ext_overflow, double* local_sumsq_out, void* stream) {
   zs_status st = check_layout(l);
@@ -440,7 +460,8 @@ extern "C" zs_status zs_unscale_check(const zs_layout* l, const void* shard, zs_
   st = check_state(l, state);
   if (st != ZS_OK) return st;
   if (shard == nullptr) return fail(ZS_EINVAL, "shard is NULL");
-  if (!is_half_dtype(grad_dtype)) return fail(ZS_EINVAL, "grad_dtype must be bf16 or fp16");
+  if (!is_grad_dtype(grad_dtype)) return fail(ZS_EINVAL, "grad_dtype must be bf16, fp16 or fp32");
+  if (!grad_aligned(shard, grad_dtype)) return fail(ZS_EINVAL, "shard is not aligned to its element size");
   hipStream_t s = as_stream(stream);
   const int64_t n = l->plan.shard_numel;
   hipError_t e = zs::launch_check(shard, n, grad_dtype, state->partials, s);
@@ -465,7 +486,8 @@ extern "C" zs_status zs_grad_norm(const zs_layout* l, const void* shard, zs_dtyp
   hipStream_t s = as_stream(stream);
   hipError_t e;
   if (shard != nullptr) {
-    if (!is_half_dtype(grad_dtype)) return fail(ZS_EINVAL, "grad_dtype must be bf16 or fp16");
+    if (!is_grad_dtype(grad_dtype)) return fail(ZS_EINVAL, "grad_dtype must be bf16, fp16 or fp32");
+    if (!grad_aligned(shard, grad_dtype)) return fail(ZS_EINVAL, "shard is not aligned to its element size");
     const int64_t n = l->plan.shard_numel;
     e = zs::launch_check(shard, n, grad_dtype, state->partials, s);
     if (e != hipSuccess) return hip_fail(e, "launching check");
@@ -491,8 +513,9 @@ extern "C" zs_status zs_adamw_step(const zs_layout* l, const void* shard, zs_dty
   if (st != ZS_OK) return st;
   if (shard == nullptr || master == nullptr || m == nullptr || v == nullptr)
     return fail(ZS_EINVAL, "shard, master, m and v must not be NULL");
-  if (!is_half_dtype(grad_dtype) || !is_half_dtype(param_dtype))
-    return fail(ZS_EINVAL, "grad_dtype and param_dtype must be bf16 or fp16");
+  if (!is_grad_dtype(grad_dtype) || !is_half_dtype(param_dtype))
+    return fail(ZS_EINVAL, "grad_dtype must be bf16, fp16 or fp32 and param_dtype bf16 or fp16");
+  if (!grad_aligned(shard, grad_dtype)) return fail(ZS_EINVAL, "shard is not aligned to its element size");
   if (!aligned16(master) || !aligned16(m) || !aligned16(v)) return fail(ZS_EINVAL, "master, m, v must be 16-byte aligned");
   if (flat_param_out != nullptr && !aligned16(flat_param_out))
     return fail(ZS_EINVAL, "flat_param_out must be 16-byte aligned");

@@ -289,7 +289,7 @@ __device__ __forceinline__ double sumsq8(const G16& g) {
 // workgroup (one 8-element group per thread).  TO_F32: widen to fp32 (master seeding).  CHECK:
 // also write the fp64 sum of squares of this block's packed values to partials[blockIdx.x]
 // (a non-finite element makes that sum non-finite).
-template <int SDT, bool TO_F32, bool CHECK>
+template <int SDT, bool TO_F32, bool ACC, bool CHECK>
 __global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __restrict__ ptrs,
                                                    void* __restrict__ dst, double* __restrict__ partials) {
   constexpr int kPackGroups = int(kPackBlock / (int64_t(kThreads) * kGroup));
@@ -328,12 +328,32 @@ __global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __
     const int cnt = cnts[u];
     if (cnt <= 0) continue;
     const int64_t q = block_base + int64_t(u * kThreads + threadIdx.x) * kGroup;
-    if (CHECK) acc += sumsq8<SDT>(vals[u]);
     if (TO_F32) {
       float f[kGroup];
 #pragma unroll
       for (int j = 0; j < kGroup; ++j) f[j] = h2f<SDT>(vals[u].get(j));
       float* d = static_cast<float*>(dst) + q;
+      if (ACC) {  // one fp32 add: the exact sum rounded once
+        float old[kGroup] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (cnt == kGroup) {
+          const v4f a = ld_v4f(d), b = ld_v4f(d + 4);
+          old[0] = a.x; old[1] = a.y; old[2] = a.z; old[3] = a.w;
+          old[4] = b.x; old[5] = b.y; old[6] = b.z; old[7] = b.w;
+        } else {
+#pragma unroll
+          for (int j = 0; j < kGroup; ++j)
+            if (j < cnt) old[j] = d[j];
+        }
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) f[j] = old[j] + f[j];
+      }
+      if (CHECK) {
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) {
+          const double x = static_cast<double>(f[j]);
+          acc += (j < cnt) ? x * x : 0.0;
+        }
+      }
       if (cnt == kGroup) {
         st_v4f(d, v4f{f[0], f[1], f[2], f[3]});
         st_v4f(d + 4, v4f{f[4], f[5], f[6], f[7]});
@@ -344,10 +364,18 @@ __global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __
       }
     } else {
       uint16_t* d = static_cast<uint16_t*>(dst) + q;
+      G16 out = vals[u];
+      if (ACC) {  // fp32 add, then one rounding to the 2-byte dtype (the fp32 sum of two
+                  // 2-byte values rounds innocuously: fp32 has > 2p+2 significand bits)
+        const G16 old = (cnt == kGroup) ? ld16_vec(d) : ld16_elem(d, cnt);
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) out.set(j, f2h<SDT>(h2f<SDT>(old.get(j)) + h2f<SDT>(vals[u].get(j))));
+      }
+      if (CHECK) acc += sumsq8<SDT>(out);
       if (cnt == kGroup)
-        st16_vec(d, vals[u]);
+        st16_vec(d, out);
       else
-        st16_elem(d, vals[u], cnt);
+        st16_elem(d, out, cnt);
     }
   }
   if (CHECK) {
@@ -373,6 +401,36 @@ __global__ __launch_bounds__(kThreads) void k_check(const uint16_t* __restrict__
   double acc = 0.0;
 #pragma unroll
   for (int u = 0; u < kPackGroups; ++u) acc += sumsq8<DT>(vals[u]);
+  const double r = block_sum(acc);
+  if (threadIdx.x == 0) partials[blockIdx.x] = r;
+}
+
+// The same pass over an fp32 shard (a gradient-accumulation buffer).
+__global__ __launch_bounds__(kThreads) void k_check_f32(const float* __restrict__ shard, int64_t n,
+                                                        double* __restrict__ partials) {
+  constexpr int kPackGroups = int(kPackBlock / (int64_t(kThreads) * kGroup));
+  const bool vec_ok = aligned16(shard);
+  double acc = 0.0;
+#pragma unroll
+  for (int u = 0; u < kPackGroups; ++u) {
+    const int64_t q = work_unit() * kPackBlock + int64_t(u * kThreads + threadIdx.x) * kGroup;
+    const int cnt = group_count(n, q);
+    float f[kGroup] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (cnt == kGroup && vec_ok) {
+      const v4f a = ld_v4f(shard + q), b = ld_v4f(shard + q + 4);
+      f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+      f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j)
+        if (j < cnt) f[j] = shard[q + j];
+    }
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      const double x = static_cast<double>(f[j]);
+      acc += x * x;
+    }
+  }
   const double r = block_sum(acc);
   if (threadIdx.x == 0) partials[blockIdx.x] = r;
 }
@@ -506,8 +564,32 @@ __device__ __forceinline__ void adamw_elem(const StepScalars& k, float x, float&
 // 6 % extra HBM write traffic.
 constexpr int kQuadsPerThread = int(kTile / (int64_t(kThreads) * 4));
 
+// Four gradient values of one quad, as fp32 (exact for every input dtype).
+template <int GDT>
+__device__ __forceinline__ v4f load_grad4(const void* shard, int64_t q, int cnt, bool vec) {
+  if constexpr (GDT == ZS_FP32) {
+    const float* g = static_cast<const float*>(shard) + q;
+    if (cnt == 4 && vec) return ld_v4f(g);
+    float t[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < cnt) t[j] = g[j];
+    return v4f{t[0], t[1], t[2], t[3]};
+  } else {
+    const uint16_t* g = static_cast<const uint16_t*>(shard) + q;
+    G16 x;
+    if (cnt == 4 && vec) {
+      const v2u w = ld_v2u(g);
+      x = G16{{w.x, w.y, 0u, 0u}};
+    } else {
+      x = ld16_elem(g, cnt < 4 ? cnt : 4);
+    }
+    return v4f{h2f<GDT>(x.get(0)), h2f<GDT>(x.get(1)), h2f<GDT>(x.get(2)), h2f<GDT>(x.get(3))};
+  }
+}
+
 template <int GDT, int PDT, bool SCATTER, bool FLAT_OUT>
-__global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const uint16_t* __restrict__ shard,
+__global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const void* __restrict__ shard,
                                                     float* __restrict__ master, float* __restrict__ mom1,
                                                     float* __restrict__ mom2, AdamwArgs hp,
                                                     const DevState* __restrict__ st,
@@ -515,11 +597,11 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const uint16_t* _
                                                     uint16_t* __restrict__ flat_out) {
   if (st->h.overflow) return;  // device-side skip: nothing changes on an overflowed step
   const StepScalars k = step_scalars(hp, st);
-  const bool g_vec = aligned8(shard);
+  const bool g_vec = (GDT == ZS_FP32) ? aligned16(shard) : aligned8(shard);
   const int64_t n = mp.len;
   const int64_t tile = work_unit();
   const int64_t base = tile * kTile;
-  G16 gv[kQuadsPerThread];
+  v4f gv[kQuadsPerThread];
   v4f pv[kQuadsPerThread], mv[kQuadsPerThread], vv[kQuadsPerThread];
   int cnts[kQuadsPerThread];
 #pragma unroll
@@ -528,18 +610,12 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const uint16_t* _
     const int64_t rem = n - q;
     const int cnt = rem >= 4 ? 4 : (rem > 0 ? static_cast<int>(rem) : 0);
     cnts[u] = cnt;
+    gv[u] = load_grad4<GDT>(shard, q, cnt, g_vec);
     if (cnt == 4) {
-      if (g_vec) {
-        const v2u x = ld_v2u(shard + q);
-        gv[u] = G16{{x.x, x.y, 0u, 0u}};
-      } else {
-        gv[u] = ld16_elem(shard + q, 4);
-      }
       pv[u] = ld_v4f(master + q);
       mv[u] = ld_v4f(mom1 + q);
       vv[u] = ld_v4f(mom2 + q);
     } else {
-      gv[u] = ld16_elem(shard + q, cnt);
       float pt[4] = {0.f, 0.f, 0.f, 0.f}, mt[4] = {0.f, 0.f, 0.f, 0.f}, vt[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -571,7 +647,7 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const uint16_t* _
     G16 out = g16_zero();
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      adamw_elem(k, h2f<GDT>(gv[u].get(j)), p[j], m[j], v[j]);
+      adamw_elem(k, gv[u][j], p[j], m[j], v[j]);
       out.set(j, f2h<PDT>(p[j]));
     }
     if (cnt == 4) {
@@ -650,28 +726,38 @@ __global__ __launch_bounds__(kThreads) void k_unpack(DevMap mp, const void* __re
 
 // ------------------------------------------------------------------ launchers
 
-hipError_t launch_pack(const DevMap& map, const uint64_t* src_ptrs, int src_dt, void* dst, int dst_dt,
+template <int SDT>
+static void pack_dispatch(const dim3& G, hipStream_t s, const DevMap& map, const uint64_t* src_ptrs, void* dst,
+                          bool f32, bool acc, double* partials) {
+  const dim3 B(kThreads);
+  const bool chk = (partials != nullptr);
+#define ZS_PACK(F, A, C) hipLaunchKernelGGL((k_pack<SDT, F, A, C>), G, B, 0, s, map, src_ptrs, dst, partials)
+  if (f32) {
+    if (acc) {
+      if (chk) ZS_PACK(true, true, true); else ZS_PACK(true, true, false);
+    } else {
+      if (chk) ZS_PACK(true, false, true); else ZS_PACK(true, false, false);
+    }
+  } else {
+    if (acc) {
+      if (chk) ZS_PACK(false, true, true); else ZS_PACK(false, true, false);
+    } else {
+      if (chk) ZS_PACK(false, false, true); else ZS_PACK(false, false, false);
+    }
+  }
+#undef ZS_PACK
+}
+
+hipError_t launch_pack(const DevMap& map, const uint64_t* src_ptrs, int src_dt, void* dst, int dst_dt, bool accumulate,
                        double* partials, hipStream_t s) {
   const int64_t nb = reduction_blocks(map.len);
   if (nb == 0) return hipSuccess;
-  const dim3 G(static_cast<unsigned>(nb)), B(kThreads);
+  const dim3 G(static_cast<unsigned>(nb));
   const bool f32 = (dst_dt == ZS_FP32);
-  const bool chk = (partials != nullptr);
-  if (src_dt == ZS_BF16) {
-    if (f32)
-      hipLaunchKernelGGL((k_pack<ZS_BF16, true, false>), G, B, 0, s, map, src_ptrs, dst, partials);
-    else if (chk)
-      hipLaunchKernelGGL((k_pack<ZS_BF16, false, true>), G, B, 0, s, map, src_ptrs, dst, partials);
-    else
-      hipLaunchKernelGGL((k_pack<ZS_BF16, false, false>), G, B, 0, s, map, src_ptrs, dst, partials);
-  } else {
-    if (f32)
-      hipLaunchKernelGGL((k_pack<ZS_FP16, true, false>), G, B, 0, s, map, src_ptrs, dst, partials);
-    else if (chk)
-      hipLaunchKernelGGL((k_pack<ZS_FP16, false, true>), G, B, 0, s, map, src_ptrs, dst, partials);
-    else
-      hipLaunchKernelGGL((k_pack<ZS_FP16, false, false>), G, B, 0, s, map, src_ptrs, dst, partials);
-  }
+  if (src_dt == ZS_BF16)
+    pack_dispatch<ZS_BF16>(G, s, map, src_ptrs, dst, f32, accumulate, partials);
+  else
+    pack_dispatch<ZS_FP16>(G, s, map, src_ptrs, dst, f32, accumulate, partials);
   return hipGetLastError();
 }
 
@@ -682,8 +768,10 @@ hipError_t launch_check(const void* shard, int64_t n, int dt, double* partials, 
   const dim3 G(static_cast<unsigned>(nb)), B(kThreads);
   if (dt == ZS_BF16)
     hipLaunchKernelGGL((k_check<ZS_BF16>), G, B, 0, s, p, n, partials);
-  else
+  else if (dt == ZS_FP16)
     hipLaunchKernelGGL((k_check<ZS_FP16>), G, B, 0, s, p, n, partials);
+  else
+    hipLaunchKernelGGL(k_check_f32, G, B, 0, s, static_cast<const float*>(shard), n, partials);
   return hipGetLastError();
 }
 
@@ -719,7 +807,7 @@ hipError_t launch_scaler_update(DevState* st, hipStream_t s) {
 }
 
 template <int GDT, int PDT>
-static void adamw_dispatch(const dim3& G, hipStream_t s, const DevMap& map, const uint16_t* shard, float* master,
+static void adamw_dispatch(const dim3& G, hipStream_t s, const DevMap& map, const void* shard, float* master,
                            float* m, float* v, const AdamwArgs& hp, const DevState* st, const uint64_t* ptrs,
                            uint16_t* flat_out) {
   const dim3 B(kThreads);
@@ -737,21 +825,28 @@ static void adamw_dispatch(const dim3& G, hipStream_t s, const DevMap& map, cons
                        flat_out);
 }
 
+template <int GDT>
+static void adamw_dispatch_p(int param_dt, const dim3& G, hipStream_t s, const DevMap& map, const void* shard,
+                             float* master, float* m, float* v, const AdamwArgs& hp, const DevState* st,
+                             const uint64_t* ptrs, uint16_t* flat_out) {
+  if (param_dt == ZS_BF16)
+    adamw_dispatch<GDT, ZS_BF16>(G, s, map, shard, master, m, v, hp, st, ptrs, flat_out);
+  else
+    adamw_dispatch<GDT, ZS_FP16>(G, s, map, shard, master, m, v, hp, st, ptrs, flat_out);
+}
+
 hipError_t launch_adamw(const DevMap& map, const void* shard, int grad_dt, float* master, float* m, float* v,
                         const AdamwArgs& hp, const DevState* st, const uint64_t* param_ptrs, void* flat_out,
                         int param_dt, hipStream_t s) {
   if (map.ntiles == 0) return hipSuccess;
   const dim3 G(static_cast<unsigned>(map.ntiles));
-  const uint16_t* g = static_cast<const uint16_t*>(shard);
   uint16_t* fo = static_cast<uint16_t*>(flat_out);
-  if (grad_dt == ZS_BF16 && param_dt == ZS_BF16)
-    adamw_dispatch<ZS_BF16, ZS_BF16>(G, s, map, g, master, m, v, hp, st, param_ptrs, fo);
-  else if (grad_dt == ZS_FP16 && param_dt == ZS_FP16)
-    adamw_dispatch<ZS_FP16, ZS_FP16>(G, s, map, g, master, m, v, hp, st, param_ptrs, fo);
-  else if (grad_dt == ZS_BF16)
-    adamw_dispatch<ZS_BF16, ZS_FP16>(G, s, map, g, master, m, v, hp, st, param_ptrs, fo);
+  if (grad_dt == ZS_BF16)
+    adamw_dispatch_p<ZS_BF16>(param_dt, G, s, map, shard, master, m, v, hp, st, param_ptrs, fo);
+  else if (grad_dt == ZS_FP16)
+    adamw_dispatch_p<ZS_FP16>(param_dt, G, s, map, shard, master, m, v, hp, st, param_ptrs, fo);
   else
-    adamw_dispatch<ZS_FP16, ZS_BF16>(G, s, map, g, master, m, v, hp, st, param_ptrs, fo);
+    adamw_dispatch_p<ZS_FP32>(param_dt, G, s, map, shard, master, m, v, hp, st, param_ptrs, fo);
   return hipGetLastError();
 }
 

@@ -29,15 +29,18 @@ def pointer_table(tensors, device):
 class ZeroShardedAdamW:
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, max_norm=1.0,
                  dp_world=1, dp_rank=0, align=1, dynamic_loss_scale=None, init_scale=None, scale_floor=1.0,
-                 growth_interval=1000, grad_dtype=None):
+                 growth_interval=1000, grad_dtype=None, accum_dtype=None):
         params = list(params)
         if not params:
             raise ValueError("empty parameter list")
         self.device = params[0].device
         self.param_dtype = params[0].dtype
-        self.grad_dtype = grad_dtype or self.param_dtype
+        self.model_grad_dtype = grad_dtype or self.param_dtype
+        # The flat buffer holds the model-dtype gradients, or an fp32 accumulation buffer
+        # when accum_dtype=torch.float32 (gradient accumulation over micro-steps).
+        self.grad_dtype = accum_dtype or self.model_grad_dtype
         if dynamic_loss_scale is None:
-            dynamic_loss_scale = self.grad_dtype == torch.float16
+            dynamic_loss_scale = self.model_grad_dtype == torch.float16
         if init_scale is None:
             init_scale = 2.0 ** 16 if dynamic_loss_scale else 1.0
         self.params = params
@@ -74,12 +77,14 @@ class ZeroShardedAdamW:
             self._grad_key = key
         return self._grad_ptrs
 
-    def pack(self, grads, stream=None):
-        """Pack the per-parameter gradients into the flat buffer (fused with the overflow check
-        and sum of squares when there is one rank)."""
-        fuse = self.state if self.dp_world == 1 else None
-        A.zs_pack(self.layout, self._grad_table(grads), self.grad_dtype, self.flat, self.grad_dtype,
-                  whole_flat=True, fuse_check=fuse, stream=stream)
+    def pack(self, grads, stream=None, accumulate=False, last=True):
+        """Pack the per-parameter gradients into the flat buffer, or add them to it
+        (accumulate=True, a later micro-step).  The pass that ends a window (last=True) is
+        fused with the overflow check and sum of squares when there is one rank."""
+        fuse = self.state if (self.dp_world == 1 and last) else None
+        fn = A.zs_pack_accumulate if accumulate else A.zs_pack
+        fn(self.layout, self._grad_table(grads), self.model_grad_dtype, self.flat, self.grad_dtype,
+           whole_flat=True, fuse_check=fuse, stream=stream)
 
     def check(self, ext_overflow=None, local_sumsq_out=None, stream=None):
         """Overflow flag and local sum of squares of the shard (after the reduce-scatter);
@@ -98,11 +103,14 @@ class ZeroShardedAdamW:
         A.zs_scaler_update(self.state, stream=stream)
 
     def step(self, grads, stream=None):
-        """Whole single-rank step (dp_world == 1)."""
+        """Whole single-rank step (dp_world == 1).  `grads` is one gradient list, or a list of
+        micro-step gradient lists accumulated into the flat buffer before the step."""
         if self.dp_world != 1:
             raise ValueError("step() is the single-rank sequence; call pack/check/norm/update with the "
                              "other ranks' flag and partial sums for dp_world > 1")
-        self.pack(grads, stream)
+        micro = grads if (grads and isinstance(grads[0], (list, tuple))) else [grads]
+        for i, g in enumerate(micro):
+            self.pack(g, stream, accumulate=i > 0, last=i == len(micro) - 1)
         self.norm(stream=stream)
         self.update(stream=stream)
 
