@@ -112,6 +112,10 @@ def main():
     ap.add_argument("--cpu-baseline-elems", type=int, default=1 << 27)
     ap.add_argument("--cpu-baseline-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--grad-accum", type=int, default=1,
+                    help="micro-steps accumulated into the flat buffer before each optimizer step")
+    ap.add_argument("--accum-dtype", choices=["fp32", "model"], default="fp32",
+                    help="dtype of the accumulation buffer when --grad-accum > 1")
     ap.add_argument("--ceilings", action="store_true",
                     help="also time a device-to-device copy and a triad (torch kernels) as bandwidth yardsticks")
     args = ap.parse_args()
@@ -137,10 +141,12 @@ def main():
     grads = gen.make_grads(wl, 1, wl.init_scale, dev, with_faults=False)
     torch.cuda.synchronize()
     log(f"inputs resident after {time.perf_counter() - t_setup:.1f} s")
+    G = max(1, args.grad_accum)
+    accum = torch.float32 if (G > 1 and args.accum_dtype == "fp32") else None
     opt = Z.ZeroShardedAdamW(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
                              weight_decay=hp["weight_decay"], max_norm=hp["max_norm"], dp_world=wl.dp_world,
                              dp_rank=wl.dp_rank, align=wl.align, dynamic_loss_scale=wl.dynamic,
-                             init_scale=wl.init_scale, growth_interval=wl.growth_interval)
+                             init_scale=wl.init_scale, growth_interval=wl.growth_interval, accum_dtype=accum)
     if wl.dp_world != 1:
         print(json.dumps({"error": "bench times the single-rank step"}))
         sys.exit(2)
@@ -152,7 +158,13 @@ def main():
     def one_step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        opt.pack(grads, stream)
+        # G micro-steps: the first packs (widening to an fp32 buffer when accumulating in
+        # fp32), the rest add; the last pass carries the overflow check and sum of squares.
+        opt.pack(grads, stream, accumulate=False, last=G == 1)
+        if ev is not None:
+            ev[4].record(stream)
+        for k in range(1, G):
+            opt.pack(grads, stream, accumulate=True, last=k == G - 1)
         if ev is not None:
             ev[1].record(stream)
         opt.norm(stream=stream)
@@ -168,7 +180,7 @@ def main():
         one_step()
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -178,15 +190,19 @@ def main():
     state = opt.read_state()
     assert state["skipped_total"] == 0 and state["step_t"] == args.warmup + args.steps
     pack_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    first_pack_ms = sum(e[0].elapsed_time(e[4]) for e in evs) / args.steps
     adamw_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
     ms_per_step = elapsed * 1e3 / args.steps
-    adamw_bytes = 28 * S          # read g 2 + master/m/v 12, write master/m/v 12 + param 2
-    pack_bytes = 4 * N            # read 2 + write 2
+    gb = 4 if accum is not None else 2            # bytes per element of the flat gradient buffer
+    adamw_bytes = (gb + 26) * S   # read g + master/m/v 12, write master/m/v 12 + param 2
+    first_bytes = (2 + gb) * N    # read the tensors, write the buffer
+    acc_bytes = (2 + 2 * gb) * N  # read the tensors and the buffer, write the buffer
+    pack_bytes = first_bytes + (G - 1) * acc_bytes
     step_bytes = pack_bytes + adamw_bytes
     adamw_gbps = adamw_bytes / (adamw_ms * 1e-3) / 1e9
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
-    traffic = measured_traffic(wl.name)
-    log(f"step {ms_per_step:.3f} ms ({step_gbps:.0f} GB/s), pack {pack_ms:.3f} ms "
+    traffic = measured_traffic(wl.name) if G == 1 else None
+    log(f"step {ms_per_step:.3f} ms ({step_gbps:.0f} GB/s), pack{'+accumulate' if G > 1 else ''} {pack_ms:.3f} ms "
         f"({pack_bytes / pack_ms / 1e6:.0f} GB/s), adamw {adamw_ms:.3f} ms ({adamw_gbps:.0f} GB/s)")
     out = {
         "metric": "optimizer-step elements/s and achieved HBM GB/s (% of MI355X peak)",
@@ -203,12 +219,17 @@ def main():
         "storage": "bf16 grads and params, fp32 master/m/v; AdamW and norm arithmetic in fp64",
         "data": "synthetic: grads N(0,1e-3) and params N(0,0.02) drawn on the GPU, random init, no dataset",
         "config": {"workload": wl.name, "tensors": len(wl.numels), "elements": N, "dp_world": wl.dp_world,
-                   "shard_elements": S, "grad_dtype": wl.dtype, "align": wl.align},
+                   "shard_elements": S, "grad_dtype": wl.dtype, "align": wl.align, "grad_accum": G,
+                   "accum_dtype": ("fp32" if accum is not None else wl.dtype)},
         "achieved_hbm_gbps": step_gbps,
         "hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": step_bytes,
         "kernels_ms": {"pack_check": pack_ms, "adamw_cast_scatter": adamw_ms,
                        "finalize_and_scaler": ms_per_step - pack_ms - adamw_ms},
+        "accumulation": None if G == 1 else {
+            "first_pack_ms": first_pack_ms, "first_pack_gbps": first_bytes / first_pack_ms / 1e6,
+            "accumulate_ms_each": (pack_ms - first_pack_ms) / (G - 1),
+            "accumulate_gbps": acc_bytes * (G - 1) / (pack_ms - first_pack_ms) / 1e6},
         "roofline": {"bound": "hbm", "kernel": "k_adamw (AdamW + unscale + clip + cast + scatter)",
                      "achieved": adamw_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": adamw_gbps / HBM_PEAK_GBPS, "traffic": traffic,

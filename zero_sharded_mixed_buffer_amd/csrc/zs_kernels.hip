@@ -323,46 +323,59 @@ __global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __
     }
   }
   double acc = 0.0;
+  if (TO_F32) {
+    // fp32 destination: widen into LDS in element order, then move the block as
+    // lane-contiguous 16-byte rows (each wave instruction covers one contiguous 1 KiB, so
+    // every cache line is written - and, when accumulating, read - by one instruction).
+    __shared__ float wide[kPackBlock];
 #pragma unroll
-  for (int u = 0; u < kPackGroups; ++u) {
-    const int cnt = cnts[u];
-    if (cnt <= 0) continue;
-    const int64_t q = block_base + int64_t(u * kThreads + threadIdx.x) * kGroup;
-    if (TO_F32) {
-      float f[kGroup];
+    for (int u = 0; u < kPackGroups; ++u) {
+      const int e = (u * kThreads + threadIdx.x) * kGroup;
 #pragma unroll
-      for (int j = 0; j < kGroup; ++j) f[j] = h2f<SDT>(vals[u].get(j));
-      float* d = static_cast<float*>(dst) + q;
+      for (int j = 0; j < kGroup; ++j) wide[e + j] = h2f<SDT>(vals[u].get(j));
+    }
+    __syncthreads();
+    float* d = static_cast<float*>(dst) + block_base;
+    const int64_t rem = mp.len - block_base;
+    constexpr int kRows = int(kPackBlock / (int64_t(kThreads) * 4));
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      const int e = i * kThreads * 4 + threadIdx.x * 4;
+      const int64_t left = rem - e;
+      const int cnt = left >= 4 ? 4 : (left > 0 ? static_cast<int>(left) : 0);
+      if (cnt <= 0) continue;
+      float f[4] = {wide[e], wide[e + 1], wide[e + 2], wide[e + 3]};
       if (ACC) {  // one fp32 add: the exact sum rounded once
-        float old[kGroup] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (cnt == kGroup) {
-          const v4f a = ld_v4f(d), b = ld_v4f(d + 4);
-          old[0] = a.x; old[1] = a.y; old[2] = a.z; old[3] = a.w;
-          old[4] = b.x; old[5] = b.y; old[6] = b.z; old[7] = b.w;
+        if (cnt == 4) {
+          const v4f o = ld_v4f(d + e);
+          f[0] += o.x; f[1] += o.y; f[2] += o.z; f[3] += o.w;
         } else {
 #pragma unroll
-          for (int j = 0; j < kGroup; ++j)
-            if (j < cnt) old[j] = d[j];
+          for (int j = 0; j < 4; ++j)
+            if (j < cnt) f[j] += d[e + j];
         }
-#pragma unroll
-        for (int j = 0; j < kGroup; ++j) f[j] = old[j] + f[j];
       }
       if (CHECK) {
 #pragma unroll
-        for (int j = 0; j < kGroup; ++j) {
+        for (int j = 0; j < 4; ++j) {
           const double x = static_cast<double>(f[j]);
           acc += (j < cnt) ? x * x : 0.0;
         }
       }
-      if (cnt == kGroup) {
-        st_v4f(d, v4f{f[0], f[1], f[2], f[3]});
-        st_v4f(d + 4, v4f{f[4], f[5], f[6], f[7]});
+      if (cnt == 4) {
+        st_v4f(d + e, v4f{f[0], f[1], f[2], f[3]});
       } else {
 #pragma unroll
-        for (int j = 0; j < kGroup; ++j)
-          if (j < cnt) d[j] = f[j];
+        for (int j = 0; j < 4; ++j)
+          if (j < cnt) d[e + j] = f[j];
       }
-    } else {
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kPackGroups; ++u) {
+      const int cnt = cnts[u];
+      if (cnt <= 0) continue;
+      const int64_t q = block_base + int64_t(u * kThreads + threadIdx.x) * kGroup;
       uint16_t* d = static_cast<uint16_t*>(dst) + q;
       G16 out = vals[u];
       if (ACC) {  // fp32 add, then one rounding to the 2-byte dtype (the fp32 sum of two
