@@ -644,7 +644,16 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const void* __res
     }
   }
   TileSeg ts;
-  if (SCATTER) ts = tile_seg(mp, ptrs, tile);
+  // A full tile inside one parameter tensor whose address is not 16-byte aligned (ragged
+  // lists): the cast parameters go through LDS and leave as destination-aligned 16-byte
+  // chunks; only the at most 15 elements at the two ends of the tile are written singly.
+  __shared__ uint32_t pstage[kTile / 2];
+  int pdelta = 0;
+  if (SCATTER) {
+    ts = tile_seg(mp, ptrs, tile);
+    if (ts.uniform && ts.base != nullptr && base + kTile <= n)
+      pdelta = int((reinterpret_cast<uintptr_t>(ts.base + base) >> 1) & 7);
+  }
 #pragma unroll
   for (int u = 0; u < kQuadsPerThread; ++u) {
     const int cnt = cnts[u];
@@ -679,7 +688,31 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const void* __res
       }
       if (FLAT_OUT) st16_elem(flat_out + q, out, cnt);
     }
-    if (SCATTER) scatter<4>(mp, ptrs, ts, q, cnt, out);
+    if (SCATTER) {
+      if (pdelta != 0) {
+        const int e = u * kThreads * 4 + threadIdx.x * 4;  // tile-relative; cnt == 4 here
+        pstage[e / 2] = out.w[0];
+        pstage[e / 2 + 1] = out.w[1];
+      } else {
+        scatter<4>(mp, ptrs, ts, q, cnt, out);
+      }
+    }
+  }
+  if (SCATTER && pdelta != 0) {  // uniform across the workgroup
+    __syncthreads();
+    const v4u* L = reinterpret_cast<const v4u*>(pstage);
+    uint16_t* D = ts.base + base;            // destination of tile element 0
+    const int e0 = (8 - pdelta) & 7;         // first tile element at a 16-byte boundary
+    constexpr int kFull = int(kTile / kGroup) - 1;  // aligned chunks fully inside the tile
+    for (int c = threadIdx.x; c < kFull; c += kThreads)
+      st16_vec(D + e0 + c * kGroup, funnel16(L[c], L[c + 1], e0));
+    if (threadIdx.x < kGroup) {            // head [0, e0) and tail [e0 + 8*kFull, kTile)
+      const uint16_t* P = reinterpret_cast<const uint16_t*>(pstage);
+      const int h = threadIdx.x;
+      if (h < e0) D[h] = P[h];
+      const int t = e0 + kFull * kGroup + h;
+      if (t < kTile) D[t] = P[t];
+    }
   }
 }
 
