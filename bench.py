@@ -116,6 +116,10 @@ def main():
                     help="micro-steps accumulated into the flat buffer before each optimizer step")
     ap.add_argument("--accum-dtype", choices=["fp32", "model"], default="fp32",
                     help="dtype of the accumulation buffer when --grad-accum > 1")
+    ap.add_argument("--bucket-numel", type=int, default=0,
+                    help="pack the gradients in buckets of at least this many elements, in backward order "
+                         "(the pages' reduce_bucket_size is 500000000), then check the shard; 0 = one pack "
+                         "with the check fused")
     ap.add_argument("--ceilings", action="store_true",
                     help="also time a device-to-device copy and a triad (torch kernels) as bandwidth yardsticks")
     args = ap.parse_args()
@@ -154,17 +158,30 @@ def main():
     N = wl.n_elems
     stream = torch.cuda.current_stream()
     lay, st = opt.layout, opt.state
+    buckets = opt.buckets(args.bucket_numel) if args.bucket_numel > 0 else None
+    if buckets is not None:
+        log(f"{len(buckets)} buckets of >= {args.bucket_numel} elements")
+
+    def pack_pass(k):
+        if buckets is None:
+            opt.pack(grads, stream, accumulate=k > 0, last=k == G - 1)
+            return
+        for b in buckets:
+            opt.pack_bucket(grads, b, stream, accumulate=k > 0)
+        if k == G - 1:
+            opt.check(stream=stream)
 
     def one_step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         # G micro-steps: the first packs (widening to an fp32 buffer when accumulating in
-        # fp32), the rest add; the last pass carries the overflow check and sum of squares.
-        opt.pack(grads, stream, accumulate=False, last=G == 1)
+        # fp32), the rest add; the last pass carries the overflow check and sum of squares
+        # (fused into a whole pack, a separate pass over the shard after bucketed packs).
+        pack_pass(0)
         if ev is not None:
             ev[4].record(stream)
         for k in range(1, G):
-            opt.pack(grads, stream, accumulate=True, last=k == G - 1)
+            pack_pass(k)
         if ev is not None:
             ev[1].record(stream)
         opt.norm(stream=stream)
@@ -197,7 +214,8 @@ def main():
     adamw_bytes = (gb + 26) * S   # read g + master/m/v 12, write master/m/v 12 + param 2
     first_bytes = (2 + gb) * N    # read the tensors, write the buffer
     acc_bytes = (2 + 2 * gb) * N  # read the tensors and the buffer, write the buffer
-    pack_bytes = first_bytes + (G - 1) * acc_bytes
+    check_bytes = gb * S if buckets is not None else 0  # the separate check re-reads the shard
+    pack_bytes = first_bytes + (G - 1) * acc_bytes + check_bytes
     step_bytes = pack_bytes + adamw_bytes
     adamw_gbps = adamw_bytes / (adamw_ms * 1e-3) / 1e9
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -220,7 +238,8 @@ def main():
         "data": "synthetic: grads N(0,1e-3) and params N(0,0.02) drawn on the GPU, random init, no dataset",
         "config": {"workload": wl.name, "tensors": len(wl.numels), "elements": N, "dp_world": wl.dp_world,
                    "shard_elements": S, "grad_dtype": wl.dtype, "align": wl.align, "grad_accum": G,
-                   "accum_dtype": ("fp32" if accum is not None else wl.dtype)},
+                   "accum_dtype": ("fp32" if accum is not None else wl.dtype),
+                   "bucket_numel": args.bucket_numel or None, "buckets": len(buckets) if buckets else None},
         "achieved_hbm_gbps": step_gbps,
         "hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": step_bytes,

@@ -165,6 +165,40 @@ zs_status zs_pack(const zs_layout* layout, const void* src_ptrs, zs_dtype src_dt
 zs_status zs_pack_accumulate(const zs_layout* layout, const void* src_ptrs, zs_dtype src_dtype, void* acc,
                              zs_dtype acc_dtype, int32_t whole_flat, zs_state* fuse_check, void* stream);
 
+/* Bucketed packing: communication starts on a bucket of gradients as soon as backward has
+ * produced all of them ("Deep dive: Megatron", section "Distributed optimizer": contiguous
+ * buffers let communication begin bucket by bucket; "3.7 Megatron-LM, DeepSpeed &
+ * Parallelism in Practice", section "DeepSpeed config for this run": reduce_bucket_size of
+ * 5e8 elements; "nano-deepspeed", section 2: a packed bucket).
+ * A bucket is a contiguous range [tensor_begin, tensor_end) of the parameter list.  It owns
+ * the flat range [offset(tensor_begin), offset(tensor_end)), where offset(n_tensors) is
+ * flat_numel: the alignment gap after a tensor and the tail padding belong to the bucket
+ * before them, so the buckets of any partition of the tensor list tile the flat buffer.
+ *
+ * zs_plan_buckets: host only, no GPU.  Walks the tensors from last to first (the order in
+ *   which backward produces their gradients) and closes a bucket once it holds at least
+ *   bucket_numel elements (the first tensor closes the last bucket).  bounds_out (NULL, or
+ *   room for 2 * n_tensors int32) receives [tensor_begin, tensor_end) pairs in closing
+ *   order; *n_buckets_out their number.  A tensor larger than bucket_numel is a bucket by
+ *   itself; a tensor is never split.  Errors: ZS_EINVAL on a NULL n_buckets_out, negative
+ *   numels or bucket_numel <= 0.
+ * zs_bucket_range: host only.  The flat range a bucket owns.  Errors: ZS_EINVAL unless
+ *   0 <= tensor_begin < tensor_end <= n_tensors.
+ * zs_pack_bucket: writes the bucket's flat range of the whole flat buffer `flat` (flat_numel
+ *   elements of flat_dtype) and nothing else, exactly as zs_pack(whole_flat = 1) or, with
+ *   accumulate != 0, zs_pack_accumulate would write that range.  flat_dtype is src_dtype or
+ *   ZS_FP32 (an fp32 communication buffer: exact widening).  Buckets with disjoint ranges
+ *   may run concurrently on different streams.  No overflow check is fused: the check runs
+ *   on the reduced shard (zs_unscale_check).  Errors: as zs_pack, and ZS_EINVAL for a bad
+ *   tensor range. */
+zs_status zs_plan_buckets(const int64_t* numels, int32_t n_tensors, int64_t bucket_numel, int32_t* bounds_out,
+                          int32_t* n_buckets_out);
+zs_status zs_bucket_range(const zs_layout* layout, int32_t tensor_begin, int32_t tensor_end, int64_t* flat_begin,
+                          int64_t* flat_end);
+zs_status zs_pack_bucket(const zs_layout* layout, const void* src_ptrs, zs_dtype src_dtype, void* flat,
+                         zs_dtype flat_dtype, int32_t tensor_begin, int32_t tensor_end, int32_t accumulate,
+                         void* stream);
+
 /* Overflow check of this rank's gradient shard (the reduce-scatter output; one GPU: the
  * rank's slice of its packed buffer).  Sets state.overflow = (any element of `shard` is
  * +inf, -inf or NaN) OR (*ext_overflow != 0), and records the shard's sum of squares of the

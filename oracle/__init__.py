@@ -9,12 +9,15 @@ from .zs_oracle import (  # noqa: F401
     OracleLayout,
     OracleScaler,
     accumulate,
+    bucket_range,
     adamw_update,
     cast_to,
     clip_coefficient,
     global_sumsq,
     nonfinite_any,
     pack,
+    pack_bucket,
+    plan_buckets,
     plan_layout,
     scaler_update,
     shard_of,

@@ -117,6 +117,52 @@ def accumulate(acc: torch.Tensor, tensors, layout: OracleLayout) -> torch.Tensor
     return (acc.double() + packed.double()).to(acc.dtype)
 
 
+def plan_buckets(numels, bucket_numel):
+    """Split the parameter list into gradient buckets.  Backward produces gradients from
+    the last tensor to the first; a bucket collects them in that order and is closed (and
+    its communication may start) once it holds at least bucket_numel elements; the first
+    tensor closes the last bucket.  Returns [tensor_begin, tensor_end) pairs in closing
+    order.  ([MEG] contiguous buffers let communication start as buckets become ready;
+    [BOOK] "DeepSpeed config for this run": reduce_bucket_size 5e8.)
+    READING: the pages give only the size knob; a bucket never splits a tensor, so a
+    tensor above the size is a bucket of its own."""
+    if bucket_numel <= 0 or any(n < 0 for n in numels):
+        raise ValueError("bucket size must be positive and sizes non-negative")
+    buckets = []
+    members = []
+    for t in reversed(range(len(numels))):
+        members.append(t)
+        if sum(numels[i] for i in members) >= bucket_numel or t == 0:
+            buckets.append((min(members), max(members) + 1))
+            members = []
+    return buckets
+
+
+def bucket_range(layout: OracleLayout, tensor_begin, tensor_end):
+    """Flat range owned by the bucket of tensors [tensor_begin, tensor_end): from the
+    offset of its first tensor up to the offset of the tensor after its last one (the end
+    of the buffer for the last tensor).  READING: the alignment gap behind a tensor and
+    the tail padding go with the bucket in front of them, so the buckets of any split of
+    the parameter list cover the flat buffer once."""
+    n = len(layout.numels)
+    if not (0 <= tensor_begin < tensor_end <= n):
+        raise ValueError("not a non-empty tensor range")
+    begin = layout.offsets[tensor_begin]
+    end = layout.flat_numel if tensor_end == n else layout.offsets[tensor_end]
+    return begin, end
+
+
+def pack_bucket(flat: torch.Tensor, tensors, layout: OracleLayout, tensor_begin, tensor_end, accumulate_into=False):
+    """The flat buffer after packing one bucket into it: the bucket's range becomes the
+    same range of pack(tensors) (or of accumulate(flat, tensors) with accumulate_into);
+    every other element keeps its value."""
+    begin, end = bucket_range(layout, tensor_begin, tensor_end)
+    full = accumulate(flat, tensors, layout) if accumulate_into else pack(tensors, layout, flat.dtype)
+    out = flat.clone()
+    out[begin:end] = full[begin:end]
+    return out
+
+
 def shard_of(flat: torch.Tensor, layout: OracleLayout) -> torch.Tensor:
     """This rank's contiguous partition of the flat buffer [MEG]."""
     return flat[layout.shard_begin:layout.shard_begin + layout.shard_numel]

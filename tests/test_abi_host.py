@@ -115,3 +115,31 @@ def test_device_calls_fail_cleanly_without_gpu():
     with pytest.raises(Z.ZsError) as e:
         Z.zs_pack(None, 0, 0, 0, 0, stream=0)
     assert e.value.status == -1
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_bucket_plan_matches_oracle(seed):
+    Z = _z()
+    rng = random.Random(300 + seed)
+    numels = [rng.choice([0, 1, 5, 64, 1000, 4096, 70000]) for _ in range(rng.randint(1, 80))]
+    size = rng.choice([1, 100, 4096, 50000, 10 ** 6, 10 ** 9])
+    assert Z.zs_plan_buckets(numels, size) == O.plan_buckets(numels, size)
+
+
+def test_bucket_plan_at_the_pages_bucket_size():
+    # 5e8-element buckets over an 8-billion-element Llama-3-8B-shaped tensor list.
+    Z = _z()
+    from workloads import WORKLOADS
+    numels = list(WORKLOADS["llama3_8b"].numels)
+    got = Z.zs_plan_buckets(numels, 500_000_000)
+    assert got == O.plan_buckets(numels, 500_000_000)
+    assert got[0][1] == len(numels) and got[-1][0] == 0 and 12 <= len(got) <= 17
+
+
+def test_bucket_plan_rejects_bad_arguments():
+    Z = _z()
+    for numels, size in (([4, 5], 0), ([4, -1], 8)):
+        with pytest.raises(Z.ZsError) as e:
+            Z.zs_plan_buckets(numels, size)
+        assert e.value.status == -1
+    assert Z.zs_plan_buckets([], 10) == []

@@ -28,3 +28,60 @@ def test_fullsize_sampled_parity(name, steps):
     worst, ndiff, wins = run_parity_sampled(wl, steps=steps, log=lambda s: print(s, flush=True))
     print(f"[fullsize] {name}: {len(wins)} windows, worst={worst}, ndiff={ndiff}, {time.time() - t0:.1f} s",
           flush=True)
+
+
+@pytest.mark.parametrize("name,flat_kind", [("llama3_8b", "model"), ("llama3_8b", "fp32"), ("ragged_20k", "model")])
+def test_fullsize_bucketed_pack(name, flat_kind):
+    """The full-size gradient list packed in 5e8-element buckets (the pages' reduce_bucket_size),
+    in backward order, into a garbage buffer; sampled windows around every bucket boundary
+    and at random places equal the oracle's pack of those windows bit for bit, and the
+    whole buffer equals the single-launch pack bit for bit."""
+    import random
+
+    import torch
+
+    import oracle as O
+    import zero_sharded_mixed_buffer_amd as Z
+    from workloads import gen
+    Z.lib()
+    wl = WORKLOADS[name]
+    dev = torch.device("cuda", 0)
+    dt = gen.TORCH_DTYPE[wl.dtype]
+    flat_dt = torch.float32 if flat_kind == "fp32" else dt
+    numels = list(wl.numels)
+    buckets = Z.zs_plan_buckets(numels, 500_000_000)
+    assert buckets == O.plan_buckets(numels, 500_000_000)
+    print(f"[case] fullsize buckets {name} flat={flat_dt}: {len(buckets)} buckets", flush=True)
+    lay = Z.zs_layout_create(numels, wl.dp_world, wl.dp_rank, wl.align)
+    olay = O.plan_layout(numels, wl.dp_world, wl.dp_rank, wl.align)
+    grads = gen.make_grads(wl, 1, wl.init_scale, dev, with_faults=False)
+    ptrs = Z.pointer_table(grads, dev)
+    ibits = torch.int32 if flat_dt == torch.float32 else torch.int16
+    flat = torch.full((olay.flat_numel,), -1, dtype=ibits, device=dev).view(flat_dt)  # NaN bits
+    for a, b in buckets:
+        Z.zs_pack_bucket(lay, ptrs, dt, flat, flat_dt, a, b)
+    torch.cuda.synchronize()
+    # windows: both sides of every bucket boundary, the ends, random places
+    W = 1 << 14
+    starts = set()
+    for a, b in buckets:
+        lo, hi = O.bucket_range(olay, a, b)
+        for edge in (lo, hi):
+            starts.add(min(max(edge - W // 2, 0), olay.flat_numel - W))
+    rng = random.Random(11)
+    starts.update(rng.randrange(0, olay.flat_numel - W) for _ in range(24))
+    for s0 in sorted(starts):
+        want = torch.zeros(W, dtype=flat_dt)
+        for t, off, n in zip(grads, olay.offsets, olay.numels):
+            x, y = max(off, s0), min(off + n, s0 + W)
+            if x < y:
+                want[x - s0:y - s0] = t.view(-1)[x - off:y - off].cpu().to(flat_dt)
+        got = flat[s0:s0 + W].cpu()
+        assert torch.equal(got.view(ibits), want.view(ibits)), f"window at {s0}"
+    whole = torch.empty_like(flat)
+    Z.zs_pack(lay, ptrs, dt, whole, flat_dt, whole_flat=True)
+    torch.cuda.synchronize()
+    assert torch.equal(whole.view(ibits), flat.view(ibits))
+    print(f"[fullsize] buckets {name} flat={flat_dt}: {len(starts)} windows equal", flush=True)
+    del whole, flat, grads
+    Z.zs_layout_destroy(lay)

@@ -136,3 +136,35 @@ def test_scaler_mistakes_are_caught(monkeypatch, kind):
     _patch(monkeypatch, "scaler_update", f)
     assert _fails(P.test_scaler_tiny_config_sequence, P.test_scaler_growth_and_backoff_sequence,
                   P.test_scaler_floor_and_static, P.test_scaler_doubles_once_per_window), kind
+
+
+@pytest.mark.parametrize("kind", ["strict_threshold", "forward_walk", "last_bucket_dropped"])
+def test_bucket_plan_mistakes_are_caught(monkeypatch, kind):
+    def wrong(numels, size):
+        order = range(len(numels)) if kind == "forward_walk" else reversed(range(len(numels)))
+        out, members = [], []
+        for t in order:
+            members.append(t)
+            full = sum(numels[i] for i in members)
+            closes = full > size if kind == "strict_threshold" else full >= size
+            edge = (t == len(numels) - 1) if kind == "forward_walk" else (t == 0)
+            if closes or (edge and kind != "last_bucket_dropped"):
+                out.append((min(members), max(members) + 1))
+                members = []
+        return out
+    _patch(monkeypatch, "plan_buckets", wrong)
+    assert _fails(P.test_plan_buckets_hand_tables, *(lambda s=s: P.test_plan_buckets_against_suffix_sum_definition(s)
+                                                    for s in range(6))), kind
+
+
+@pytest.mark.parametrize("kind", ["end_at_last_element", "begin_after_gap"])
+def test_bucket_range_mistakes_are_caught(monkeypatch, kind):
+    def wrong(layout, a, b):
+        if kind == "end_at_last_element":  # drops the gap behind the last tensor and the tail
+            return layout.offsets[a], layout.offsets[b - 1] + layout.numels[b - 1]
+        begin = layout.offsets[a] if a == 0 else layout.offsets[a - 1] + layout.numels[a - 1]
+        end = layout.flat_numel if b == len(layout.numels) else layout.offsets[b - 1] + layout.numels[b - 1]
+        return begin, end
+    _patch(monkeypatch, "bucket_range", wrong)
+    assert _fails(P.test_bucket_range_hand_table, lambda: P.test_bucket_ranges_tile_the_flat_buffer(64, 4),
+                  lambda: P.test_buckets_in_any_order_rebuild_the_whole_pack(False)), kind

@@ -488,3 +488,91 @@ def test_nonfinite_flag_fp32_accumulator():
         assert O.nonfinite_any(y) is True
     big = torch.tensor([3.4e38, -3.4e38, 1e-45])
     assert O.nonfinite_any(big) is False
+
+
+# ------------------------------------------------------------------------------------------
+# Gradient buckets ("Deep dive: Megatron", section "Distributed optimizer": communication
+# starts as buckets of the contiguous buffer become ready; "DeepSpeed config for this run":
+# reduce_bucket_size).
+# ------------------------------------------------------------------------------------------
+
+def test_plan_buckets_hand_tables():
+    # Worked by hand: walk 4,3 | 2,5 | 3 from the end with a bucket size of 6.
+    assert O.plan_buckets([3, 5, 2, 7, 1], 6) == [(3, 5), (1, 3), (0, 1)]
+    assert O.plan_buckets([3, 5, 2, 7, 1], 100) == [(0, 5)]
+    assert O.plan_buckets([3, 5, 2, 7, 1], 1) == [(4, 5), (3, 4), (2, 3), (1, 2), (0, 1)]
+    # A tensor above the size is a bucket of its own; it is never split.
+    assert O.plan_buckets([2, 50, 2], 10) == [(1, 3), (0, 1)]
+    # An empty tensor adds nothing and joins the bucket being filled.
+    assert O.plan_buckets([4, 0, 4], 4) == [(2, 3), (0, 2)]
+    assert O.plan_buckets([7], 3) == [(0, 1)]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_plan_buckets_against_suffix_sum_definition(seed):
+    # The same split from prefix sums: a bucket ending at `hi` starts at the largest t
+    # with numels[t:hi] >= size, or at 0 when there is none.
+    rng = np.random.default_rng(seed)
+    numels = [int(x) for x in rng.integers(0, 40, size=int(rng.integers(1, 30)))]
+    size = int(rng.integers(1, 90))
+    pre = np.concatenate([[0], np.cumsum(numels)])
+    want, hi = [], len(numels)
+    while hi > 0:
+        ok = [t for t in range(hi) if pre[hi] - pre[t] >= size]
+        lo = max(ok) if ok else 0
+        want.append((lo, hi))
+        hi = lo
+    assert O.plan_buckets(numels, size) == want
+
+
+def test_bucket_range_hand_table():
+    # sizes 5, 3, 10 at a 8-element alignment: offsets 0, 8, 16, flat length 32.  The gap
+    # behind a tensor and the tail belong to the bucket in front of them.
+    lay = O.plan_layout([5, 3, 10], 1, 0, 8)
+    assert (lay.offsets, lay.flat_numel) == ([0, 8, 16], 32)
+    assert O.bucket_range(lay, 0, 1) == (0, 8)
+    assert O.bucket_range(lay, 1, 2) == (8, 16)
+    assert O.bucket_range(lay, 2, 3) == (16, 32)
+    assert O.bucket_range(lay, 0, 2) == (0, 16)
+    assert O.bucket_range(lay, 0, 3) == (0, 32)
+
+
+@pytest.mark.parametrize("align,dp_world", [(1, 1), (64, 4), (8, 3)])
+def test_bucket_ranges_tile_the_flat_buffer(align, dp_world):
+    rng = np.random.default_rng(align + dp_world)
+    numels = [int(x) for x in rng.integers(0, 300, size=23)]
+    lay = O.plan_layout(numels, dp_world, 0, align)
+    cuts = sorted(set(int(c) for c in rng.integers(1, 23, size=6)))
+    bounds = list(zip([0] + cuts, cuts + [23]))
+    ranges = [O.bucket_range(lay, a, b) for a, b in bounds]
+    assert ranges[0][0] == 0 and ranges[-1][1] == lay.flat_numel
+    for (b0, e0), (b1, _) in zip(ranges, ranges[1:]):
+        assert e0 == b1
+    for (a, b), (lo, hi) in zip(bounds, ranges):
+        for t in range(a, b):  # every element of a member tensor lies inside its bucket
+            assert lo <= lay.offsets[t] and lay.offsets[t] + numels[t] <= hi
+    with pytest.raises(ValueError):
+        O.bucket_range(lay, 3, 3)
+
+
+@pytest.mark.parametrize("accumulate_into", [False, True])
+def test_buckets_in_any_order_rebuild_the_whole_pack(accumulate_into):
+    torch.manual_seed(7)
+    numels = [5, 0, 17, 64, 3, 129, 1, 40]
+    lay = O.plan_layout(numels, 2, 1, 8)
+    ts = [torch.randn(n).to(torch.bfloat16) for n in numels]
+    start = torch.randn(lay.flat_numel).to(torch.bfloat16)
+    # concatenation with zero gaps, built directly from the offsets
+    cat = torch.zeros(lay.flat_numel, dtype=torch.bfloat16)
+    for t, off in zip(ts, lay.offsets):
+        cat[off:off + t.numel()] = t
+    want = (start.double() + cat.double()).to(torch.bfloat16) if accumulate_into else cat
+    buf = start.clone()
+    for a, b in [(5, 8), (0, 2), (2, 5)]:
+        buf = O.pack_bucket(buf, ts, lay, a, b, accumulate_into=accumulate_into)
+    assert torch.equal(buf.view(torch.int16), want.view(torch.int16))
+    # one bucket touches its own range only
+    one = O.pack_bucket(start, ts, lay, 2, 5, accumulate_into=accumulate_into)
+    lo, hi = O.bucket_range(lay, 2, 5)
+    assert torch.equal(one[:lo].view(torch.int16), start[:lo].view(torch.int16))
+    assert torch.equal(one[hi:].view(torch.int16), start[hi:].view(torch.int16))

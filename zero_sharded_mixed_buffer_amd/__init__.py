@@ -24,7 +24,10 @@ from ._abi import (  # noqa: F401
     zs_layout_destroy,
     zs_layout_info,
     zs_pack,
+    zs_bucket_range,
     zs_pack_accumulate,
+    zs_pack_bucket,
+    zs_plan_buckets,
     zs_plan,
     zs_plan_segments,
     zs_scaler_update,

@@ -56,6 +56,9 @@ _SIGS = {
     "zs_state_write": [c_void_p, POINTER(StateHost), c_void_p],
     "zs_pack": [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p],
     "zs_pack_accumulate": [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p],
+    "zs_plan_buckets": [c_void_p, c_int32, c_int64, c_void_p, c_void_p],
+    "zs_bucket_range": [c_void_p, c_int32, c_int32, c_void_p, c_void_p],
+    "zs_pack_bucket": [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p],
     "zs_unscale_check": [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p],
     "zs_grad_norm": [c_void_p, c_void_p, c_int32, c_void_p, POINTER(AdamwHParams), c_void_p, c_void_p, c_void_p],
     "zs_adamw_step": [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, POINTER(AdamwHParams), c_void_p,
@@ -164,6 +167,24 @@ def zs_layout_destroy(layout):
     lib().zs_layout_destroy(layout)
 
 
+def zs_plan_buckets(numels, bucket_numel):
+    """Returns the [tensor_begin, tensor_end) pairs of the buckets, in closing order."""
+    n = len(numels)
+    arr = _i64_array(numels)
+    bounds = (c_int32 * max(2 * n, 1))()
+    nb = c_int32()
+    _check(lib().zs_plan_buckets(ctypes.addressof(arr) if n else None, n, bucket_numel, ctypes.addressof(bounds),
+                                 byref(nb)), "zs_plan_buckets")
+    return [(bounds[2 * i], bounds[2 * i + 1]) for i in range(nb.value)]
+
+
+def zs_bucket_range(layout, tensor_begin, tensor_end):
+    """Returns the flat range (begin, end) of the bucket of tensors [tensor_begin, tensor_end)."""
+    b, e = c_int64(), c_int64()
+    _check(lib().zs_bucket_range(layout, tensor_begin, tensor_end, byref(b), byref(e)), "zs_bucket_range")
+    return b.value, e.value
+
+
 def zs_layout_info(layout):
     """Returns (flat_numel, shard_begin, shard_numel)."""
     a, b, c = c_int64(), c_int64(), c_int64()
@@ -214,6 +235,12 @@ def zs_pack(layout, src_ptrs, src_dtype, dst, dst_dtype, whole_flat=True, fuse_c
 def zs_pack_accumulate(layout, src_ptrs, src_dtype, acc, acc_dtype, whole_flat=True, fuse_check=None, stream=None):
     _check(lib().zs_pack_accumulate(layout, _ptr(src_ptrs), dtype_code(src_dtype), _ptr(acc), dtype_code(acc_dtype),
                                     int(bool(whole_flat)), fuse_check, _stream(stream)), "zs_pack_accumulate")
+
+
+def zs_pack_bucket(layout, src_ptrs, src_dtype, flat, flat_dtype, tensor_begin, tensor_end, accumulate=False,
+                   stream=None):
+    _check(lib().zs_pack_bucket(layout, _ptr(src_ptrs), dtype_code(src_dtype), _ptr(flat), dtype_code(flat_dtype),
+                                tensor_begin, tensor_end, int(bool(accumulate)), _stream(stream)), "zs_pack_bucket")
 
 
 def zs_unscale_check(layout, shard, grad_dtype, state, ext_overflow=None, local_sumsq_out=None, stream=None):

@@ -290,6 +290,34 @@ extern "C" zs_status zs_plan_segments(const int64_t* numels, int32_t n_tensors, 
   return ok();
 }
 
+extern "C" zs_status zs_plan_buckets(const int64_t* numels, int32_t n_tensors, int64_t bucket_numel,
+                                     int32_t* bounds_out, int32_t* n_buckets_out) {
+  if (n_buckets_out == nullptr) return fail(ZS_EINVAL, "n_buckets_out is NULL");
+  if (n_tensors < 0 || (n_tensors > 0 && numels == nullptr)) return fail(ZS_EINVAL, "bad tensor list");
+  if (bucket_numel <= 0) return fail(ZS_EINVAL, "bucket_numel must be positive");
+  for (int32_t i = 0; i < n_tensors; ++i)
+    if (numels[i] < 0) return fail(ZS_EINVAL, "numels[%d] is negative", i);
+  // Gradients become ready from the last tensor to the first; a bucket takes tensors
+  // until it holds at least bucket_numel elements.
+  int32_t nb = 0;
+  int32_t hi = n_tensors;
+  int64_t filled = 0;
+  for (int32_t t = n_tensors - 1; t >= 0; --t) {
+    filled += numels[t];
+    if (filled >= bucket_numel || t == 0) {
+      if (bounds_out) {
+        bounds_out[2 * nb] = t;
+        bounds_out[2 * nb + 1] = hi;
+      }
+      ++nb;
+      hi = t;
+      filled = 0;
+    }
+  }
+  *n_buckets_out = nb;
+  return ok();
+}
+
 // ---------------------------------------------------------------------------- layout / state
 
 extern "C" zs_status zs_layout_create(const int64_t* numels, int32_t n_tensors, int32_t dp_world, int32_t dp_rank,
@@ -451,6 +479,46 @@ extern "C" zs_status zs_pack_accumulate(const zs_layout* l, const void* src_ptrs
                                         zs_dtype acc_dtype, int32_t whole_flat, zs_state* fuse_check, void* stream) {
   return pack_common(l, src_ptrs, src_dtype, acc, acc_dtype, whole_flat, true, fuse_check, stream,
                      "zs_pack_accumulate");
+}
+
+namespace {
+
+// Flat range [begin, end) owned by the bucket of tensors [t0, t1): from the first tensor's
+// offset to the next tensor's offset (the flat length after the last tensor), so the
+// alignment gaps and the tail padding belong to the bucket before them.
+zs_status bucket_range(const zs_layout* l, int32_t t0, int32_t t1, int64_t* begin, int64_t* end) {
+  const int32_t n = static_cast<int32_t>(l->plan.numels.size());
+  if (t0 < 0 || t1 > n || t0 >= t1) return fail(ZS_EINVAL, "bucket [%d, %d) is not a non-empty tensor range of %d", t0, t1, n);
+  *begin = l->plan.offsets[t0];
+  *end = (t1 == n) ? l->plan.flat_numel : l->plan.offsets[t1];
+  return ok();
+}
+
+}  // namespace
+
+extern "C" zs_status zs_bucket_range(const zs_layout* l, int32_t tensor_begin, int32_t tensor_end, int64_t* flat_begin,
+                                     int64_t* flat_end) {
+  if (l == nullptr || flat_begin == nullptr || flat_end == nullptr) return fail(ZS_EINVAL, "NULL argument");
+  return bucket_range(l, tensor_begin, tensor_end, flat_begin, flat_end);
+}
+
+extern "C" zs_status zs_pack_bucket(const zs_layout* l, const void* src_ptrs, zs_dtype src_dtype, void* flat,
+                                    zs_dtype flat_dtype, int32_t tensor_begin, int32_t tensor_end, int32_t accumulate,
+                                    void* stream) {
+  zs_status st = check_layout(l);
+  if (st != ZS_OK) return st;
+  if (src_ptrs == nullptr || flat == nullptr) return fail(ZS_EINVAL, "zs_pack_bucket: src_ptrs or flat is NULL");
+  if (!is_half_dtype(src_dtype)) return fail(ZS_EINVAL, "zs_pack_bucket: src_dtype must be bf16 or fp16");
+  if (flat_dtype != src_dtype && flat_dtype != ZS_FP32)
+    return fail(ZS_EUNSUPPORTED, "zs_pack_bucket: the buffer must have the source dtype or fp32");
+  if (!aligned16(flat)) return fail(ZS_EINVAL, "zs_pack_bucket: the flat buffer must be 16-byte aligned");
+  int64_t lo = 0, hi = 0;
+  st = bucket_range(l, tensor_begin, tensor_end, &lo, &hi);
+  if (st != ZS_OK) return st;
+  hipError_t e = zs::launch_pack(l->map_full, static_cast<const uint64_t*>(src_ptrs), src_dtype, flat, flat_dtype,
+                                 accumulate != 0, nullptr, as_stream(stream), lo, hi);
+  if (e != hipSuccess) return hip_fail(e, "launching the bucket pack");
+  return ok();
 }
 
 extern "C" zs_status zs_unscale_check(const zs_layout* l, const void* shard, zs_dtype grad_dtype, zs_state* state,

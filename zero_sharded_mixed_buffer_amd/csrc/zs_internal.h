@@ -60,8 +60,9 @@ enum FlagMode : int { kFlagSet = 0, kFlagOr = 1 };
 // launch_pack / launch_check write reduction_blocks(len) partial sums when partials != null;
 // launch_reduce_finalize folds n partials (via level2 scratch of kLevel2 doubles when n is
 // large) into the state's flag and local sum of squares.
+// launch_pack covers flat elements [lo, hi) of the map's range (hi < 0: to its end).
 hipError_t launch_pack(const DevMap& map, const uint64_t* src_ptrs, int src_dt, void* dst, int dst_dt, bool accumulate,
-                       double* partials, hipStream_t s);
+                       double* partials, hipStream_t s, int64_t lo = 0, int64_t hi = -1);
 hipError_t launch_check(const void* shard, int64_t n, int dt, double* partials, hipStream_t s);
 hipError_t launch_reduce_finalize(const double* partials, int64_t nparts, double* level2, DevState* st,
                                   const int32_t* ext, int mode, double* local_out, hipStream_t s);

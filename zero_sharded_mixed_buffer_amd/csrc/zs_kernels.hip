@@ -285,32 +285,51 @@ __device__ __forceinline__ double sumsq8(const G16& g) {
 
 // ------------------------------------------------------------------ pack (+ fused check)
 
-// Gather the tensors into the flat range; padding becomes zero.  kPackBlock elements per
-// workgroup (one 8-element group per thread).  TO_F32: widen to fp32 (master seeding).  CHECK:
-// also write the fp64 sum of squares of this block's packed values to partials[blockIdx.x]
-// (a non-finite element makes that sum non-finite).
-template <int SDT, bool TO_F32, bool ACC, bool CHECK>
-__global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __restrict__ ptrs,
-                                                   void* __restrict__ dst, double* __restrict__ partials) {
-  constexpr int kPackGroups = int(kPackBlock / (int64_t(kThreads) * kGroup));
-  constexpr int kChunks = int(kPackBlock / kGroup);  // 16-byte chunks of one block
-  __shared__ v4u stage[kChunks + 1];
-  const int64_t block_base = work_unit() * kPackBlock;
-  const TileSeg ts = tile_seg(mp, ptrs, block_base / kTile);
+// Read the elements q+jlo .. q+jhi-1 (0 <= jlo < jhi <= 8) into positions jlo..jhi-1 of a
+// group, one element at a time; nothing outside that range is read.
+__device__ __forceinline__ G16 gather16_masked(const DevMap& mp, const uint64_t* ptrs, const TileSeg& ts, int64_t q,
+                                               int jlo, int jhi) {
+  G16 g = g16_zero();
+  int s = seg_find(mp, ts.lo, ts.hi, q + jlo);
+#pragma unroll
+  for (int j = 0; j < kGroup; ++j) {
+    if (j < jlo || j >= jhi) continue;
+    const int64_t e = q + j;
+    while (mp.seg_begin[s + 1] <= e) ++s;
+    const uint16_t* p = seg_elem(mp, ptrs, s, e);
+    if (p != nullptr) g.set(j, *p);
+  }
+  return g;
+}
+
+constexpr int kPackGroups = int(kPackBlock / (int64_t(kThreads) * kGroup));
+constexpr int kPackChunks = int(kPackBlock / kGroup);  // 16-byte chunks of one block
+
+// One block of the pack: elements [block_base, block_base + kPackBlock) of the flat range,
+// of which only those in [lo, end) are read from the tensors and written.  EDGE = false
+// promises that the whole block lies in [lo, end), so every group is full and needs no
+// mask.  Returns this thread's share of the sum of squares of the written values (CHECK).
+// `stage` (kPackChunks + 1 chunks) and `wide` (kPackBlock floats) are the block's LDS.
+template <int SDT, bool TO_F32, bool ACC, bool CHECK, bool EDGE>
+__device__ __forceinline__ double pack_block(const DevMap& mp, const uint64_t* ptrs, void* dst, const TileSeg& ts,
+                                             int64_t block_base, int64_t lo, int64_t end, v4u* stage,
+                                             float* wide) {
   G16 vals[kPackGroups];
+  int jlos[kPackGroups];
   int cnts[kPackGroups];
   // A full block inside one tensor whose source address is not 16-byte aligned: load the
   // aligned chunks that cover it (all inside the tensor segment) through LDS and shift.
   const int delta = (ts.base != nullptr) ? int((reinterpret_cast<uintptr_t>(ts.base + block_base) >> 1) & 7) : 0;
-  const bool staged = ts.uniform && ts.base != nullptr && delta != 0 && block_base + kPackBlock <= mp.len &&
-                      block_base - delta >= ts.seg_b && block_base - delta + kPackBlock + kGroup <= ts.seg_e;
+  const bool staged = !EDGE && ts.uniform && ts.base != nullptr && delta != 0 && block_base - delta >= ts.seg_b &&
+                      block_base - delta + kPackBlock + kGroup <= ts.seg_e;
   if (staged) {
     const v4u* chunk = reinterpret_cast<const v4u*>(ts.base + (block_base - delta));
-    for (int i = threadIdx.x; i <= kChunks; i += kThreads) stage[i] = ld_v4u(chunk + i);
+    for (int i = threadIdx.x; i <= kPackChunks; i += kThreads) stage[i] = ld_v4u(chunk + i);
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kPackGroups; ++u) {
       const int k = u * kThreads + threadIdx.x;
+      jlos[u] = 0;
       cnts[u] = kGroup;
       vals[u] = funnel16(stage[k], stage[k + 1], delta);
     }
@@ -318,8 +337,25 @@ __global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __
 #pragma unroll
     for (int u = 0; u < kPackGroups; ++u) {
       const int64_t q = block_base + int64_t(u * kThreads + threadIdx.x) * kGroup;
-      cnts[u] = group_count(mp.len, q);
-      vals[u] = cnts[u] > 0 ? gather16(mp, ptrs, ts, q, cnts[u]) : g16_zero();
+      if (!EDGE) {
+        jlos[u] = 0;
+        cnts[u] = kGroup;
+        vals[u] = gather16(mp, ptrs, ts, q, kGroup);
+        continue;
+      }
+      // elements [q + jlo, q + cnt) of this group lie in [lo, end)
+      const int64_t a = q < lo ? lo : q;
+      const int64_t b = q + kGroup < end ? q + kGroup : end;
+      const int jlo = (a < b) ? static_cast<int>(a - q) : 0;
+      const int cnt = (a < b) ? static_cast<int>(b - q) : 0;
+      jlos[u] = jlo;
+      cnts[u] = cnt;
+      if (cnt <= 0)
+        vals[u] = g16_zero();
+      else if (jlo == 0)
+        vals[u] = gather16(mp, ptrs, ts, q, cnt);
+      else
+        vals[u] = gather16_masked(mp, ptrs, ts, q, jlo, cnt);
     }
   }
   double acc = 0.0;
@@ -327,7 +363,6 @@ __global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __
     // fp32 destination: widen into LDS in element order, then move the block as
     // lane-contiguous 16-byte rows (each wave instruction covers one contiguous 1 KiB, so
     // every cache line is written - and, when accumulating, read - by one instruction).
-    __shared__ float wide[kPackBlock];
 #pragma unroll
     for (int u = 0; u < kPackGroups; ++u) {
       const int e = (u * kThreads + threadIdx.x) * kGroup;
@@ -336,61 +371,103 @@ __global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __
     }
     __syncthreads();
     float* d = static_cast<float*>(dst) + block_base;
-    const int64_t rem = mp.len - block_base;
+    const int64_t elo = lo - block_base;  // block-relative kept range [elo, ehi)
+    const int64_t ehi = end - block_base;
     constexpr int kRows = int(kPackBlock / (int64_t(kThreads) * 4));
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
       const int e = i * kThreads * 4 + threadIdx.x * 4;
-      const int64_t left = rem - e;
-      const int cnt = left >= 4 ? 4 : (left > 0 ? static_cast<int>(left) : 0);
-      if (cnt <= 0) continue;
+      int jlo = 0, cnt = 4;
+      if (EDGE) {
+        const int64_t a = e < elo ? elo : e;
+        const int64_t b = e + 4 < ehi ? e + 4 : ehi;
+        if (a >= b) continue;
+        jlo = static_cast<int>(a - e);
+        cnt = static_cast<int>(b - e);
+      }
+      const bool full = !EDGE || (jlo == 0 && cnt == 4);
       float f[4] = {wide[e], wide[e + 1], wide[e + 2], wide[e + 3]};
       if (ACC) {  // one fp32 add: the exact sum rounded once
-        if (cnt == 4) {
+        if (full) {
           const v4f o = ld_v4f(d + e);
           f[0] += o.x; f[1] += o.y; f[2] += o.z; f[3] += o.w;
         } else {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (j < cnt) f[j] += d[e + j];
+            if (j >= jlo && j < cnt) f[j] += d[e + j];
         }
       }
       if (CHECK) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const double x = static_cast<double>(f[j]);
-          acc += (j < cnt) ? x * x : 0.0;
+          acc += (j >= jlo && j < cnt) ? x * x : 0.0;
         }
       }
-      if (cnt == 4) {
+      if (full) {
         st_v4f(d + e, v4f{f[0], f[1], f[2], f[3]});
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (j < cnt) d[e + j] = f[j];
+          if (j >= jlo && j < cnt) d[e + j] = f[j];
       }
     }
   } else {
 #pragma unroll
     for (int u = 0; u < kPackGroups; ++u) {
-      const int cnt = cnts[u];
-      if (cnt <= 0) continue;
+      const int cnt = cnts[u], jlo = jlos[u];
+      if (EDGE && cnt <= 0) continue;
+      const bool full = !EDGE || (jlo == 0 && cnt == kGroup);
       const int64_t q = block_base + int64_t(u * kThreads + threadIdx.x) * kGroup;
       uint16_t* d = static_cast<uint16_t*>(dst) + q;
       G16 out = vals[u];
       if (ACC) {  // fp32 add, then one rounding to the 2-byte dtype (the fp32 sum of two
                   // 2-byte values rounds innocuously: fp32 has > 2p+2 significand bits)
-        const G16 old = (cnt == kGroup) ? ld16_vec(d) : ld16_elem(d, cnt);
+        G16 old = g16_zero();
+        if (full) {
+          old = ld16_vec(d);
+        } else {
+#pragma unroll
+          for (int j = 0; j < kGroup; ++j)
+            if (j >= jlo && j < cnt) old.set(j, d[j]);
+        }
 #pragma unroll
         for (int j = 0; j < kGroup; ++j) out.set(j, f2h<SDT>(h2f<SDT>(old.get(j)) + h2f<SDT>(vals[u].get(j))));
       }
       if (CHECK) acc += sumsq8<SDT>(out);
-      if (cnt == kGroup)
+      if (full) {
         st16_vec(d, out);
-      else
-        st16_elem(d, out, cnt);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j)
+          if (j >= jlo && j < cnt) d[j] = static_cast<uint16_t>(out.get(j));
+      }
     }
   }
+  return acc;
+}
+
+// Gather the tensors into the flat range; padding becomes zero.  kPackBlock elements per
+// workgroup (one 8-element group per thread); workgroup b handles block blk0 + b, and only
+// flat elements in [lo, hi) are read from the tensors and written (a whole pack passes
+// 0, 0, len; a bucket passes its own range).  TO_F32: widen to fp32 (master seeding, fp32
+// accumulation buffers).  ACC: add to the buffer instead of overwriting it.  CHECK: also
+// write the fp64 sum of squares of this block's resulting values to partials[blockIdx.x]
+// (a non-finite element makes that sum non-finite); used only for whole packs.
+template <int SDT, bool TO_F32, bool ACC, bool CHECK>
+__global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __restrict__ ptrs,
+                                                   void* __restrict__ dst, double* __restrict__ partials,
+                                                   int64_t blk0, int64_t lo, int64_t hi) {
+  __shared__ v4u stage[kPackChunks + 1];
+  __shared__ float wide[TO_F32 ? kPackBlock : 1];
+  const int64_t block_base = (blk0 + work_unit()) * kPackBlock;
+  const int64_t end = hi < mp.len ? hi : mp.len;
+  const TileSeg ts = tile_seg(mp, ptrs, block_base / kTile);
+  // uniform across the workgroup: no element of the block is clipped
+  const bool whole = block_base >= lo && block_base + kPackBlock <= end;
+  const double acc = whole
+      ? pack_block<SDT, TO_F32, ACC, CHECK, false>(mp, ptrs, dst, ts, block_base, lo, end, stage, wide)
+      : pack_block<SDT, TO_F32, ACC, CHECK, true>(mp, ptrs, dst, ts, block_base, lo, end, stage, wide);
   if (CHECK) {
     const double r = block_sum(acc);
     if (threadIdx.x == 0) partials[blockIdx.x] = r;
@@ -774,10 +851,11 @@ __global__ __launch_bounds__(kThreads) void k_unpack(DevMap mp, const void* __re
 
 template <int SDT>
 static void pack_dispatch(const dim3& G, hipStream_t s, const DevMap& map, const uint64_t* src_ptrs, void* dst,
-                          bool f32, bool acc, double* partials) {
+                          bool f32, bool acc, double* partials, int64_t blk0, int64_t lo, int64_t hi) {
   const dim3 B(kThreads);
   const bool chk = (partials != nullptr);
-#define ZS_PACK(F, A, C) hipLaunchKernelGGL((k_pack<SDT, F, A, C>), G, B, 0, s, map, src_ptrs, dst, partials)
+#define ZS_PACK(F, A, C) \
+  hipLaunchKernelGGL((k_pack<SDT, F, A, C>), G, B, 0, s, map, src_ptrs, dst, partials, blk0, lo, hi)
   if (f32) {
     if (acc) {
       if (chk) ZS_PACK(true, true, true); else ZS_PACK(true, true, false);
@@ -795,15 +873,18 @@ static void pack_dispatch(const dim3& G, hipStream_t s, const DevMap& map, const
 }
 
 hipError_t launch_pack(const DevMap& map, const uint64_t* src_ptrs, int src_dt, void* dst, int dst_dt, bool accumulate,
-                       double* partials, hipStream_t s) {
-  const int64_t nb = reduction_blocks(map.len);
-  if (nb == 0) return hipSuccess;
+                       double* partials, hipStream_t s, int64_t lo, int64_t hi) {
+  if (hi < 0) hi = map.len;
+  if (hi <= lo) return hipSuccess;
+  const int64_t blk0 = lo / kPackBlock;
+  const int64_t nb = (hi + kPackBlock - 1) / kPackBlock - blk0;
+  if (nb <= 0) return hipSuccess;
   const dim3 G(static_cast<unsigned>(nb));
   const bool f32 = (dst_dt == ZS_FP32);
   if (src_dt == ZS_BF16)
-    pack_dispatch<ZS_BF16>(G, s, map, src_ptrs, dst, f32, accumulate, partials);
+    pack_dispatch<ZS_BF16>(G, s, map, src_ptrs, dst, f32, accumulate, partials, blk0, lo, hi);
   else
-    pack_dispatch<ZS_FP16>(G, s, map, src_ptrs, dst, f32, accumulate, partials);
+    pack_dispatch<ZS_FP16>(G, s, map, src_ptrs, dst, f32, accumulate, partials, blk0, lo, hi);
   return hipGetLastError();
 }
 

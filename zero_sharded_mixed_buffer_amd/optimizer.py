@@ -86,6 +86,20 @@ class ZeroShardedAdamW:
         fn(self.layout, self._grad_table(grads), self.model_grad_dtype, self.flat, self.grad_dtype,
            whole_flat=True, fuse_check=fuse, stream=stream)
 
+    def buckets(self, bucket_numel):
+        """Tensor ranges [begin, end) of the gradient buckets, in the order backward fills them."""
+        return A.zs_plan_buckets(self.numels, bucket_numel)
+
+    def bucket_range(self, bucket):
+        """Flat range (begin, end) of the buffer that a bucket owns."""
+        return A.zs_bucket_range(self.layout, bucket[0], bucket[1])
+
+    def pack_bucket(self, grads, bucket, stream=None, accumulate=False):
+        """Pack (or add) the gradients of one bucket into its range of the flat buffer, as
+        soon as backward has produced them; `grads` is the whole gradient list."""
+        A.zs_pack_bucket(self.layout, self._grad_table(grads), self.model_grad_dtype, self.flat, self.grad_dtype,
+                         bucket[0], bucket[1], accumulate=accumulate, stream=stream)
+
     def check(self, ext_overflow=None, local_sumsq_out=None, stream=None):
         """Overflow flag and local sum of squares of the shard (after the reduce-scatter);
         local_sumsq_out (a device double) receives the value to exchange with the other ranks."""
