@@ -14,6 +14,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -120,8 +121,9 @@ def main():
                     help="pack the gradients in buckets of at least this many elements, in backward order "
                          "(the pages' reduce_bucket_size is 500000000), then check the shard; 0 = one pack "
                          "with the check fused")
-    ap.add_argument("--ceilings", action="store_true",
-                    help="also time a device-to-device copy and a triad (torch kernels) as bandwidth yardsticks")
+    ap.add_argument("--no-ceilings", dest="ceilings", action="store_false",
+                    help="skip timing a device-to-device copy and a triad (torch kernels) as bandwidth yardsticks")
+    ap.add_argument("--ceilings", dest="ceilings", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -192,12 +194,14 @@ def main():
         if ev is not None:
             ev[3].record(stream)
         Z.zs_scaler_update(st, stream)
+        if ev is not None:
+            ev[5].record(stream)
 
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -210,6 +214,10 @@ def main():
     first_pack_ms = sum(e[0].elapsed_time(e[4]) for e in evs) / args.steps
     adamw_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
     ms_per_step = elapsed * 1e3 / args.steps
+    step_ms = sorted(e[0].elapsed_time(e[5]) for e in evs)  # per-step HIP-event durations
+    step_median = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (
+        step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
+    step_p90 = step_ms[min(len(step_ms) - 1, int(math.ceil(0.9 * len(step_ms))) - 1)]
     gb = 4 if accum is not None else 2            # bytes per element of the flat gradient buffer
     adamw_bytes = (gb + 26) * S   # read g + master/m/v 12, write master/m/v 12 + param 2
     first_bytes = (2 + gb) * N    # read the tensors, write the buffer
@@ -230,6 +238,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "step_ms_events": {"median": step_median, "p90": step_p90, "min": step_ms[0], "max": step_ms[-1]},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
