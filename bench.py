@@ -54,6 +54,95 @@ def cpu_baseline(wl, n_elems, steps):
                       f"step time ({per_step:.2f} s)"}
 
 
+def host_copy_gbps(torch, gib=2, reps=3):
+    """Host-memory yardstick: torch's (multi-threaded) copy of a `gib` GiB fp32 tensor,
+    read + write bytes over the best time."""
+    n = gib * (1 << 30) // 4
+    a = torch.ones(n)
+    b = torch.empty(n)
+    b.copy_(a)
+    best = float("inf")
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        b.copy_(a)
+        best = min(best, time.perf_counter() - t0)
+    del a, b
+    return 2 * 4 * n / best / 1e9
+
+
+def run_offload(args, wl, torch, Z, gen):
+    """The offloaded step: pack + check + norm on the GPU, the AdamW update of the fp32 state
+    in pinned host memory on the host CPU (chunks copied down and parameters copied up),
+    scatter-back and scaler update on the GPU.  Returns the JSON line."""
+    dev = torch.device("cuda", 0)
+    hp = wl.hparams
+    params = gen.make_params(wl, dev)
+    grads = gen.make_grads(wl, 1, wl.init_scale, dev, with_faults=False)
+    t_setup = time.perf_counter()
+    opt = Z.ZeroShardedAdamW(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                             weight_decay=hp["weight_decay"], max_norm=hp["max_norm"], dynamic_loss_scale=wl.dynamic,
+                             init_scale=wl.init_scale, growth_interval=wl.growth_interval, offload=True,
+                             offload_chunk=args.offload_chunk, offload_threads=args.offload_threads)
+    log(f"offload state pinned and seeded after {time.perf_counter() - t_setup:.1f} s")
+    S, N = opt.shard_numel, wl.n_elems
+    stream = torch.cuda.current_stream()
+
+    def one_step(times=None):
+        opt.pack(grads, stream)
+        opt.norm(stream=stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        opt.update(stream=stream)  # returns once the new parameters are on the device
+        if times is not None:
+            times.append(time.perf_counter() - t0)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    upd = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step(upd)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    state = opt.read_state()
+    assert state["skipped_total"] == 0 and state["step_t"] == args.warmup + args.steps
+    threads = opt.offload_threads or int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    opt.close()
+    del params, grads, opt
+    torch.cuda.empty_cache()
+    upd_s = sorted(upd)[len(upd) // 2]
+    host_bytes = 28 * S  # read grad 2 + master/m/v 12, write master/m/v 12 + param 2
+    host_gbps = host_bytes / upd_s / 1e9
+    copy_gbps = host_copy_gbps(torch)
+    log(f"offload step {elapsed * 1e3 / args.steps:.1f} ms, host update {upd_s * 1e3:.1f} ms "
+        f"({host_gbps:.0f} GB/s host traffic; host copy yardstick {copy_gbps:.0f} GB/s)")
+    return {
+        "metric": "optimizer-step elements/s and achieved HBM GB/s (% of MI355X peak)",
+        "value": S * args.steps / elapsed,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "storage": "bf16 grads and params on the GPU; fp32 master/m/v in pinned host memory; fp64 update on the host",
+        "data": "synthetic: grads N(0,1e-3) and params N(0,0.02) drawn on the GPU, random init, no dataset",
+        "config": {"workload": wl.name, "mode": "offload", "tensors": len(wl.numels), "elements": N,
+                   "shard_elements": S, "grad_dtype": wl.dtype, "offload_chunk": args.offload_chunk,
+                   "host_threads": threads},
+        "offload": {"host_update_ms_median": upd_s * 1e3, "host_update_gbps": host_gbps,
+                    "host_bytes_per_element": 28, "pcie_bytes_per_element": 4,
+                    "host_copy_yardstick_gbps": copy_gbps},
+        "roofline": {"bound": "host-dram", "kernel": "host AdamW update (zs_host_adamw_step chunks)",
+                     "achieved": host_gbps, "peak": copy_gbps, "unit": "GB/s", "frac": host_gbps / copy_gbps,
+                     "traffic": None, "peak_source": "measured host copy on the same machine (no published figure)"},
+    }
+
+
 def kernel_source_sha256():
     h = hashlib.sha256()
     for f in ("zero_sharded_mixed_buffer_amd/csrc/zs_kernels.hip", "zero_sharded_mixed_buffer_amd/csrc/zs_internal.h"):
@@ -121,6 +210,10 @@ def main():
                     help="pack the gradients in buckets of at least this many elements, in backward order "
                          "(the pages' reduce_bucket_size is 500000000), then check the shard; 0 = one pack "
                          "with the check fused")
+    ap.add_argument("--offload", action="store_true",
+                    help="keep master/m/v in pinned host memory and run the update on the host CPU")
+    ap.add_argument("--offload-chunk", type=int, default=1 << 24, help="elements per offloaded chunk")
+    ap.add_argument("--offload-threads", type=int, default=0, help="host threads (0: OMP_NUM_THREADS or all)")
     ap.add_argument("--no-ceilings", dest="ceilings", action="store_false",
                     help="skip timing a device-to-device copy and a triad (torch kernels) as bandwidth yardsticks")
     ap.add_argument("--ceilings", dest="ceilings", action="store_true", help=argparse.SUPPRESS)
@@ -140,6 +233,17 @@ def main():
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.offload:
+        if wl.dp_world != 1:
+            print(json.dumps({"error": "bench times the single-rank step"}))
+            sys.exit(2)
+        log(f"workload {wl.name} (offloaded): {len(wl.numels)} tensors, {wl.n_elems} elements")
+        out = run_offload(args, wl, torch, Z, gen)
+        if not args.no_cpu_baseline:
+            log("timing the CPU oracle baseline")
+            out["cpu_baseline"] = cpu_baseline(wl, args.cpu_baseline_elems, args.cpu_baseline_steps)
+        print(json.dumps(out), flush=True)
+        return
     hp = wl.hparams
     log(f"workload {wl.name}: {len(wl.numels)} tensors, {wl.n_elems} elements, dp {wl.dp_world}")
     t_setup = time.perf_counter()

@@ -275,6 +275,43 @@ zs_status zs_unpack(const zs_layout* layout, const void* src, zs_dtype src_dtype
  * Errors: ZS_EINVAL on a NULL state. */
 zs_status zs_scaler_update(zs_state* state, void* stream);
 
+/* Offloaded optimizer step: the fp32 master, m and v live in host memory and the host CPU
+ * runs the update, which is bound by memory bandwidth, not by arithmetic ("3.7
+ * Megatron-LM, DeepSpeed & Parallelism in Practice", section "ZeRO-Offload and
+ * ZeRO-Infinity": optimizer states in CPU RAM, offload_optimizer with pin_memory, the state
+ * processed in sub_group_size chunks).  The arithmetic is zs_adamw_step's: fp64 per
+ * element, each stored fp32 value rounded once to nearest even, the parameter the
+ * round-to-nearest-even cast of the new master.  Neither call changes the device state:
+ * zs_scaler_update commits the step as after zs_adamw_step.
+ *
+ * zs_host_adamw_step: the update of `count` consecutive shard elements, every array in HOST
+ *   memory and owned by the caller: grad (grad_dtype bf16, fp16 or fp32; the reduced,
+ *   still loss-scaled gradient), master / m / v (fp32, updated in place) and param_out
+ *   (NULL, or count elements of param_dtype bf16 / fp16).  `scalars` is the state as
+ *   zs_state_read returns it after zs_grad_norm: loss_scale, clip_coef, step_t (the update
+ *   uses t = step_t + 1) and overflow (non-zero: nothing is written).  n_threads host
+ *   threads share the range (<= 0: OMP_NUM_THREADS, else every hardware thread).  No GPU
+ *   is used.  Errors: ZS_EINVAL on NULL arrays (count > 0), bad dtypes, invalid
+ *   hyper-parameters or scalars (loss_scale not a power of two, clip_coef outside (0, 1]).
+ * zs_offload_adamw_step: the whole update of this rank's shard_numel elements.  Reads the
+ *   state (synchronising `stream`), then pipelines chunks of chunk_numel elements: the
+ *   gradient chunk is copied from the device shard (grad_dtype) into `grad_stage`, the host
+ *   updates master / m / v (host arrays of shard_numel fp32 each), and the new parameters
+ *   go from `param_stage` to the device buffer flat_param_out (shard_numel elements of
+ *   param_dtype: the rank's all-gather input, or with dp_world == 1 the source of
+ *   zs_unpack).  grad_stage and param_stage hold two chunks each (2 * chunk_numel elements
+ *   of grad_dtype and param_dtype) and should be pinned (hipHostMalloc) so that copies
+ *   overlap the host work.  On an overflowed step nothing is copied or written.  Returns
+ *   after the last copy has completed.  Errors: ZS_EINVAL on NULL pointers, bad dtypes,
+ *   chunk_numel <= 0; ZS_EHIP from the copies. */
+zs_status zs_host_adamw_step(const void* grad, zs_dtype grad_dtype, float* master, float* m, float* v,
+                             int64_t count, const zs_adamw_hparams* hp, const zs_state_host* scalars,
+                             void* param_out, zs_dtype param_dtype, int32_t n_threads);
+zs_status zs_offload_adamw_step(const zs_layout* layout, const void* shard, zs_dtype grad_dtype, zs_state* state,
+                                const zs_adamw_hparams* hp, float* master, float* m, float* v, void* grad_stage,
+                                void* param_stage, int64_t chunk_numel, void* flat_param_out,
+                                zs_dtype param_dtype, int32_t n_threads, void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* zs_last_error(void);
 

@@ -19,10 +19,12 @@ from ._abi import (  # noqa: F401
     state_host,
     zs_adamw_step,
     zs_grad_norm,
+    zs_host_adamw_step,
     zs_last_error,
     zs_layout_create,
     zs_layout_destroy,
     zs_layout_info,
+    zs_offload_adamw_step,
     zs_pack,
     zs_bucket_range,
     zs_pack_accumulate,

@@ -65,6 +65,10 @@ _SIGS = {
                       c_void_p, c_void_p, c_int32, c_void_p],
     "zs_unpack": [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_void_p],
     "zs_scaler_update": [c_void_p, c_void_p],
+    "zs_host_adamw_step": [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_int64, POINTER(AdamwHParams),
+                           POINTER(StateHost), c_void_p, c_int32, c_int32],
+    "zs_offload_adamw_step": [c_void_p, c_void_p, c_int32, c_void_p, POINTER(AdamwHParams), c_void_p, c_void_p,
+                              c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_int32, c_int32, c_void_p],
 }
 
 
@@ -272,3 +276,23 @@ def zs_scaler_update(state, stream=None):
 
 def zs_last_error():
     return lib().zs_last_error().decode(errors="replace")
+
+
+# ------------------------------------------------------------------------------ offloaded step
+
+def zs_host_adamw_step(grad, grad_dtype, master, m, v, count, hp: AdamwHParams, scalars: StateHost,
+                       param_out=None, param_dtype=None, n_threads=0):
+    """Host AdamW over `count` elements of host arrays (see zs.h)."""
+    pdt = dtype_code(param_dtype) if param_dtype is not None else ZS_BF16
+    _check(lib().zs_host_adamw_step(_ptr(grad), dtype_code(grad_dtype), _ptr(master), _ptr(m), _ptr(v), int(count),
+                                    byref(hp), byref(scalars), _ptr(param_out), pdt, int(n_threads)),
+           "zs_host_adamw_step")
+
+
+def zs_offload_adamw_step(layout, shard, grad_dtype, state, hp: AdamwHParams, master, m, v, grad_stage, param_stage,
+                          chunk_numel, flat_param_out, param_dtype, n_threads=0, stream=None):
+    """Offloaded update of the rank's shard: chunks down, host update, parameters up (see zs.h)."""
+    _check(lib().zs_offload_adamw_step(layout, _ptr(shard), dtype_code(grad_dtype), state, byref(hp), _ptr(master),
+                                       _ptr(m), _ptr(v), _ptr(grad_stage), _ptr(param_stage), int(chunk_numel),
+                                       _ptr(flat_param_out), dtype_code(param_dtype), int(n_threads),
+                                       _stream(stream)), "zs_offload_adamw_step")

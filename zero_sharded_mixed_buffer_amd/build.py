@@ -16,7 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libzs.so")
 
 SOURCES = ["zs_abi.cpp", "zs_kernels.hip"]
-HEADERS = ["zs_internal.h"]
+HOST_SOURCES = ["zs_host.cpp"]  # plain C++ (the offloaded host step), built by the host compiler
+HEADERS = ["zs_internal.h", "zs_host.h"]
 
 # Packed fp32 vector ops are disabled for all device code; fp contraction is left to the
 # sources, which switch it off where an fp64 expression must round like its plain form.
@@ -28,6 +29,15 @@ HIP_FLAGS = [
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+
+
+# The host step must round like its plain form (no fused multiply-add); math errno is off so
+# that sqrt can be vectorised (IEEE results are unchanged).
+HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-ffp-contract=off", "-fno-math-errno", "-pthread"]
+
+
+def cxx() -> str:
+    return os.environ.get("CXX", "g++")
 
 
 def hipcc() -> str:
@@ -44,8 +54,12 @@ def build(verbose: bool = False) -> str:
         cmd = [hipcc(), *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
         _run(cmd, verbose)
         objs.append(obj)
+    for src in HOST_SOURCES:
+        obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
+        _run([cxx(), *HOST_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-pthread", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB
 

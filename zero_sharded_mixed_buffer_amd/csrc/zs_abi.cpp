@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "zs.h"
+#include "zs_host.h"
 #include "zs_internal.h"
 
 using zs::DevMap;
@@ -626,3 +627,119 @@ extern "C" zs_status zs_scaler_update(zs_state* state, void* stream) {
 }
 
 extern "C" const char* zs_last_error(void) { return g_last_error.c_str(); }
+
+// ---------------------------------------------------------------------------- offloaded step
+
+namespace {
+
+zs_status check_host_scalars(const zs_state_host* sc) {
+  if (sc == nullptr) return fail(ZS_EINVAL, "scalars is NULL");
+  if (!is_pow2_double(sc->loss_scale)) return fail(ZS_EINVAL, "loss_scale must be a positive power of two");
+  if (!(sc->clip_coef > 0.0) || !(sc->clip_coef <= 1.0)) return fail(ZS_EINVAL, "clip_coef must lie in (0, 1]");
+  if (sc->step_t < 0) return fail(ZS_EINVAL, "step_t must be >= 0");
+  return ok();
+}
+
+zs_host::Scalars host_scalars(const zs_adamw_hparams* hp, const zs_state_host* sc) {
+  return zs_host::step_scalars(hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, sc->loss_scale,
+                               sc->clip_coef, sc->step_t);
+}
+
+size_t dtype_bytes(int dt) { return dt == ZS_FP32 ? 4 : 2; }
+
+}  // namespace
+
+extern "C" zs_status zs_host_adamw_step(const void* grad, zs_dtype grad_dtype, float* master, float* m, float* v,
+                                        int64_t count, const zs_adamw_hparams* hp, const zs_state_host* scalars,
+                                        void* param_out, zs_dtype param_dtype, int32_t n_threads) {
+  zs_status st = check_hparams(hp);
+  if (st != ZS_OK) return st;
+  st = check_host_scalars(scalars);
+  if (st != ZS_OK) return st;
+  if (count < 0) return fail(ZS_EINVAL, "count is negative");
+  if (count > 0 && (grad == nullptr || master == nullptr || m == nullptr || v == nullptr))
+    return fail(ZS_EINVAL, "grad, master, m and v must not be NULL");
+  if (!is_grad_dtype(grad_dtype) || !is_half_dtype(param_dtype))
+    return fail(ZS_EINVAL, "grad_dtype must be bf16, fp16 or fp32 and param_dtype bf16 or fp16");
+  if (!grad_aligned(grad, grad_dtype) || !grad_aligned(master, ZS_FP32) || !grad_aligned(m, ZS_FP32) ||
+      !grad_aligned(v, ZS_FP32) || !grad_aligned(param_out, ZS_BF16))
+    return fail(ZS_EINVAL, "arrays must be aligned to their element size");
+  if (scalars->overflow != 0) return ok();  // a skipped step changes nothing
+  zs_host::adamw(host_scalars(hp, scalars), grad_dtype, grad, master, m, v, param_dtype, param_out, count,
+                 n_threads > 0 ? n_threads : zs_host::default_threads());
+  return ok();
+}
+
+extern "C" zs_status zs_offload_adamw_step(const zs_layout* l, const void* shard, zs_dtype grad_dtype,
+                                           zs_state* state, const zs_adamw_hparams* hp, float* master, float* m,
+                                           float* v, void* grad_stage, void* param_stage, int64_t chunk_numel,
+                                           void* flat_param_out, zs_dtype param_dtype, int32_t n_threads,
+                                           void* stream) {
+  zs_status st = check_layout(l);
+  if (st != ZS_OK) return st;
+  st = check_state(l, state);
+  if (st != ZS_OK) return st;
+  st = check_hparams(hp);
+  if (st != ZS_OK) return st;
+  if (shard == nullptr || master == nullptr || m == nullptr || v == nullptr || grad_stage == nullptr ||
+      param_stage == nullptr || flat_param_out == nullptr)
+    return fail(ZS_EINVAL, "zs_offload_adamw_step: a required pointer is NULL");
+  if (!is_grad_dtype(grad_dtype) || !is_half_dtype(param_dtype))
+    return fail(ZS_EINVAL, "grad_dtype must be bf16, fp16 or fp32 and param_dtype bf16 or fp16");
+  if (chunk_numel <= 0) return fail(ZS_EINVAL, "chunk_numel must be positive");
+  if (!grad_aligned(shard, grad_dtype) || !grad_aligned(flat_param_out, ZS_BF16))
+    return fail(ZS_EINVAL, "device arrays must be aligned to their element size");
+  hipStream_t s = as_stream(stream);
+  // The step's scalars: loss scale, clip coefficient, overflow flag and t, as left on the
+  // device by the check and the norm.
+  DevState dev{};
+  hipError_t e = hipMemcpyAsync(&dev, state->dev, sizeof dev, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "reading the state");
+  if (dev.h.overflow != 0) return ok();  // skipped step: the scaler update commits it
+  const zs_host::Scalars k = host_scalars(hp, &dev.h);
+  const int threads = n_threads > 0 ? n_threads : zs_host::default_threads();
+  const int64_t S = l->plan.shard_numel;
+  const int64_t nchunks = (S + chunk_numel - 1) / chunk_numel;
+  const size_t gb = dtype_bytes(grad_dtype), pb = dtype_bytes(param_dtype);
+  char* gstage = static_cast<char*>(grad_stage);
+  char* pstage = static_cast<char*>(param_stage);
+  const char* gsrc = static_cast<const char*>(shard);
+  char* pdst = static_cast<char*>(flat_param_out);
+  hipEvent_t ev_g[2] = {nullptr, nullptr}, ev_p[2] = {nullptr, nullptr};
+  for (int i = 0; i < 2 && e == hipSuccess; ++i) {
+    e = hipEventCreateWithFlags(&ev_g[i], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_p[i], hipEventDisableTiming);
+  }
+  auto chunk_len = [&](int64_t c) { return std::min(chunk_numel, S - c * chunk_numel); };
+  auto fetch = [&](int64_t c) -> hipError_t {  // gradient chunk c into staging slot c % 2
+    const int slot = static_cast<int>(c & 1);
+    hipError_t r = hipMemcpyAsync(gstage + slot * chunk_numel * gb, gsrc + c * chunk_numel * gb,
+                                  static_cast<size_t>(chunk_len(c)) * gb, hipMemcpyDeviceToHost, s);
+    if (r == hipSuccess) r = hipEventRecord(ev_g[slot], s);
+    return r;
+  };
+  // Double-buffered pipeline: the copy of chunk c+1 down and of chunk c-1 up run while the
+  // host updates chunk c.
+  if (e == hipSuccess && nchunks > 0) e = fetch(0);
+  for (int64_t c = 0; c < nchunks && e == hipSuccess; ++c) {
+    const int slot = static_cast<int>(c & 1);
+    if (c + 1 < nchunks) e = fetch(c + 1);
+    if (e == hipSuccess) e = hipEventSynchronize(ev_g[slot]);
+    if (e == hipSuccess && c >= 2) e = hipEventSynchronize(ev_p[slot]);  // slot's previous upload done
+    if (e != hipSuccess) break;
+    const int64_t off = c * chunk_numel, n = chunk_len(c);
+    char* pslot = pstage + slot * chunk_numel * pb;
+    zs_host::adamw(k, grad_dtype, gstage + slot * chunk_numel * gb, master + off, m + off, v + off, param_dtype,
+                   pslot, n, threads);
+    e = hipMemcpyAsync(pdst + off * pb, pslot, static_cast<size_t>(n) * pb, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipEventRecord(ev_p[slot], s);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  for (int i = 0; i < 2; ++i) {
+    if (ev_g[i]) (void)hipEventDestroy(ev_g[i]);
+    if (ev_p[i]) (void)hipEventDestroy(ev_p[i]);
+  }
+  if (e != hipSuccess) return hip_fail(e, "offloaded step");
+  return ok();
+}

@@ -8,7 +8,9 @@ step as a fixed sequence of ABI calls on one stream:
     (dp_world == 1: the check is fused into the pack pass)
 
 It makes no decisions of its own and never synchronises; the skip on overflow,
-the clip and the scaler all happen on the device.
+the clip and the scaler all happen on the device.  With offload=True the fp32
+master / m / v live in pinned host memory and update() runs the offloaded step
+(zs_offload_adamw_step, which synchronises its stream) followed by zs_unpack.
 """
 
 from __future__ import annotations
@@ -29,7 +31,8 @@ def pointer_table(tensors, device):
 class ZeroShardedAdamW:
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, max_norm=1.0,
                  dp_world=1, dp_rank=0, align=1, dynamic_loss_scale=None, init_scale=None, scale_floor=1.0,
-                 growth_interval=1000, grad_dtype=None, accum_dtype=None):
+                 growth_interval=1000, grad_dtype=None, accum_dtype=None, offload=False,
+                 offload_chunk=1 << 24, offload_threads=0):
         params = list(params)
         if not params:
             raise ValueError("empty parameter list")
@@ -53,15 +56,34 @@ class ZeroShardedAdamW:
             self.state = A.zs_state_create(self.layout, A.state_host(init_scale, scale_floor, dynamic_loss_scale,
                                                                      growth_interval))
         dev = self.device
+        self.offload = bool(offload)
         self.flat = torch.zeros(self.flat_numel, dtype=self.grad_dtype, device=dev)
-        self.master = torch.empty(self.shard_numel, dtype=torch.float32, device=dev)
-        self.m = torch.zeros(self.shard_numel, dtype=torch.float32, device=dev)
-        self.v = torch.zeros(self.shard_numel, dtype=torch.float32, device=dev)
         self.param_ptrs = pointer_table(params, dev)
         self.local_sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
         self._grad_key = None
         self._grad_ptrs = None
-        A.zs_pack(self.layout, self.param_ptrs, self.param_dtype, self.master, torch.float32, whole_flat=False)
+        S = self.shard_numel
+        if not self.offload:
+            self.master = torch.empty(S, dtype=torch.float32, device=dev)
+            self.m = torch.zeros(S, dtype=torch.float32, device=dev)
+            self.v = torch.zeros(S, dtype=torch.float32, device=dev)
+            A.zs_pack(self.layout, self.param_ptrs, self.param_dtype, self.master, torch.float32, whole_flat=False)
+        else:
+            # Optimizer state in pinned host memory, two-chunk staging buffers for the copies
+            # and the device buffer that receives the new parameters of the shard.
+            self.offload_chunk = int(offload_chunk)
+            self.offload_threads = int(offload_threads)
+            self.master = torch.empty(S, dtype=torch.float32, pin_memory=True)
+            self.m = torch.zeros(S, dtype=torch.float32, pin_memory=True)
+            self.v = torch.zeros(S, dtype=torch.float32, pin_memory=True)
+            c = min(self.offload_chunk, max(S, 1))
+            self.grad_stage = torch.empty(2 * c, dtype=self.grad_dtype, pin_memory=True)
+            self.param_stage = torch.empty(2 * c, dtype=self.param_dtype, pin_memory=True)
+            self.flat_param = torch.empty(S, dtype=self.param_dtype, device=dev)
+            seed = torch.empty(S, dtype=torch.float32, device=dev)
+            A.zs_pack(self.layout, self.param_ptrs, self.param_dtype, seed, torch.float32, whole_flat=False)
+            self.master.copy_(seed)  # synchronous: the pinned copy is complete on return
+            del seed
 
     @property
     def shard(self):
@@ -112,8 +134,22 @@ class ZeroShardedAdamW:
         A.zs_grad_norm(self.layout, None, self.grad_dtype, self.state, self.hp, rank_sumsq, None, stream=stream)
 
     def update(self, scatter=True, flat_param_out=None, stream=None):
-        A.zs_adamw_step(self.layout, self.shard, self.grad_dtype, self.master, self.m, self.v, self.hp, self.state,
-                        self.param_ptrs if scatter else None, flat_param_out, self.param_dtype, stream=stream)
+        if self.offload:
+            # The host updates the state chunk by chunk; the new parameters of the shard land
+            # in self.flat_param (the all-gather input with several ranks) and are scattered.
+            A.zs_offload_adamw_step(self.layout, self.shard, self.grad_dtype, self.state, self.hp, self.master,
+                                    self.m, self.v, self.grad_stage, self.param_stage,
+                                    min(self.offload_chunk, max(self.shard_numel, 1)), self.flat_param,
+                                    self.param_dtype, self.offload_threads, stream=stream)
+            if flat_param_out is not None:
+                flat_param_out.copy_(self.flat_param)
+            if scatter:
+                A.zs_unpack(self.layout, self.flat_param, self.param_dtype, False, self.param_ptrs, self.param_dtype,
+                            self.state, stream=stream)
+        else:
+            A.zs_adamw_step(self.layout, self.shard, self.grad_dtype, self.master, self.m, self.v, self.hp,
+                            self.state, self.param_ptrs if scatter else None, flat_param_out, self.param_dtype,
+                            stream=stream)
         A.zs_scaler_update(self.state, stream=stream)
 
     def step(self, grads, stream=None):
