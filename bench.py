@@ -72,7 +72,7 @@ def host_copy_gbps(torch, gib=2, reps=3):
 
 def run_offload(args, wl, torch, Z, gen):
     """The offloaded step: pack + check + norm on the GPU, the AdamW update of the fp32 state
-    in pinned host memory on the host CPU (chunks copied down and parameters copied up),
+    in host memory on the host CPU (chunks copied down and parameters copied up),
     scatter-back and scaler update on the GPU.  Returns the JSON line."""
     dev = torch.device("cuda", 0)
     hp = wl.hparams
@@ -83,7 +83,7 @@ def run_offload(args, wl, torch, Z, gen):
                              weight_decay=hp["weight_decay"], max_norm=hp["max_norm"], dynamic_loss_scale=wl.dynamic,
                              init_scale=wl.init_scale, growth_interval=wl.growth_interval, offload=True,
                              offload_chunk=args.offload_chunk, offload_threads=args.offload_threads)
-    log(f"offload state pinned and seeded after {time.perf_counter() - t_setup:.1f} s")
+    log(f"offload state allocated and seeded after {time.perf_counter() - t_setup:.1f} s")
     S, N = opt.shard_numel, wl.n_elems
     stream = torch.cuda.current_stream()
 
@@ -129,7 +129,7 @@ def run_offload(args, wl, torch, Z, gen):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f64",
-        "storage": "bf16 grads and params on the GPU; fp32 master/m/v in pinned host memory; fp64 update on the host",
+        "storage": "bf16 grads and params on the GPU; fp32 master/m/v in host memory; fp64 update on the host",
         "data": "synthetic: grads N(0,1e-3) and params N(0,0.02) drawn on the GPU, random init, no dataset",
         "config": {"workload": wl.name, "mode": "offload", "tensors": len(wl.numels), "elements": N,
                    "shard_elements": S, "grad_dtype": wl.dtype, "offload_chunk": args.offload_chunk,
@@ -211,7 +211,7 @@ def main():
                          "(the pages' reduce_bucket_size is 500000000), then check the shard; 0 = one pack "
                          "with the check fused")
     ap.add_argument("--offload", action="store_true",
-                    help="keep master/m/v in pinned host memory and run the update on the host CPU")
+                    help="keep master/m/v in host memory and run the update on the host CPU")
     ap.add_argument("--offload-chunk", type=int, default=1 << 24, help="elements per offloaded chunk")
     ap.add_argument("--offload-threads", type=int, default=0, help="host threads (0: OMP_NUM_THREADS or all)")
     ap.add_argument("--no-ceilings", dest="ceilings", action="store_false",

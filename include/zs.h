@@ -296,7 +296,8 @@ zs_status zs_scaler_update(zs_state* state, void* stream);
  * zs_offload_adamw_step: the whole update of this rank's shard_numel elements.  Reads the
  *   state (synchronising `stream`), then pipelines chunks of chunk_numel elements: the
  *   gradient chunk is copied from the device shard (grad_dtype) into `grad_stage`, the host
- *   updates master / m / v (host arrays of shard_numel fp32 each), and the new parameters
+ *   updates master / m / v (host arrays of shard_numel fp32 each; only the CPU reads them,
+ *   so they need not be pinned), and the new parameters
  *   go from `param_stage` to the device buffer flat_param_out (shard_numel elements of
  *   param_dtype: the rank's all-gather input, or with dp_world == 1 the source of
  *   zs_unpack).  grad_stage and param_stage hold two chunks each (2 * chunk_numel elements

@@ -1,4 +1,4 @@
-"""GPU parity of the offloaded step (optimizer state in pinned host memory, update on the
+"""GPU parity of the offloaded step (optimizer state in host memory, update on the
 host CPU, zs_offload_adamw_step) against the oracle, through the C ABI.
 
 The device still packs, checks, takes the norm and updates the scaler; the host updates

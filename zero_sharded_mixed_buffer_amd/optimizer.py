@@ -9,7 +9,7 @@ step as a fixed sequence of ABI calls on one stream:
 
 It makes no decisions of its own and never synchronises; the skip on overflow,
 the clip and the scaler all happen on the device.  With offload=True the fp32
-master / m / v live in pinned host memory and update() runs the offloaded step
+master / m / v live in host memory and update() runs the offloaded step
 (zs_offload_adamw_step, which synchronises its stream) followed by zs_unpack.
 """
 
@@ -69,20 +69,21 @@ class ZeroShardedAdamW:
             self.v = torch.zeros(S, dtype=torch.float32, device=dev)
             A.zs_pack(self.layout, self.param_ptrs, self.param_dtype, self.master, torch.float32, whole_flat=False)
         else:
-            # Optimizer state in pinned host memory, two-chunk staging buffers for the copies
-            # and the device buffer that receives the new parameters of the shard.
+            # Optimizer state in host memory (only the CPU touches it, so it need not be
+            # pinned), pinned two-chunk staging buffers for the copies, and the device buffer
+            # that receives the new parameters of the shard.
             self.offload_chunk = int(offload_chunk)
             self.offload_threads = int(offload_threads)
-            self.master = torch.empty(S, dtype=torch.float32, pin_memory=True)
-            self.m = torch.zeros(S, dtype=torch.float32, pin_memory=True)
-            self.v = torch.zeros(S, dtype=torch.float32, pin_memory=True)
+            self.master = torch.empty(S, dtype=torch.float32)
+            self.m = torch.zeros(S, dtype=torch.float32)
+            self.v = torch.zeros(S, dtype=torch.float32)
             c = min(self.offload_chunk, max(S, 1))
             self.grad_stage = torch.empty(2 * c, dtype=self.grad_dtype, pin_memory=True)
             self.param_stage = torch.empty(2 * c, dtype=self.param_dtype, pin_memory=True)
             self.flat_param = torch.empty(S, dtype=self.param_dtype, device=dev)
             seed = torch.empty(S, dtype=torch.float32, device=dev)
             A.zs_pack(self.layout, self.param_ptrs, self.param_dtype, seed, torch.float32, whole_flat=False)
-            self.master.copy_(seed)  # synchronous: the pinned copy is complete on return
+            self.master.copy_(seed)  # synchronous: complete on return
             del seed
 
     @property
