@@ -257,25 +257,43 @@ def main():
                              weight_decay=hp["weight_decay"], max_norm=hp["max_norm"], dp_world=wl.dp_world,
                              dp_rank=wl.dp_rank, align=wl.align, dynamic_loss_scale=wl.dynamic,
                              init_scale=wl.init_scale, growth_interval=wl.growth_interval, accum_dtype=accum)
-    if wl.dp_world != 1:
-        print(json.dumps({"error": "bench times the single-rank step"}))
-        sys.exit(2)
     S = opt.shard_numel
     N = wl.n_elems
+    d, r = wl.dp_world, wl.dp_rank
     stream = torch.cuda.current_stream()
     lay, st = opt.layout, opt.state
     buckets = opt.buckets(args.bucket_numel) if args.bucket_numel > 0 else None
     if buckets is not None:
         log(f"{len(buckets)} buckets of >= {args.bucket_numel} elements")
+    # With several ranks this is rank r's step: its own pack of the full local gradients, the
+    # check of its shard (the reduce-scatter output), the norm over every rank's partial sum
+    # and the update writing the rank's slice of the all-gather input.  The other ranks'
+    # partial sums come from their shards of the same buffer, computed once beforehand
+    # (on a real group the other GPUs compute them).
+    exchange = torch.zeros(d, dtype=torch.float64, device=dev) if d > 1 else None
+    flat_param = torch.empty(S, dtype=opt.param_dtype, device=dev) if d > 1 else None
+    if d > 1:
+        opt.pack(grads, stream)
+        for q in range(d):
+            if q == r:
+                continue
+            lq = Z.zs_layout_create(wl.numels, d, q, wl.align)
+            sq = Z.zs_state_create(lq, Z.state_host(wl.init_scale, 1.0, wl.dynamic, wl.growth_interval))
+            Z.zs_unscale_check(lq, opt.flat[q * S:(q + 1) * S], opt.grad_dtype, sq, None, exchange[q:q + 1], stream)
+            torch.cuda.synchronize()
+            Z.zs_state_destroy(sq)
+            Z.zs_layout_destroy(lq)
+    separate_check = buckets is not None or d > 1
 
     def pack_pass(k):
+        last = k == G - 1
         if buckets is None:
-            opt.pack(grads, stream, accumulate=k > 0, last=k == G - 1)
-            return
-        for b in buckets:
-            opt.pack_bucket(grads, b, stream, accumulate=k > 0)
-        if k == G - 1:
-            opt.check(stream=stream)
+            opt.pack(grads, stream, accumulate=k > 0, last=last)
+        else:
+            for b in buckets:
+                opt.pack_bucket(grads, b, stream, accumulate=k > 0)
+        if last and separate_check:
+            opt.check(local_sumsq_out=exchange[r:r + 1] if d > 1 else None, stream=stream)
 
     def one_step(ev=None):
         if ev is not None:
@@ -290,11 +308,11 @@ def main():
             pack_pass(k)
         if ev is not None:
             ev[1].record(stream)
-        opt.norm(stream=stream)
+        opt.norm(rank_sumsq=exchange, stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        Z.zs_adamw_step(lay, opt.shard, opt.grad_dtype, opt.master, opt.m, opt.v, opt.hp, st, opt.param_ptrs, None,
-                        opt.param_dtype, stream)
+        Z.zs_adamw_step(lay, opt.shard, opt.grad_dtype, opt.master, opt.m, opt.v, opt.hp, st,
+                        opt.param_ptrs if d == 1 else None, flat_param, opt.param_dtype, stream)
         if ev is not None:
             ev[3].record(stream)
         Z.zs_scaler_update(st, stream)
@@ -326,12 +344,28 @@ def main():
     adamw_bytes = (gb + 26) * S   # read g + master/m/v 12, write master/m/v 12 + param 2
     first_bytes = (2 + gb) * N    # read the tensors, write the buffer
     acc_bytes = (2 + 2 * gb) * N  # read the tensors and the buffer, write the buffer
-    check_bytes = gb * S if buckets is not None else 0  # the separate check re-reads the shard
+    check_bytes = gb * S if separate_check else 0  # the separate check re-reads the shard
     pack_bytes = first_bytes + (G - 1) * acc_bytes + check_bytes
     step_bytes = pack_bytes + adamw_bytes
     adamw_gbps = adamw_bytes / (adamw_ms * 1e-3) / 1e9
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     traffic = measured_traffic(wl.name) if G == 1 else None
+    unpack = None
+    if d > 1:
+        # After the all-gather every rank scatters the whole model-dtype buffer into its
+        # parameters: timed on its own, outside the step (4 B per element of the buffer).
+        gathered = torch.empty(opt.flat_numel, dtype=opt.param_dtype, device=dev)
+        gathered.zero_()
+        ue = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        Z.zs_unpack(lay, gathered, opt.param_dtype, True, opt.param_ptrs, opt.param_dtype, None, stream)
+        ue[0].record(stream)
+        for _ in range(5):
+            Z.zs_unpack(lay, gathered, opt.param_dtype, True, opt.param_ptrs, opt.param_dtype, None, stream)
+        ue[1].record(stream)
+        torch.cuda.synchronize()
+        u_ms = ue[0].elapsed_time(ue[1]) / 5
+        unpack = {"unpack_whole_ms": u_ms, "gbps": 4 * opt.flat_numel / u_ms / 1e6}
+        del gathered
     log(f"step {ms_per_step:.3f} ms ({step_gbps:.0f} GB/s), pack{'+accumulate' if G > 1 else ''} {pack_ms:.3f} ms "
         f"({pack_bytes / pack_ms / 1e6:.0f} GB/s), adamw {adamw_ms:.3f} ms ({adamw_gbps:.0f} GB/s)")
     out = {
@@ -350,6 +384,7 @@ def main():
         "storage": "bf16 grads and params, fp32 master/m/v; AdamW and norm arithmetic in fp64",
         "data": "synthetic: grads N(0,1e-3) and params N(0,0.02) drawn on the GPU, random init, no dataset",
         "config": {"workload": wl.name, "tensors": len(wl.numels), "elements": N, "dp_world": wl.dp_world,
+                   "dp_rank": wl.dp_rank,
                    "shard_elements": S, "grad_dtype": wl.dtype, "align": wl.align, "grad_accum": G,
                    "accum_dtype": ("fp32" if accum is not None else wl.dtype),
                    "bucket_numel": args.bucket_numel or None, "buckets": len(buckets) if buckets else None},
@@ -358,6 +393,7 @@ def main():
         "algorithmic_bytes_per_step": step_bytes,
         "kernels_ms": {"pack_check": pack_ms, "adamw_cast_scatter": adamw_ms,
                        "finalize_and_scaler": ms_per_step - pack_ms - adamw_ms},
+        "unpack_after_allgather": unpack,
         "accumulation": None if G == 1 else {
             "first_pack_ms": first_pack_ms, "first_pack_gbps": first_bytes / first_pack_ms / 1e6,
             "accumulate_ms_each": (pack_ms - first_pack_ms) / (G - 1),
