@@ -368,7 +368,7 @@ def run_parity(wl, steps=None, align=None, dp_rank=None, check_every_step=True, 
     return report
 
 
-def run_parity_accumulation(wl, micro_steps, accum_dtype, steps=None, dp_rank=None):
+def run_parity_accumulation(wl, micro_steps, accum_dtype, steps=None, dp_rank=None, offload=False):
     """Gradient accumulation: `micro_steps` gradient lists per step are packed into the flat
     buffer (first) and added to it (the rest, the last one fused with the check at dp 1),
     in accum_dtype (fp32 or the model dtype); then the step.  Checks the accumulated buffer
@@ -383,7 +383,8 @@ def run_parity_accumulation(wl, micro_steps, accum_dtype, steps=None, dp_rank=No
     opt = Z.ZeroShardedAdamW(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
                              weight_decay=hp["weight_decay"], max_norm=hp["max_norm"], dp_world=d, dp_rank=rank,
                              align=align, dynamic_loss_scale=wl.dynamic, init_scale=wl.init_scale,
-                             growth_interval=wl.growth_interval, accum_dtype=accum_dtype)
+                             growth_interval=wl.growth_interval, accum_dtype=accum_dtype, offload=offload,
+                             offload_chunk=50_001, offload_threads=3 if offload else 0)
     ref = O.OracleRank(wl.numels, d, rank, [p.cpu() for p in params], oracle_scaler(wl), hp, align)
     lay = ref.layout
     S = lay.shard_numel

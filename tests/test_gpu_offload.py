@@ -37,6 +37,19 @@ def test_offload_parity(name, chunk):
     assert [s.step for s in rep.steps if s.overflow_gpu] == [k for k in sorted(wl.faults) if k <= steps]
 
 
+@pytest.mark.parametrize("name,accum", [("ragged_mini", torch.float32), ("moe_mini_dp4", None)])
+def test_offload_with_gradient_accumulation(name, accum):
+    """Micro-steps accumulated on the device (fp32 or model-dtype buffer), then the offloaded
+    update reading that buffer."""
+    from harness import run_parity_accumulation
+    _z()
+    wl = WORKLOADS[name]
+    acc_dt = accum if accum is not None else gen.TORCH_DTYPE[wl.dtype]
+    print(f"[case] offload + accumulation {name} accum={acc_dt}", flush=True)
+    flags = run_parity_accumulation(wl, 3, acc_dt, steps=min(wl.steps, 5), offload=True)
+    assert flags == [int(k in wl.faults) for k in range(1, min(wl.steps, 5) + 1)]
+
+
 def test_offload_and_device_steps_agree():
     """The same gradients through the device update and the offloaded update: the states
     and the parameters agree bit for bit (one arithmetic on both sides)."""
