@@ -102,7 +102,8 @@ typedef struct zs_state zs_state;    /* opaque; device zs_state_host + reduction
  * divisible buffer).  numels: host array of n_tensors sizes (>= 0, n_tensors >= 1);
  * align_elems: a power of two; offsets_out: optional host array of n_tensors flat offsets.
  * Errors: ZS_EINVAL on a NULL required pointer, n_tensors < 1, a negative size, dp_world
- * < 1, dp_rank outside [0, dp_world) or align_elems not a power of two. */
+ * < 1, dp_rank outside [0, dp_world), align_elems not a power of two, or a flat buffer
+ * above 68,719,472,640 elements (2^24 - 1 tiles of 4096: the largest grid of one launch). */
 zs_status zs_plan(const int64_t* numels, int32_t n_tensors, int32_t dp_world, int32_t dp_rank,
                   int64_t align_elems, int64_t* offsets_out, int64_t* flat_numel_out,
                   int64_t* shard_begin_out, int64_t* shard_numel_out);

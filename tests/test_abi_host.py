@@ -97,6 +97,17 @@ def test_plan_rejects_bad_arguments():
         Z.zs_plan([], 1, 0, 1)
 
 
+def test_plan_rejects_a_flat_buffer_beyond_one_launch_grid():
+    Z = _z()
+    limit = ((2 ** 32 - 1) // 256) * 4096
+    assert Z.zs_plan([limit], 1, 0)[1] == limit
+    assert Z.zs_plan([limit - 5, 5], 1, 0)[1] == limit
+    for numels in ([limit + 1], [limit, 1], [2 ** 40]):
+        with pytest.raises(Z.ZsError) as e:
+            Z.zs_plan(numels, 1, 0)
+        assert e.value.status == -1 and "launch limit" in Z.zs_last_error()
+
+
 def test_page_example_partition():
     Z = _z()
     # Four parameters over two ranks: rank r owns [2r, 2r+2) ("Deep dive: Megatron", distributed optimizer).

@@ -85,8 +85,13 @@ zs_status make_plan(const int64_t* numels, int32_t n, int32_t dp_world, int32_t 
     if (pos < 0) return fail(ZS_EINVAL, "total size overflows int64");
   }
   p.flat_numel = round_up(pos, int64_t(dp_world) * align);
-  if (p.flat_numel / zs::kPackBlock >= (int64_t(1) << 31))
-    return fail(ZS_EINVAL, "flat buffer of %lld elements exceeds the supported 2^42", (long long)p.flat_numel);
+  // One workgroup of kThreads per 4096-element tile, and a launch holds fewer than 2^32
+  // work-items: at most 2^24 - 1 tiles (68.7e9 elements, beyond what one GPU can hold
+  // beside the 6 bytes per element of replicated model state anyway).
+  constexpr int64_t kMaxTiles = ((int64_t(1) << 32) - 1) / zs::kThreads;
+  if ((p.flat_numel + zs::kTile - 1) / zs::kTile > kMaxTiles)
+    return fail(ZS_EINVAL, "flat buffer of %lld elements exceeds the %lld-element launch limit",
+                (long long)p.flat_numel, (long long)(kMaxTiles * zs::kTile));
   p.shard_numel = p.flat_numel / dp_world;
   p.shard_begin = int64_t(dp_rank) * p.shard_numel;
   *out = std::move(p);
