@@ -154,3 +154,40 @@ def test_bucket_plan_rejects_bad_arguments():
             Z.zs_plan_buckets(numels, size)
         assert e.value.status == -1
     assert Z.zs_plan_buckets([], 10) == []
+
+
+def test_plain_c_program_uses_the_host_entry_points(tmp_path):
+    """tests/c/abi_host.c, built as C99 against include/zs.h and linked to libzs.so: planning,
+    bucket split and one host AdamW update, compared with the oracle."""
+    import shutil
+    import struct
+    import subprocess
+
+    import torch
+
+    Z = _z()
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.fail("no C compiler")
+    libdir = os.path.dirname(Z._abi.LIB_PATH)
+    exe = str(tmp_path / "abi_host")
+    subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "c", "abi_host.c"), "-o", exe, "-L", libdir, "-lzs",
+                    f"-Wl,-rpath,{libdir}"], check=True)
+    env = dict(os.environ, LD_LIBRARY_PATH=":".join(filter(None, ["/opt/rocm/lib", os.environ.get("LD_LIBRARY_PATH")])))
+    lines = subprocess.run([exe], check=True, capture_output=True, text=True, env=env).stdout.splitlines()
+    numels = [3, 5, 2, 7, 1]
+    lay = O.plan_layout(numels, 2, 1, 4)
+    assert lines[0].split() == ["plan", str(lay.flat_numel), str(lay.shard_begin), str(lay.shard_numel)] + \
+        [str(o) for o in lay.offsets]
+    want_b = O.plan_buckets(numels, 6)
+    assert lines[1].split() == ["buckets", str(len(want_b))] + [f"{a}:{b}" for a, b in want_b]
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_norm=1.0)
+    f32 = lambda xs: torch.tensor(xs, dtype=torch.float32)
+    p, m, v = O.adamw_update(f32([1.0, -2.0, 0.5, 0.25]), f32([0.0, 0.1, 0.0, 0.0]), f32([0.0, 0.01, 0.0, 0.0]),
+                             f32([0.5, -0.25, 1e-3, 0.0]), 2.0, 0.5, 3, hp)
+    pb = O.cast_to(p, torch.bfloat16).view(torch.int16)
+    hexf = lambda x: "%08x" % struct.unpack("<I", struct.pack("<f", float(x)))[0]
+    for i in range(4):
+        assert lines[2 + i].split() == ["adamw", hexf(p[i]), hexf(m[i]), hexf(v[i]), "%04x" % (int(pb[i]) & 0xFFFF)]
+    assert lines[6] == "invalid -1"
