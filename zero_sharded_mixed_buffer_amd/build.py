@@ -16,8 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libzs.so")
 
 SOURCES = ["zs_abi.cpp", "zs_kernels.hip"]
-HOST_SOURCES = ["zs_host.cpp"]  # plain C++ (the offloaded host step), built by the host compiler
-HEADERS = ["zs_internal.h", "zs_host.h"]
+HOST_SOURCES = ["zs_host.cpp", "zs_plan.cpp"]  # plain C++ (host step, planner), built by the host compiler
+HEADERS = ["zs_internal.h", "zs_host.h", "zs_plan.h"]
 
 # Packed fp32 vector ops are disabled for all device code; fp contraction is left to the
 # sources, which switch it off where an fp64 expression must round like its plain form.
@@ -34,6 +34,10 @@ HIP_FLAGS = [
 # The host step must round like its plain form (no fused multiply-add); math errno is off so
 # that sqrt can be vectorised (IEEE results are unchanged).
 HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-ffp-contract=off", "-fno-math-errno", "-pthread"]
+
+
+# roctx ranges around the entry points (profiler markers).
+LINK_LIBS = ["-L/opt/rocm/lib", "-lrocprofiler-sdk-roctx", "-Wl,-rpath,/opt/rocm/lib"]
 
 
 def cxx() -> str:
@@ -59,7 +63,7 @@ def build(verbose: bool = False) -> str:
         _run([cxx(), *HOST_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-pthread", "-o", tmp, *objs], verbose)
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-pthread", "-o", tmp, *objs, *LINK_LIBS], verbose)
     os.replace(tmp, LIB)
     return LIB
 

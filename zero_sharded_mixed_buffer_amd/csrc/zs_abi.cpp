@@ -3,6 +3,7 @@
 // Every step entry point only enqueues work on the caller's stream.
 
 #include <hip/hip_runtime.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include <algorithm>
 #include <cmath>
@@ -16,6 +17,7 @@
 #include "zs.h"
 #include "zs_host.h"
 #include "zs_internal.h"
+#include "zs_plan.h"
 
 using zs::DevMap;
 using zs::DevState;
@@ -40,7 +42,15 @@ zs_status hip_fail(hipError_t e, const char* what) {
   return fail(ZS_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+// A named profiler range around each step entry point, on the calling host thread (shown by
+// rocprofv3 --marker-trace; a no-op when no profiler is attached).
+class TraceRange {
+ public:
+  explicit TraceRange(const char* name) { roctxRangePushA(name); }
+  ~TraceRange() { roctxRangePop(); }
+  TraceRange(const TraceRange&) = delete;
+  TraceRange& operator=(const TraceRange&) = delete;
+};
 
 bool is_pow2_double(double x) {
   if (!(x > 0.0) || !std::isfinite(x)) return false;
@@ -52,99 +62,22 @@ int64_t round_up(int64_t x, int64_t m) { return ((x + m - 1) / m) * m; }
 
 // ---------------------------------------------------------------------------- planner
 
-struct Plan {
-  std::vector<int64_t> numels;
-  std::vector<int64_t> offsets;
-  int64_t flat_numel = 0;
-  int64_t shard_begin = 0;
-  int64_t shard_numel = 0;
-  int32_t dp_world = 1;
-  int32_t dp_rank = 0;
-  int64_t align = 1;
-};
+using zs_planner::HostMap;
+using zs_planner::Plan;
+
+// One workgroup of kThreads per kTile-element tile, and a launch holds fewer than 2^32
+// work-items: at most 2^24 - 1 tiles (68.7e9 elements, beyond what one GPU can hold beside
+// the 6 bytes per element of replicated model state anyway).
+constexpr int64_t kMaxFlat = (((int64_t(1) << 32) - 1) / zs::kThreads) * zs::kTile;
 
 zs_status make_plan(const int64_t* numels, int32_t n, int32_t dp_world, int32_t dp_rank, int64_t align,
                     Plan* out) {
-  if (numels == nullptr) return fail(ZS_EINVAL, "numels is NULL");
-  if (n < 1) return fail(ZS_EINVAL, "n_tensors must be >= 1 (got %d)", n);
-  if (dp_world < 1) return fail(ZS_EINVAL, "dp_world must be >= 1 (got %d)", dp_world);
-  if (dp_rank < 0 || dp_rank >= dp_world) return fail(ZS_EINVAL, "dp_rank %d outside [0, %d)", dp_rank, dp_world);
-  if (!is_pow2(align)) return fail(ZS_EINVAL, "align_elems must be a power of two (got %lld)", (long long)align);
-  Plan p;
-  p.numels.assign(numels, numels + n);
-  p.offsets.resize(n);
-  p.dp_world = dp_world;
-  p.dp_rank = dp_rank;
-  p.align = align;
-  int64_t pos = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    if (numels[i] < 0) return fail(ZS_EINVAL, "numels[%d] is negative", i);
-    pos = round_up(pos, align);
-    p.offsets[i] = pos;
-    pos += numels[i];
-    if (pos < 0) return fail(ZS_EINVAL, "total size overflows int64");
-  }
-  p.flat_numel = round_up(pos, int64_t(dp_world) * align);
-  // One workgroup of kThreads per 4096-element tile, and a launch holds fewer than 2^32
-  // work-items: at most 2^24 - 1 tiles (68.7e9 elements, beyond what one GPU can hold
-  // beside the 6 bytes per element of replicated model state anyway).
-  constexpr int64_t kMaxTiles = ((int64_t(1) << 32) - 1) / zs::kThreads;
-  if ((p.flat_numel + zs::kTile - 1) / zs::kTile > kMaxTiles)
-    return fail(ZS_EINVAL, "flat buffer of %lld elements exceeds the %lld-element launch limit",
-                (long long)p.flat_numel, (long long)(kMaxTiles * zs::kTile));
-  p.shard_numel = p.flat_numel / dp_world;
-  p.shard_begin = int64_t(dp_rank) * p.shard_numel;
-  *out = std::move(p);
+  const std::string err = zs_planner::make_plan(numels, n, dp_world, dp_rank, align, kMaxFlat, out);
+  if (!err.empty()) return fail(ZS_EINVAL, "%s", err.c_str());
   return ok();
 }
 
-struct HostMap {
-  std::vector<int64_t> seg_begin;  // nseg + 1
-  std::vector<int64_t> seg_local;
-  std::vector<int32_t> seg_tensor;
-  std::vector<int32_t> tile_first;  // ntiles + 1
-  int64_t len = 0;
-  int64_t ntiles = 0;
-};
-
-// Split [begin, begin + len) into maximal pieces inside one tensor or inside padding.
-HostMap build_map(const Plan& p, int64_t begin, int64_t len) {
-  HostMap m;
-  m.len = len;
-  const int64_t end = begin + len;
-  int64_t cur = begin;
-  for (size_t i = 0; i < p.numels.size(); ++i) {
-    const int64_t a = std::max(p.offsets[i], begin);
-    const int64_t b = std::min(p.offsets[i] + p.numels[i], end);
-    if (a >= b) continue;
-    if (a > cur) {
-      m.seg_begin.push_back(cur - begin);
-      m.seg_local.push_back(0);
-      m.seg_tensor.push_back(-1);
-    }
-    m.seg_begin.push_back(a - begin);
-    m.seg_local.push_back(a - p.offsets[i]);
-    m.seg_tensor.push_back(static_cast<int32_t>(i));
-    cur = b;
-  }
-  if (cur < end) {
-    m.seg_begin.push_back(cur - begin);
-    m.seg_local.push_back(0);
-    m.seg_tensor.push_back(-1);
-  }
-  const int64_t nseg = static_cast<int64_t>(m.seg_tensor.size());
-  m.seg_begin.push_back(len);
-  m.ntiles = (len + zs::kTile - 1) / zs::kTile;
-  m.tile_first.resize(m.ntiles + 1);
-  int64_t s = 0;
-  for (int64_t k = 0; k < m.ntiles; ++k) {
-    const int64_t x = k * zs::kTile;
-    while (m.seg_begin[s + 1] <= x) ++s;
-    m.tile_first[k] = static_cast<int32_t>(s);
-  }
-  m.tile_first[m.ntiles] = static_cast<int32_t>(nseg > 0 ? nseg - 1 : 0);
-  return m;
-}
+HostMap build_map(const Plan& p, int64_t begin, int64_t len) { return zs_planner::build_map(p, begin, len, zs::kTile); }
 
 // One device allocation per map: seg_begin | seg_local | seg_tensor | tile_first.
 zs_status upload_map(const HostMap& h, void** mem, DevMap* out) {
@@ -303,23 +236,7 @@ extern "C" zs_status zs_plan_buckets(const int64_t* numels, int32_t n_tensors, i
   if (bucket_numel <= 0) return fail(ZS_EINVAL, "bucket_numel must be positive");
   for (int32_t i = 0; i < n_tensors; ++i)
     if (numels[i] < 0) return fail(ZS_EINVAL, "numels[%d] is negative", i);
-  // Gradients become ready from the last tensor to the first; a bucket takes tensors
-  // until it holds at least bucket_numel elements.
-  int32_t nb = 0;
-  int32_t hi = n_tensors;
-  int64_t filled = 0;
-  for (int32_t t = n_tensors - 1; t >= 0; --t) {
-    filled += numels[t];
-    if (filled >= bucket_numel || t == 0) {
-      if (bounds_out) {
-        bounds_out[2 * nb] = t;
-        bounds_out[2 * nb + 1] = hi;
-      }
-      ++nb;
-      hi = t;
-      filled = 0;
-    }
-  }
+  const int32_t nb = zs_planner::plan_buckets(numels, n_tensors, bucket_numel, bounds_out);
   *n_buckets_out = nb;
   return ok();
 }
@@ -478,25 +395,23 @@ zs_status pack_common(const zs_layout* l, const void* src_ptrs, zs_dtype src_dty
 
 extern "C" zs_status zs_pack(const zs_layout* l, const void* src_ptrs, zs_dtype src_dtype, void* dst,
                              zs_dtype dst_dtype, int32_t whole_flat, zs_state* fuse_check, void* stream) {
+  const TraceRange trace("zs_pack");
   return pack_common(l, src_ptrs, src_dtype, dst, dst_dtype, whole_flat, false, fuse_check, stream, "zs_pack");
 }
 
 extern "C" zs_status zs_pack_accumulate(const zs_layout* l, const void* src_ptrs, zs_dtype src_dtype, void* acc,
                                         zs_dtype acc_dtype, int32_t whole_flat, zs_state* fuse_check, void* stream) {
+  const TraceRange trace("zs_pack_accumulate");
   return pack_common(l, src_ptrs, src_dtype, acc, acc_dtype, whole_flat, true, fuse_check, stream,
                      "zs_pack_accumulate");
 }
 
 namespace {
 
-// Flat range [begin, end) owned by the bucket of tensors [t0, t1): from the first tensor's
-// offset to the next tensor's offset (the flat length after the last tensor), so the
-// alignment gaps and the tail padding belong to the bucket before them.
 zs_status bucket_range(const zs_layout* l, int32_t t0, int32_t t1, int64_t* begin, int64_t* end) {
-  const int32_t n = static_cast<int32_t>(l->plan.numels.size());
-  if (t0 < 0 || t1 > n || t0 >= t1) return fail(ZS_EINVAL, "bucket [%d, %d) is not a non-empty tensor range of %d", t0, t1, n);
-  *begin = l->plan.offsets[t0];
-  *end = (t1 == n) ? l->plan.flat_numel : l->plan.offsets[t1];
+  if (!zs_planner::bucket_range(l->plan, t0, t1, begin, end))
+    return fail(ZS_EINVAL, "bucket [%d, %d) is not a non-empty tensor range of %d", t0, t1,
+                static_cast<int32_t>(l->plan.numels.size()));
   return ok();
 }
 
@@ -511,6 +426,7 @@ extern "C" zs_status zs_bucket_range(const zs_layout* l, int32_t tensor_begin, i
 extern "C" zs_status zs_pack_bucket(const zs_layout* l, const void* src_ptrs, zs_dtype src_dtype, void* flat,
                                     zs_dtype flat_dtype, int32_t tensor_begin, int32_t tensor_end, int32_t accumulate,
                                     void* stream) {
+  const TraceRange trace("zs_pack_bucket");
   zs_status st = check_layout(l);
   if (st != ZS_OK) return st;
   if (src_ptrs == nullptr || flat == nullptr) return fail(ZS_EINVAL, "zs_pack_bucket: src_ptrs or flat is NULL");
@@ -529,6 +445,7 @@ extern "C" zs_status zs_pack_bucket(const zs_layout* l, const void* src_ptrs, zs
 
 extern "C" zs_status zs_unscale_check(const zs_layout* l, const void* shard, zs_dtype grad_dtype, zs_state* state,
                                       const int32_t* ext_overflow, double* local_sumsq_out, void* stream) {
+  const TraceRange trace("zs_unscale_check");
   zs_status st = check_layout(l);
   if (st != ZS_OK) return st;
   st = check_state(l, state);
@@ -549,6 +466,7 @@ extern "C" zs_status zs_unscale_check(const zs_layout* l, const void* shard, zs_
 extern "C" zs_status zs_grad_norm(const zs_layout* l, const void* shard, zs_dtype grad_dtype, zs_state* state,
                                   const zs_adamw_hparams* hp, const double* rank_sumsq, double* local_sumsq_out,
                                   void* stream) {
+  const TraceRange trace("zs_grad_norm");
   zs_status st = check_layout(l);
   if (st != ZS_OK) return st;
   st = check_state(l, state);
@@ -579,6 +497,7 @@ extern "C" zs_status zs_adamw_step(const zs_layout* l, const void* shard, zs_dty
                                    float* m, float* v, const zs_adamw_hparams* hp, zs_state* state,
                                    const void* param_ptrs, void* flat_param_out, zs_dtype param_dtype,
                                    void* stream) {
+  const TraceRange trace("zs_adamw_step");
   zs_status st = check_layout(l);
   if (st != ZS_OK) return st;
   st = check_state(l, state);
@@ -604,6 +523,7 @@ extern "C" zs_status zs_adamw_step(const zs_layout* l, const void* shard, zs_dty
 extern "C" zs_status zs_unpack(const zs_layout* l, const void* src, zs_dtype src_dtype, int32_t whole_flat,
                                const void* dst_ptrs, zs_dtype dst_dtype, const zs_state* honour_skip,
                                void* stream) {
+  const TraceRange trace("zs_unpack");
   zs_status st = check_layout(l);
   if (st != ZS_OK) return st;
   if (src == nullptr || dst_ptrs == nullptr) return fail(ZS_EINVAL, "src or dst_ptrs is NULL");
@@ -623,6 +543,7 @@ extern "C" zs_status zs_unpack(const zs_layout* l, const void* src, zs_dtype src
 }
 
 extern "C" zs_status zs_scaler_update(zs_state* state, void* stream) {
+  const TraceRange trace("zs_scaler_update");
   if (state == nullptr) return fail(ZS_EINVAL, "state is NULL");
   zs_status st = check_device(state->device);
   if (st != ZS_OK) return st;
@@ -657,6 +578,7 @@ size_t dtype_bytes(int dt) { return dt == ZS_FP32 ? 4 : 2; }
 extern "C" zs_status zs_host_adamw_step(const void* grad, zs_dtype grad_dtype, float* master, float* m, float* v,
                                         int64_t count, const zs_adamw_hparams* hp, const zs_state_host* scalars,
                                         void* param_out, zs_dtype param_dtype, int32_t n_threads) {
+  const TraceRange trace("zs_host_adamw_step");
   zs_status st = check_hparams(hp);
   if (st != ZS_OK) return st;
   st = check_host_scalars(scalars);
@@ -680,6 +602,7 @@ extern "C" zs_status zs_offload_adamw_step(const zs_layout* l, const void* shard
                                            float* v, void* grad_stage, void* param_stage, int64_t chunk_numel,
                                            void* flat_param_out, zs_dtype param_dtype, int32_t n_threads,
                                            void* stream) {
+  const TraceRange trace("zs_offload_adamw_step");
   zs_status st = check_layout(l);
   if (st != ZS_OK) return st;
   st = check_state(l, state);

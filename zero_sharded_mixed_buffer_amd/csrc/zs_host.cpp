@@ -85,8 +85,16 @@ inline float grad_at(const void* g, int64_t i) {
   }
 }
 
+// Function clones resolved at load time.  ThreadSanitizer cannot run the resolvers (they
+// run before its runtime starts), so a ThreadSanitizer build keeps the baseline only.
+#if defined(__SANITIZE_THREAD__)
+#define ZS_HOST_CLONES
+#else
+#define ZS_HOST_CLONES __attribute__((target_clones("avx512f", "avx2", "default")))
+#endif
+
 template <int GD, int PD, bool OUT>
-__attribute__((target_clones("avx512f", "avx2", "default"))) void update_range(
+ZS_HOST_CLONES void update_range(
     const Scalars& kk, const void* __restrict__ grad, float* __restrict__ master, float* __restrict__ mom1,
     float* __restrict__ mom2, uint16_t* __restrict__ pout, int64_t lo, int64_t hi) {
   const Scalars k = kk;
@@ -150,8 +158,8 @@ void adamw(const Scalars& k, int grad_dt, const void* grad, float* master, float
   if (count <= 0) return;
   const RangeFn fn = pick(grad_dt, param_dt, param_out != nullptr);
   uint16_t* pout = static_cast<uint16_t*>(param_out);
-  // Contiguous parts of whole 64-element runs (4 KiB of fp32 state per 1024 elements keeps
-  // every thread on its own cache lines); small ranges stay on the calling thread.
+  // One contiguous part per thread, each a multiple of 64 elements so that no two threads
+  // write the same cache line of any array; small ranges stay on the calling thread.
   constexpr int64_t kGrain = 1 << 16;
   const int64_t max_parts = (count + kGrain - 1) / kGrain;
   const int parts = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(n_threads, max_parts)));
