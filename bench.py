@@ -214,6 +214,9 @@ def main():
                     help="keep master/m/v in host memory and run the update on the host CPU")
     ap.add_argument("--offload-chunk", type=int, default=1 << 24, help="elements per offloaded chunk")
     ap.add_argument("--offload-threads", type=int, default=0, help="host threads (0: OMP_NUM_THREADS or all)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the single-rank step captured once in a HIP graph and replayed, against the "
+                         "same step issued call by call (launch-bound small lists)")
     ap.add_argument("--no-ceilings", dest="ceilings", action="store_false",
                     help="skip timing a device-to-device copy and a triad (torch kernels) as bandwidth yardsticks")
     ap.add_argument("--ceilings", dest="ceilings", action="store_true", help=argparse.SUPPRESS)
@@ -332,6 +335,35 @@ def main():
     elapsed = time.perf_counter() - t0
     state = opt.read_state()
     assert state["skipped_total"] == 0 and state["step_t"] == args.warmup + args.steps
+    graph_replay = None
+    if args.graph:
+        if d != 1 or G != 1 or buckets is not None:
+            print(json.dumps({"error": "--graph times the plain single-rank step"}))
+            sys.exit(2)
+        # capture once (after a warm-up on the capturing side stream), then replay
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            opt.step(grads)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            opt.step(grads)
+        torch.cuda.synchronize()
+        t_g = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        t_g = time.perf_counter() - t_g
+        t_e = time.perf_counter()
+        for _ in range(args.steps):
+            opt.step(grads)
+        torch.cuda.synchronize()
+        t_e = time.perf_counter() - t_e
+        graph_replay = {"ms_per_step": t_g * 1e3 / args.steps, "eager_ms_per_step": t_e * 1e3 / args.steps}
+        log(f"graph replay {graph_replay['ms_per_step']:.4f} ms/step, call by call "
+            f"{graph_replay['eager_ms_per_step']:.4f} ms/step")
+        del graph
     pack_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     first_pack_ms = sum(e[0].elapsed_time(e[4]) for e in evs) / args.steps
     adamw_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
@@ -394,6 +426,7 @@ def main():
         "kernels_ms": {"pack_check": pack_ms, "adamw_cast_scatter": adamw_ms,
                        "finalize_and_scaler": ms_per_step - pack_ms - adamw_ms},
         "unpack_after_allgather": unpack,
+        "graph_replay": graph_replay,
         "accumulation": None if G == 1 else {
             "first_pack_ms": first_pack_ms, "first_pack_gbps": first_bytes / first_pack_ms / 1e6,
             "accumulate_ms_each": (pack_ms - first_pack_ms) / (G - 1),
