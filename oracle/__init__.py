@@ -12,6 +12,7 @@ from .zs_oracle import (  # noqa: F401
     bucket_range,
     adamw_update,
     cast_to,
+    decay_mask,
     clip_coefficient,
     global_sumsq,
     nonfinite_any,

@@ -244,7 +244,7 @@ def clip_coefficient(sumsq: float, max_norm: float):
 # AdamW on the fp32 shard  [NDS] AdamW only; [BOOK] torch.optim.AdamW, 12 bytes of fp32 state
 # ----------------------------------------------------------------------------------------------
 
-def adamw_update(master, m, v, x, loss_scale, clip, t, hp):
+def adamw_update(master, m, v, x, loss_scale, clip, t, hp, decay=None):
     """One AdamW update of this rank's fp32 master / m / v from its gradient shard x.
 
     g   = clip * x / loss_scale
@@ -255,6 +255,8 @@ def adamw_update(master, m, v, x, loss_scale, clip, t, hp):
     Decoupled weight decay as in torch.optim.AdamW; t counts applied updates from 1.
     READING: arithmetic in fp64; each of m_t, v_t, p_t is rounded once to fp32 when
     stored, and p_t uses the stored fp32 m_t and v_t.
+    decay: None (every element decays), or a bool tensor over the shard that is False for
+    the elements of no-decay tensors, which update as if weight_decay were 0.
     Returns new (master, m, v) fp32 tensors.
     """
     lr, b1, b2 = hp["lr"], hp["beta1"], hp["beta2"]
@@ -264,8 +266,27 @@ def adamw_update(master, m, v, x, loss_scale, clip, t, hp):
     v_t = (b2 * v.double() + (1.0 - b2) * (g * g)).float()
     m_hat = m_t.double() / (1.0 - b1 ** t)
     v_hat = v_t.double() / (1.0 - b2 ** t)
-    p_t = (master.double() * (1.0 - lr * wd) - lr * m_hat / (v_hat.sqrt() + eps)).float()
+    mult = torch.full_like(master, 1.0 - lr * wd, dtype=torch.float64)
+    if decay is not None:
+        mult = torch.where(decay, mult, torch.ones_like(mult))
+    p_t = (master.double() * mult - lr * m_hat / (v_hat.sqrt() + eps)).float()
     return p_t, m_t, v_t
+
+
+def decay_mask(layout: OracleLayout, no_decay):
+    """Bool mask over this rank's shard: False on the elements of the tensors listed as
+    no-decay, True elsewhere (padding included, where the master stays 0 either way).
+    READING: the pages instantiate torch.optim.AdamW with one parameter group ([BOOK]
+    "Initializing a DeepSpeed Engine"); the usual second group, biases and normalisation
+    weights with weight_decay 0 and every other hyper-parameter shared, is taken as a
+    per-tensor flag."""
+    mask = torch.ones(layout.shard_numel, dtype=torch.bool)
+    lo, hi = layout.shard_begin, layout.shard_begin + layout.shard_numel
+    for off, n, nd in zip(layout.offsets, layout.numels, no_decay):
+        a, b = max(off, lo), min(off + n, hi)
+        if nd and a < b:
+            mask[a - lo:b - lo] = False
+    return mask
 
 
 # ----------------------------------------------------------------------------------------------
@@ -312,8 +333,9 @@ def scaler_update(s: OracleScaler, overflow: bool) -> OracleScaler:
 class OracleRank:
     """One data-parallel rank: layout, fp32 master / m / v of its shard and the scaler."""
 
-    def __init__(self, numels, dp_world, dp_rank, params, scaler: OracleScaler, hp, align=1):
+    def __init__(self, numels, dp_world, dp_rank, params, scaler: OracleScaler, hp, align=1, no_decay=None):
         self.layout = plan_layout(numels, dp_world, dp_rank, align)
+        self.decay = decay_mask(self.layout, no_decay) if no_decay is not None else None
         self.hp = dict(hp)
         self.scaler = scaler
         self.master = shard_of(pack(params, self.layout, torch.float32), self.layout).clone()
@@ -339,7 +361,7 @@ class OracleRank:
             norm, c = clip_coefficient(ss, self.hp["max_norm"])
             t = self.scaler.step_t + 1
             self.master, self.m, self.v = adamw_update(self.master, self.m, self.v, shard_x,
-                                                       self.scaler.loss_scale, c, t, self.hp)
+                                                       self.scaler.loss_scale, c, t, self.hp, self.decay)
             self.params = unpack(self.master, lay, self.params, whole_flat=False)
             rec.update(local_sumsq=local, sumsq=ss, norm=norm, clip=c)
         self.scaler = scaler_update(self.scaler, overflow)

@@ -168,3 +168,15 @@ def test_bucket_range_mistakes_are_caught(monkeypatch, kind):
     _patch(monkeypatch, "bucket_range", wrong)
     assert _fails(P.test_bucket_range_hand_table, lambda: P.test_bucket_ranges_tile_the_flat_buffer(64, 4),
                   lambda: P.test_buckets_in_any_order_rebuild_the_whole_pack(False)), kind
+
+
+@pytest.mark.parametrize("kind", ["ignored", "inverted"])
+def test_no_decay_mistakes_are_caught(monkeypatch, kind):
+    real = Z.adamw_update
+
+    def wrong(master, m, v, x, loss_scale, clip, t, hp, decay=None):
+        if decay is not None:
+            decay = None if kind == "ignored" else ~decay
+        return real(master, m, v, x, loss_scale, clip, t, hp, decay)
+    _patch(monkeypatch, "adamw_update", wrong)
+    assert _fails(P.test_no_decay_tensors_closed_form, P.test_no_decay_group_matches_torch_param_groups), kind

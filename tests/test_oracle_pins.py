@@ -122,7 +122,7 @@ def test_adamw_closed_form_constant_gradient():
         assert abs(master[i].item() - p_cf) <= 12 * 2.0 ** -24 * (abs(p_cf) + HP["lr"])
         assert abs(m[i].item() - m_cf) <= 12 * 2.0 ** -24 * abs(m_cf)
         assert abs(v[i].item() - v_cf) <= 12 * 2.0 ** -24 * abs(v_cf)
-    # The survey's worked value: p0 = 1, g = 0.5 gives p_10 = 0.98990047 in fp32.
+    # Worked value: p0 = 1, g = 0.5 gives p_10 = 0.98990047 in fp32 (the closed form rounds there too).
     assert master[0].item() == np.float32(0.98990047)
 
 
@@ -576,3 +576,60 @@ def test_buckets_in_any_order_rebuild_the_whole_pack(accumulate_into):
     lo, hi = O.bucket_range(lay, 2, 5)
     assert torch.equal(one[:lo].view(torch.int16), start[:lo].view(torch.int16))
     assert torch.equal(one[hi:].view(torch.int16), start[hi:].view(torch.int16))
+
+
+# ------------------------------------------------------------------------------------------
+# No-decay tensors (a second parameter group with weight_decay 0)
+# ------------------------------------------------------------------------------------------
+
+def test_no_decay_tensors_closed_form():
+    # zero gradients for 10 steps: decayed tensors shrink by (1 - lr*wd)^t, no-decay
+    # tensors keep their value exactly
+    lay = O.plan_layout([2, 3, 1], 1, 0)
+    mask = O.decay_mask(lay, [False, True, False])
+    assert mask.tolist() == [True, True, False, False, False, True]
+    p = torch.tensor([1.0, -2.0, 0.5, 0.25, -0.75, 3.0])
+    m = torch.zeros(6)
+    v = torch.zeros(6)
+    for t in range(1, 11):
+        p, m, v = O.adamw_update(p, m, v, torch.zeros(6), 1.0, 1.0, t, HP, mask)
+    lam = HP["lr"] * HP["weight_decay"]
+    assert p[2:5].tolist() == [0.5, 0.25, -0.75]
+    for i, x0 in ((0, 1.0), (1, -2.0), (5, 3.0)):
+        assert abs(p[i].item() - x0 * (1 - lam) ** 10) <= 10 * abs(x0) * 2.0 ** -24
+
+
+def test_no_decay_mask_follows_the_shard():
+    # four ranks over [5, 0, 9, 2] at align 2: the mask of each rank is its slice of the
+    # whole-buffer mask
+    numels, nd = [5, 0, 9, 2], [True, False, False, True]
+    full = O.decay_mask(O.plan_layout(numels, 1, 0, 2), nd)
+    whole = torch.ones(O.plan_layout(numels, 4, 0, 2).flat_numel, dtype=torch.bool)
+    whole[:full.numel()] = full
+    parts = [O.decay_mask(O.plan_layout(numels, 4, r, 2), nd) for r in range(4)]
+    assert torch.equal(torch.cat(parts), whole)
+
+
+def test_no_decay_group_matches_torch_param_groups():
+    # torch.optim.AdamW with two parameter groups (weight_decay wd and 0) in fp64, one step
+    # from the oracle's fp32 state, for t = 1..5; same bounds as the single-group pin
+    gen = torch.Generator().manual_seed(11)
+    n1, n2 = 3000, 1096
+    hp = dict(HP, weight_decay=0.3)
+    lay = O.plan_layout([n1, n2], 1, 0)
+    mask = O.decay_mask(lay, [False, True])
+    master = (torch.randn(n1 + n2, generator=gen) * 0.02).float()
+    m = torch.zeros(n1 + n2)
+    v = torch.zeros(n1 + n2)
+    for t in range(1, 6):
+        g = (torch.randn(n1 + n2, generator=gen) * 1e-3).float()
+        refs = []
+        for sl, wd in ((slice(0, n1), hp["weight_decay"]), (slice(n1, n1 + n2), 0.0)):
+            refs.append(_torch_adamw_one_step(master[sl], m[sl], v[sl], g[sl], t, dict(hp, weight_decay=wd)))
+        p_ref, m_ref, v_ref = (torch.cat([r[i] for r in refs]) for i in range(3))
+        master, m, v = O.adamw_update(master, m, v, g, 1.0, 1.0, t, hp, mask)
+        for a, b in ((m, m_ref), (v, v_ref)):
+            assert torch.all((a.double() - b).abs() <= b.abs().mul(2.0 ** -23))
+        ratio = (m_ref / (1 - hp["beta1"] ** t)).abs() / ((v_ref / (1 - hp["beta2"] ** t)).sqrt() + hp["eps"])
+        bound = p_ref.abs().mul(2.0 ** -24) + hp["lr"] * 2.0 ** -23 * ratio + 1e-30
+        assert torch.all((master.double() - p_ref).abs() <= bound)
