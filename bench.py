@@ -214,6 +214,8 @@ def main():
                     help="keep master/m/v in host memory and run the update on the host CPU")
     ap.add_argument("--offload-chunk", type=int, default=1 << 24, help="elements per offloaded chunk")
     ap.add_argument("--offload-threads", type=int, default=0, help="host threads (0: OMP_NUM_THREADS or all)")
+    ap.add_argument("--no-decay", choices=["none", "1d"], default="none",
+                    help="1d: tensors with at most one dimension (biases, norm weights) take no weight decay")
     ap.add_argument("--graph", action="store_true",
                     help="also time the single-rank step captured once in a HIP graph and replayed, against the "
                          "same step issued call by call (launch-bound small lists)")
@@ -259,7 +261,8 @@ def main():
     opt = Z.ZeroShardedAdamW(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
                              weight_decay=hp["weight_decay"], max_norm=hp["max_norm"], dp_world=wl.dp_world,
                              dp_rank=wl.dp_rank, align=wl.align, dynamic_loss_scale=wl.dynamic,
-                             init_scale=wl.init_scale, growth_interval=wl.growth_interval, accum_dtype=accum)
+                             init_scale=wl.init_scale, growth_interval=wl.growth_interval, accum_dtype=accum,
+                             no_decay="1d" if args.no_decay == "1d" else None)
     S = opt.shard_numel
     N = wl.n_elems
     d, r = wl.dp_world, wl.dp_rank
@@ -419,7 +422,8 @@ def main():
                    "dp_rank": wl.dp_rank,
                    "shard_elements": S, "grad_dtype": wl.dtype, "align": wl.align, "grad_accum": G,
                    "accum_dtype": ("fp32" if accum is not None else wl.dtype),
-                   "bucket_numel": args.bucket_numel or None, "buckets": len(buckets) if buckets else None},
+                   "bucket_numel": args.bucket_numel or None, "buckets": len(buckets) if buckets else None,
+                   "no_decay": args.no_decay},
         "achieved_hbm_gbps": step_gbps,
         "hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": step_bytes,

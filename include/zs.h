@@ -127,6 +127,18 @@ void zs_layout_destroy(zs_layout* layout);
 zs_status zs_layout_info(const zs_layout* layout, int64_t* flat_numel, int64_t* shard_begin,
                          int64_t* shard_numel);
 
+/* Tensors without weight decay: a second parameter group that shares every
+ * hyper-parameter but takes weight_decay 0, as is usual for biases and normalisation
+ * weights ("Initializing a DeepSpeed Engine": torch.optim.AdamW, whose parameter groups
+ * carry their own weight_decay).  no_decay: host array of n_tensors flags (non-zero: that
+ * tensor's elements update with a decay multiplier of exactly 1), or NULL to make every
+ * tensor decay again (the default).  Applies to zs_adamw_step and zs_offload_adamw_step
+ * on this layout.  Synchronises the device (work in flight may still read the previous
+ * table), so call it at set-up, not between the calls of a step.
+ * Errors: ZS_EINVAL on a NULL layout or n_tensors different from the layout's;
+ * ZS_ENOMEM / ZS_EHIP from the upload. */
+zs_status zs_layout_set_no_decay(zs_layout* layout, const uint8_t* no_decay, int32_t n_tensors);
+
 /* Device state for one rank (scaler, step count, flag, norm results) and the workspace of
  * the norm reduction, on the layout's device.  `init` gives the starting zs_state_host
  * (loss_scale 2^16 with dynamic = 1 for fp16, 1 with dynamic = 0 for bf16, typically).

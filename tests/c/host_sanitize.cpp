@@ -112,7 +112,7 @@ void planner_cases() {
   CHECK(!zs_planner::make_plan(one, 1, 1, 0, 3, int64_t(1) << 36, &p).empty());
 }
 
-uint16_t bf16_rne(float f) {  // independent restatement: round through double
+uint16_t bf16_rne(float f) {  // independent restatement: compare the dropped half with the tie
   uint32_t u;
   std::memcpy(&u, &f, 4);
   if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
@@ -151,11 +151,52 @@ void host_step_cases() {
   }
 }
 
+// No-decay runs: elements inside a run update with a decay multiplier of 1.
+void host_runs_cases() {
+  for (int c = 0; c < 40; ++c) {
+    const int64_t count = uniform(1, 200000);
+    std::vector<int64_t> runs;
+    int64_t pos = uniform(0, 50);
+    while (pos < count) {
+      const int64_t len = uniform(1, 30000);
+      runs.push_back(pos);
+      runs.push_back(std::min(count, pos + len));
+      pos += len + uniform(1, 30000);
+    }
+    std::vector<float> g(count), p(count), m(count, 0.0f), v(count, 0.0f);
+    for (int64_t i = 0; i < count; ++i) {
+      g[i] = (unit() - 0.5f) * 2e-3f;
+      p[i] = (unit() - 0.5f) * 0.04f;
+    }
+    std::vector<float> a = p, am = m, av = v, b = p, bm = m, bv = v;
+    const zs_host::Scalars k = zs_host::step_scalars(1e-2, 0.9, 0.999, 1e-8, 0.3, 1.0, 1.0, 0);
+    zs_host::Scalars knd = k;
+    knd.decay = 1.0;
+    const int threads = static_cast<int>(uniform(1, 6));
+    zs_host::adamw(k, 2, g.data(), a.data(), am.data(), av.data(), 0, nullptr, count, threads, runs.data(),
+                   static_cast<int64_t>(runs.size() / 2));
+    // reference: one call per element range, in order
+    int64_t cur = 0;
+    for (size_t r = 0; r < runs.size(); r += 2) {
+      if (cur < runs[r]) zs_host::adamw(k, 2, g.data() + cur, b.data() + cur, bm.data() + cur, bv.data() + cur, 0,
+                                        nullptr, runs[r] - cur, 1);
+      zs_host::adamw(knd, 2, g.data() + runs[r], b.data() + runs[r], bm.data() + runs[r], bv.data() + runs[r], 0,
+                     nullptr, runs[r + 1] - runs[r], 1);
+      cur = runs[r + 1];
+    }
+    if (cur < count) zs_host::adamw(k, 2, g.data() + cur, b.data() + cur, bm.data() + cur, bv.data() + cur, 0, nullptr,
+                                    count - cur, 1);
+    CHECK(std::memcmp(a.data(), b.data(), count * 4) == 0 && std::memcmp(am.data(), bm.data(), count * 4) == 0 &&
+          std::memcmp(av.data(), bv.data(), count * 4) == 0);
+  }
+}
+
 }  // namespace
 
 int main() {
   planner_cases();
   host_step_cases();
+  host_runs_cases();
   std::printf("ok\n");
   return 0;
 }

@@ -246,10 +246,11 @@ def run_parity_sampled(wl, steps=None, log=print):
 
 
 def run_parity(wl, steps=None, align=None, dp_rank=None, check_every_step=True, offload=False,
-               offload_chunk=1 << 24):
+               offload_chunk=1 << 24, no_decay=None):
     """Run `steps` optimizer steps of workload `wl` on cuda:0 and in the oracle, checking
     every stage each step.  offload=True keeps master / m / v in host memory and runs the
     update on the host (zs_offload_adamw_step, in chunks of offload_chunk elements).
+    no_decay: per-tensor flags of tensors that take no weight decay (or None).
     Returns a RunReport; raises AssertionError on a mismatch of the bit-exact quantities."""
     steps = wl.steps if steps is None else steps
     align = wl.align if align is None else align
@@ -265,8 +266,8 @@ def run_parity(wl, steps=None, align=None, dp_rank=None, check_every_step=True, 
                              weight_decay=hp["weight_decay"], max_norm=hp["max_norm"], dp_world=d, dp_rank=rank,
                              align=align, dynamic_loss_scale=wl.dynamic, init_scale=wl.init_scale,
                              growth_interval=wl.growth_interval, offload=offload, offload_chunk=offload_chunk,
-                             offload_threads=4 if offload else 0)
-    ref = O.OracleRank(wl.numels, d, rank, params_cpu, oracle_scaler(wl), hp, align)
+                             offload_threads=4 if offload else 0, no_decay=no_decay)
+    ref = O.OracleRank(wl.numels, d, rank, params_cpu, oracle_scaler(wl), hp, align, no_decay=no_decay)
     lay = ref.layout
     assert (opt.flat_numel, opt.shard_begin, opt.shard_numel) == (lay.flat_numel, lay.shard_begin, lay.shard_numel)
     # Master seeding (pack with widening) is exact.

@@ -24,6 +24,7 @@ from ._abi import (  # noqa: F401
     zs_layout_create,
     zs_layout_destroy,
     zs_layout_info,
+    zs_layout_set_no_decay,
     zs_offload_adamw_step,
     zs_pack,
     zs_bucket_range,

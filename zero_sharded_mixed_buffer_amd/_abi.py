@@ -57,6 +57,7 @@ _SIGS = {
     "zs_pack": [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p],
     "zs_pack_accumulate": [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p],
     "zs_plan_buckets": [c_void_p, c_int32, c_int64, c_void_p, c_void_p],
+    "zs_layout_set_no_decay": [c_void_p, c_void_p, c_int32],
     "zs_bucket_range": [c_void_p, c_int32, c_int32, c_void_p, c_void_p],
     "zs_pack_bucket": [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p],
     "zs_unscale_check": [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p],
@@ -187,6 +188,15 @@ def zs_bucket_range(layout, tensor_begin, tensor_end):
     b, e = c_int64(), c_int64()
     _check(lib().zs_bucket_range(layout, tensor_begin, tensor_end, byref(b), byref(e)), "zs_bucket_range")
     return b.value, e.value
+
+
+def zs_layout_set_no_decay(layout, no_decay):
+    """Per-tensor no-decay flags (a sequence of bools, one per tensor), or None to clear."""
+    if no_decay is None:
+        _check(lib().zs_layout_set_no_decay(layout, None, 0), "zs_layout_set_no_decay")
+        return
+    flags = (ctypes.c_uint8 * max(len(no_decay), 1))(*[1 if f else 0 for f in no_decay])
+    _check(lib().zs_layout_set_no_decay(layout, ctypes.addressof(flags), len(no_decay)), "zs_layout_set_no_decay")
 
 
 def zs_layout_info(layout):

@@ -107,6 +107,7 @@ zs_status upload_map(const HostMap& h, void** mem, DevMap* out) {
   out->seg_local = reinterpret_cast<const int64_t*>(base + b1);
   out->seg_tensor = reinterpret_cast<const int32_t*>(base + b2);
   out->tile_first = reinterpret_cast<const int32_t*>(base + b3);
+  out->seg_nodecay = nullptr;
   out->len = h.len;
   out->ntiles = h.ntiles;
   out->nseg = static_cast<int32_t>(nseg);
@@ -158,6 +159,8 @@ struct zs_layout {
   DevMap map_shard{};
   DevMap map_full{};
   int64_t nparts = 0;  // partial-sum slots: workgroups of the largest pack / check pass
+  void* mem_nodecay = nullptr;         // per-segment no-decay flags of the shard map, or null
+  std::vector<int64_t> nodecay_runs;   // the same as shard-relative [begin, end) pairs
 };
 
 struct zs_state {
@@ -281,7 +284,53 @@ extern "C" void zs_layout_destroy(zs_layout* l) {
   if (l == nullptr) return;
   if (l->mem_shard) (void)hipFree(l->mem_shard);
   if (l->mem_full) (void)hipFree(l->mem_full);
+  if (l->mem_nodecay) (void)hipFree(l->mem_nodecay);
   delete l;
+}
+
+extern "C" zs_status zs_layout_set_no_decay(zs_layout* l, const uint8_t* no_decay, int32_t n_tensors) {
+  zs_status st = check_layout(l);
+  if (st != ZS_OK) return st;
+  const int32_t n = static_cast<int32_t>(l->plan.numels.size());
+  if (no_decay != nullptr && n_tensors != n)
+    return fail(ZS_EINVAL, "no_decay has %d flags for %d tensors", n_tensors, n);
+  // work already enqueued may still read the previous table
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "synchronising before replacing the no-decay table");
+  if (l->mem_nodecay) (void)hipFree(l->mem_nodecay);
+  l->mem_nodecay = nullptr;
+  l->map_shard.seg_nodecay = nullptr;
+  if (l->plan.dp_world == 1) l->map_full.seg_nodecay = nullptr;
+  l->nodecay_runs.clear();
+  if (no_decay == nullptr) return ok();
+  const HostMap m = build_map(l->plan, l->plan.shard_begin, l->plan.shard_numel);
+  const size_t nseg = m.seg_tensor.size();
+  std::vector<uint8_t> flags(std::max<size_t>(nseg, 1), 0);
+  for (size_t s = 0; s < nseg; ++s) {
+    const int32_t t = m.seg_tensor[s];
+    if (t < 0 || no_decay[t] == 0) continue;
+    flags[s] = 1;
+    if (!l->nodecay_runs.empty() && l->nodecay_runs.back() == m.seg_begin[s]) {
+      l->nodecay_runs.back() = m.seg_begin[s + 1];  // adjacent runs merge
+    } else {
+      l->nodecay_runs.push_back(m.seg_begin[s]);
+      l->nodecay_runs.push_back(m.seg_begin[s + 1]);
+    }
+  }
+  if (l->nodecay_runs.empty()) return ok();  // every element of this shard decays
+  void* d = nullptr;
+  e = hipMalloc(&d, flags.size());
+  if (e != hipSuccess) return fail(ZS_ENOMEM, "hipMalloc for the no-decay table: %s", hipGetErrorString(e));
+  e = hipMemcpy(d, flags.data(), flags.size(), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(d);
+    l->nodecay_runs.clear();
+    return hip_fail(e, "uploading the no-decay table");
+  }
+  l->mem_nodecay = d;
+  l->map_shard.seg_nodecay = static_cast<const uint8_t*>(d);
+  if (l->plan.dp_world == 1) l->map_full.seg_nodecay = l->map_shard.seg_nodecay;
+  return ok();
 }
 
 extern "C" zs_status zs_layout_info(const zs_layout* l, int64_t* flat_numel, int64_t* shard_begin,
@@ -649,6 +698,7 @@ extern "C" zs_status zs_offload_adamw_step(const zs_layout* l, const void* shard
   };
   // Double-buffered pipeline: the copy of chunk c+1 down and of chunk c-1 up run while the
   // host updates chunk c.
+  std::vector<int64_t> runs;
   if (e == hipSuccess && nchunks > 0) e = fetch(0);
   for (int64_t c = 0; c < nchunks && e == hipSuccess; ++c) {
     const int slot = static_cast<int>(c & 1);
@@ -658,8 +708,17 @@ extern "C" zs_status zs_offload_adamw_step(const zs_layout* l, const void* shard
     if (e != hipSuccess) break;
     const int64_t off = c * chunk_numel, n = chunk_len(c);
     char* pslot = pstage + slot * chunk_numel * pb;
+    // this chunk's no-decay runs, chunk-relative
+    runs.clear();
+    for (size_t r = 0; r + 1 < l->nodecay_runs.size(); r += 2) {
+      const int64_t a = std::max(l->nodecay_runs[r], off), b = std::min(l->nodecay_runs[r + 1], off + n);
+      if (a < b) {
+        runs.push_back(a - off);
+        runs.push_back(b - off);
+      }
+    }
     zs_host::adamw(k, grad_dtype, gstage + slot * chunk_numel * gb, master + off, m + off, v + off, param_dtype,
-                   pslot, n, threads);
+                   pslot, n, threads, runs.empty() ? nullptr : runs.data(), static_cast<int64_t>(runs.size() / 2));
     e = hipMemcpyAsync(pdst + off * pb, pslot, static_cast<size_t>(n) * pb, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipEventRecord(ev_p[slot], s);
   }

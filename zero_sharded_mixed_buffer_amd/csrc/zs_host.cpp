@@ -153,11 +153,44 @@ int default_threads() {
   return hw == 0 ? 1 : static_cast<int>(std::min(hw, 256u));
 }
 
+namespace {
+
+// Elements [lo, hi) of one thread's part: plain runs with `k`, no-decay runs with `knd`.
+void update_part(RangeFn fn, const Scalars& k, const Scalars& knd, const void* grad, float* master, float* m,
+                 float* v, uint16_t* pout, int64_t lo, int64_t hi, const int64_t* runs, int64_t n_runs) {
+  if (runs == nullptr || n_runs == 0) {
+    fn(k, grad, master, m, v, pout, lo, hi);
+    return;
+  }
+  // first run ending after lo
+  int64_t a = 0, b = n_runs;
+  while (a < b) {
+    const int64_t mid = (a + b) / 2;
+    if (runs[2 * mid + 1] <= lo)
+      a = mid + 1;
+    else
+      b = mid;
+  }
+  int64_t cur = lo;
+  for (int64_t r = a; r < n_runs && cur < hi; ++r) {
+    const int64_t rb = std::max(runs[2 * r], cur), re = std::min(runs[2 * r + 1], hi);
+    if (rb >= hi) break;
+    if (cur < rb) fn(k, grad, master, m, v, pout, cur, rb);
+    if (rb < re) fn(knd, grad, master, m, v, pout, rb, re);
+    cur = std::max(cur, re);
+  }
+  if (cur < hi) fn(k, grad, master, m, v, pout, cur, hi);
+}
+
+}  // namespace
+
 void adamw(const Scalars& k, int grad_dt, const void* grad, float* master, float* m, float* v, int param_dt,
-           void* param_out, int64_t count, int n_threads) {
+           void* param_out, int64_t count, int n_threads, const int64_t* nd_runs, int64_t n_runs) {
   if (count <= 0) return;
   const RangeFn fn = pick(grad_dt, param_dt, param_out != nullptr);
   uint16_t* pout = static_cast<uint16_t*>(param_out);
+  Scalars knd = k;
+  knd.decay = 1.0;
   // One contiguous part per thread, each a multiple of 64 elements so that no two threads
   // write the same cache line of any array; small ranges stay on the calling thread.
   constexpr int64_t kGrain = 1 << 16;
@@ -168,9 +201,11 @@ void adamw(const Scalars& k, int grad_dt, const void* grad, float* master, float
   pool.reserve(parts - 1);
   for (int p = 1; p < parts; ++p) {
     const int64_t lo = std::min(count, p * per), hi = std::min(count, (p + 1) * per);
-    if (lo < hi) pool.emplace_back(fn, std::cref(k), grad, master, m, v, pout, lo, hi);
+    if (lo < hi)
+      pool.emplace_back(update_part, fn, std::cref(k), std::cref(knd), grad, master, m, v, pout, lo, hi, nd_runs,
+                        n_runs);
   }
-  fn(k, grad, master, m, v, pout, 0, std::min(count, per));
+  update_part(fn, k, knd, grad, master, m, v, pout, 0, std::min(count, per), nd_runs, n_runs);
   for (auto& t : pool) t.join();
 }
 

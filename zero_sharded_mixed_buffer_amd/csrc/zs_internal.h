@@ -37,6 +37,7 @@ struct DevMap {
   const int64_t* seg_local;   // nseg
   const int32_t* seg_tensor;  // nseg
   const int32_t* tile_first;  // ntiles + 1
+  const uint8_t* seg_nodecay;  // nseg flags (1: the segment's tensor takes no weight decay), or null
   int64_t len;
   int64_t ntiles;
   int32_t nseg;

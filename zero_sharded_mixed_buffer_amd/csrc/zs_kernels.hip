@@ -141,7 +141,8 @@ __device__ __forceinline__ int seg_find(const DevMap& mp, int lo, int hi, int64_
 }
 
 // Segment context of one tile.  When the whole tile lies in one segment, `base` maps a
-// range index q straight to the tensor element (base + q), or is null for padding.
+// range index q straight to the tensor element (base + q), or is null for padding (and
+// when no pointer table is given).
 struct TileSeg {
   int lo, hi;
   bool uniform;
@@ -157,7 +158,7 @@ __device__ __forceinline__ TileSeg tile_seg(const DevMap& mp, const uint64_t* pt
   t.base = nullptr;
   t.seg_b = mp.seg_begin[t.lo];
   t.seg_e = mp.seg_begin[t.lo + 1];
-  if (t.uniform) {
+  if (t.uniform && ptrs != nullptr) {
     const int32_t tensor = mp.seg_tensor[t.lo];
     if (tensor >= 0) t.base = reinterpret_cast<uint16_t*>(ptrs[tensor]) + (mp.seg_local[t.lo] - t.seg_b);
   }
@@ -632,15 +633,17 @@ __device__ __forceinline__ StepScalars step_scalars(const AdamwArgs& hp, const D
   return k;
 }
 
-// One element: returns the new (p, m, v) as fp32.
-__device__ __forceinline__ void adamw_elem(const StepScalars& k, float x, float& p, float& m, float& v) {
+// One element: returns the new (p, m, v) as fp32.  `decay` is the decoupled weight-decay
+// multiplier, 1 - lr * wd, or 1 for a tensor without weight decay.
+__device__ __forceinline__ void adamw_elem(const StepScalars& k, double decay, float x, float& p, float& m,
+                                           float& v) {
 #pragma clang fp contract(off)
   const double g = static_cast<double>(x) * k.gs;
   const float m1 = static_cast<float>(k.b1 * static_cast<double>(m) + k.omb1 * g);
   const float v1 = static_cast<float>(k.b2 * static_cast<double>(v) + k.omb2 * (g * g));
   const double den = sqrt(static_cast<double>(v1) * k.rbc2) + k.eps;
   const double upd = k.a * static_cast<double>(m1) / den;
-  p = static_cast<float>(static_cast<double>(p) * k.decay - upd);
+  p = static_cast<float>(static_cast<double>(p) * decay - upd);
   m = m1;
   v = v1;
 }
@@ -720,17 +723,18 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const void* __res
       vv[u] = v4f{vt[0], vt[1], vt[2], vt[3]};
     }
   }
-  TileSeg ts;
+  // No-decay tensors: one multiplier for a tile inside one segment, else per element.
+  const bool groups = (mp.seg_nodecay != nullptr);
+  TileSeg ts{};
+  if (SCATTER || groups) ts = tile_seg(mp, SCATTER ? ptrs : nullptr, tile);
+  const double tile_decay = (groups && ts.uniform && mp.seg_nodecay[ts.lo]) ? 1.0 : k.decay;
   // A full tile inside one parameter tensor whose address is not 16-byte aligned (ragged
   // lists): the cast parameters go through LDS and leave as destination-aligned 16-byte
   // chunks; only the at most 15 elements at the two ends of the tile are written singly.
   __shared__ uint32_t pstage[kTile / 2];
   int pdelta = 0;
-  if (SCATTER) {
-    ts = tile_seg(mp, ptrs, tile);
-    if (ts.uniform && ts.base != nullptr && base + kTile <= n)
-      pdelta = int((reinterpret_cast<uintptr_t>(ts.base + base) >> 1) & 7);
-  }
+  if (SCATTER && ts.uniform && ts.base != nullptr && base + kTile <= n)
+    pdelta = int((reinterpret_cast<uintptr_t>(ts.base + base) >> 1) & 7);
 #pragma unroll
   for (int u = 0; u < kQuadsPerThread; ++u) {
     const int cnt = cnts[u];
@@ -743,10 +747,20 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const void* __res
       m[j] = mv[u][j];
       v[j] = vv[u][j];
     }
+    double dec[4] = {tile_decay, tile_decay, tile_decay, tile_decay};
+    if (groups && !ts.uniform) {  // a tile that crosses segments: look each element up
+      int s = seg_find(mp, ts.lo, ts.hi, q);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j >= cnt) break;
+        while (mp.seg_begin[s + 1] <= q + j) ++s;
+        dec[j] = mp.seg_nodecay[s] ? 1.0 : k.decay;
+      }
+    }
     G16 out = g16_zero();
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      adamw_elem(k, gv[u][j], p[j], m[j], v[j]);
+      adamw_elem(k, dec[j], gv[u][j], p[j], m[j], v[j]);
       out.set(j, f2h<PDT>(p[j]));
     }
     if (cnt == 4) {

@@ -32,7 +32,7 @@ class ZeroShardedAdamW:
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, max_norm=1.0,
                  dp_world=1, dp_rank=0, align=1, dynamic_loss_scale=None, init_scale=None, scale_floor=1.0,
                  growth_interval=1000, grad_dtype=None, accum_dtype=None, offload=False,
-                 offload_chunk=1 << 24, offload_threads=0):
+                 offload_chunk=1 << 24, offload_threads=0, no_decay=None):
         params = list(params)
         if not params:
             raise ValueError("empty parameter list")
@@ -55,6 +55,15 @@ class ZeroShardedAdamW:
             self.flat_numel, self.shard_begin, self.shard_numel = A.zs_layout_info(self.layout)
             self.state = A.zs_state_create(self.layout, A.state_host(init_scale, scale_floor, dynamic_loss_scale,
                                                                      growth_interval))
+            # no_decay: one flag per parameter (a second group with weight_decay 0), or
+            # "1d" for the usual choice of every tensor with at most one dimension
+            if isinstance(no_decay, str):
+                if no_decay != "1d":
+                    raise ValueError("no_decay is a list of flags or '1d'")
+                no_decay = [p.dim() <= 1 for p in params]
+            self.no_decay = list(no_decay) if no_decay is not None else None
+            if self.no_decay is not None:
+                A.zs_layout_set_no_decay(self.layout, self.no_decay)
         dev = self.device
         self.offload = bool(offload)
         self.flat = torch.zeros(self.flat_numel, dtype=self.grad_dtype, device=dev)
