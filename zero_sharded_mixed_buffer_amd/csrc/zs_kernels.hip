@@ -681,7 +681,9 @@ __device__ __forceinline__ v4f load_grad4(const void* shard, int64_t q, int cnt,
   }
 }
 
-template <int GDT, int PDT, bool SCATTER, bool FLAT_OUT>
+// GROUPS: the map carries no-decay flags (a separate instantiation, so that the common
+// single-group kernel keeps its registers).
+template <int GDT, int PDT, bool SCATTER, bool FLAT_OUT, bool GROUPS>
 __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const void* __restrict__ shard,
                                                     float* __restrict__ master, float* __restrict__ mom1,
                                                     float* __restrict__ mom2, AdamwArgs hp,
@@ -724,7 +726,7 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const void* __res
     }
   }
   // No-decay tensors: one multiplier for a tile inside one segment, else per element.
-  const bool groups = (mp.seg_nodecay != nullptr);
+  constexpr bool groups = GROUPS;
   TileSeg ts{};
   if (SCATTER || groups) ts = tile_seg(mp, SCATTER ? ptrs : nullptr, tile);
   const double tile_decay = (groups && ts.uniform && mp.seg_nodecay[ts.lo]) ? 1.0 : k.decay;
@@ -735,6 +737,10 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const void* __res
   int pdelta = 0;
   if (SCATTER && ts.uniform && ts.base != nullptr && base + kTile <= n)
     pdelta = int((reinterpret_cast<uintptr_t>(ts.base + base) >> 1) & 7);
+  // The quads of the tile; PER_ELEM (a tile across segments with no-decay flags, rare) looks
+  // each element's decay up, every other tile uses the tile's one multiplier.
+  auto update_quads = [&](auto per_elem) {
+    constexpr bool PER_ELEM = decltype(per_elem)::value;
 #pragma unroll
   for (int u = 0; u < kQuadsPerThread; ++u) {
     const int cnt = cnts[u];
@@ -748,7 +754,7 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const void* __res
       v[j] = vv[u][j];
     }
     double dec[4] = {tile_decay, tile_decay, tile_decay, tile_decay};
-    if (groups && !ts.uniform) {  // a tile that crosses segments: look each element up
+    if constexpr (PER_ELEM) {
       int s = seg_find(mp, ts.lo, ts.hi, q);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -789,6 +795,11 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const void* __res
       }
     }
   }
+  };
+  if (groups && !ts.uniform)  // uniform across the workgroup
+    update_quads(std::true_type{});
+  else
+    update_quads(std::false_type{});
   if (SCATTER && pdelta != 0) {  // uniform across the workgroup
     __syncthreads();
     const v4u* L = reinterpret_cast<const v4u*>(pstage);
@@ -947,23 +958,32 @@ hipError_t launch_scaler_update(DevState* st, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int GDT, int PDT, bool GROUPS>
+static void adamw_dispatch_g(const dim3& G, hipStream_t s, const DevMap& map, const void* shard, float* master,
+                             float* m, float* v, const AdamwArgs& hp, const DevState* st, const uint64_t* ptrs,
+                             uint16_t* flat_out) {
+  const dim3 B(kThreads);
+#define ZS_ADAMW(SC, FO) \
+  hipLaunchKernelGGL((k_adamw<GDT, PDT, SC, FO, GROUPS>), G, B, 0, s, map, shard, master, m, v, hp, st, ptrs, flat_out)
+  if (ptrs != nullptr && flat_out != nullptr)
+    ZS_ADAMW(true, true);
+  else if (ptrs != nullptr)
+    ZS_ADAMW(true, false);
+  else if (flat_out != nullptr)
+    ZS_ADAMW(false, true);
+  else
+    ZS_ADAMW(false, false);
+#undef ZS_ADAMW
+}
+
 template <int GDT, int PDT>
 static void adamw_dispatch(const dim3& G, hipStream_t s, const DevMap& map, const void* shard, float* master,
                            float* m, float* v, const AdamwArgs& hp, const DevState* st, const uint64_t* ptrs,
                            uint16_t* flat_out) {
-  const dim3 B(kThreads);
-  if (ptrs != nullptr && flat_out != nullptr)
-    hipLaunchKernelGGL((k_adamw<GDT, PDT, true, true>), G, B, 0, s, map, shard, master, m, v, hp, st, ptrs,
-                       flat_out);
-  else if (ptrs != nullptr)
-    hipLaunchKernelGGL((k_adamw<GDT, PDT, true, false>), G, B, 0, s, map, shard, master, m, v, hp, st, ptrs,
-                       flat_out);
-  else if (flat_out != nullptr)
-    hipLaunchKernelGGL((k_adamw<GDT, PDT, false, true>), G, B, 0, s, map, shard, master, m, v, hp, st, ptrs,
-                       flat_out);
+  if (map.seg_nodecay != nullptr)
+    adamw_dispatch_g<GDT, PDT, true>(G, s, map, shard, master, m, v, hp, st, ptrs, flat_out);
   else
-    hipLaunchKernelGGL((k_adamw<GDT, PDT, false, false>), G, B, 0, s, map, shard, master, m, v, hp, st, ptrs,
-                       flat_out);
+    adamw_dispatch_g<GDT, PDT, false>(G, s, map, shard, master, m, v, hp, st, ptrs, flat_out);
 }
 
 template <int GDT>
