@@ -144,10 +144,16 @@ def run_offload(args, wl, torch, Z, gen):
 
 
 def kernel_source_sha256():
+    """Hash of the kernel sources with comments and blank space removed, so that counter
+    summaries stay valid across comment edits and go stale on any code change."""
+    import re
     h = hashlib.sha256()
     for f in ("zero_sharded_mixed_buffer_amd/csrc/zs_kernels.hip", "zero_sharded_mixed_buffer_amd/csrc/zs_internal.h"):
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -3,13 +3,14 @@
 // All kernels stream HBM: no data is reused, so the design goals are full 16-byte
 // accesses per lane, whole-wave contiguous 1 KiB rows, enough independent loads in flight
 // per wave, one short-lived workgroup per unit of work (the hardware dispatcher keeps
-// every CU full and the tail short), non-temporal stores for data nobody re-reads soon,
-// and no per-tensor launches.  Tensor boundaries are resolved through a device
-// segment map (zs_internal.h): a tile of 4096 flat elements that lies inside one tensor
-// (every tile of a large tensor) takes a uniform fast path with one base pointer; tiles
-// that meet several segments look each 8-element group up by binary search over the
-// tile's few segments and fall back to 2-byte accesses only where a group straddles a
-// boundary or its tensor address is not 16-byte aligned.
+// every CU full and the tail short), non-temporal loads and stores for data nobody
+// re-reads soon, and no per-tensor launches.  Tensor boundaries are resolved through a
+// device segment map (zs_internal.h): a tile of 4096 flat elements that lies inside one
+// tensor (every tile of a large tensor) takes a uniform fast path with one base pointer;
+// when that tensor's address is not 16-byte aligned (ragged lists), the tile goes through
+// LDS and is funnel-shifted into aligned 16-byte chunks.  Tiles that meet several segments
+// look each 8-element group up by binary search over the tile's few segments and fall back
+// to 2-byte accesses only where a group straddles a boundary.
 //
 // Numerics (the pages keep master weights and Adam moments in FP32 and ask for sensitive
 // reductions in higher precision - "Deep dive: Megatron", section "Precision"):
