@@ -206,7 +206,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--cpu-baseline-elems", type=int, default=1 << 27)
-    ap.add_argument("--cpu-baseline-steps", type=int, default=3)
+    ap.add_argument("--cpu-baseline-steps", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--grad-accum", type=int, default=1,
                     help="micro-steps accumulated into the flat buffer before each optimizer step")
