@@ -191,3 +191,14 @@ def test_plain_c_program_uses_the_host_entry_points(tmp_path):
     for i in range(4):
         assert lines[2 + i].split() == ["adamw", hexf(p[i]), hexf(m[i]), hexf(v[i]), "%04x" % (int(pb[i]) & 0xFFFF)]
     assert lines[6] == "invalid -1"
+
+
+def test_invalid_arguments_raise_value_errors():
+    Z = _z()
+    with pytest.raises(ValueError):
+        Z.zs_plan([4], 2, 5, 1)       # rank outside the group
+    with pytest.raises(ValueError):
+        Z.zs_plan([4], 1, 0, 3)       # alignment not a power of two
+    with pytest.raises(Z.ZsError) as e:
+        Z.zs_plan_buckets([4, 5], 0)
+    assert isinstance(e.value, ValueError) and e.value.status == -1

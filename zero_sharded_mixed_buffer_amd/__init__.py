@@ -13,6 +13,7 @@ from ._abi import (  # noqa: F401
     AdamwHParams,
     StateHost,
     ZsError,
+    ZsInvalidArgument,
     dtype_code,
     hparams,
     lib,

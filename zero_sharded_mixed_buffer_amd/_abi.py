@@ -22,9 +22,16 @@ STATUS = {0: "ZS_OK", -1: "ZS_EINVAL", -2: "ZS_EHIP", -3: "ZS_ENOMEM", -4: "ZS_E
 
 
 class ZsError(RuntimeError):
+    """A non-OK status from the library; `status` holds the zs_status code."""
+
     def __init__(self, what, status, message):
         super().__init__(f"{what} failed with {STATUS.get(status, status)}: {message}")
         self.status = status
+
+
+class ZsInvalidArgument(ZsError, ValueError):
+    """ZS_EINVAL: an argument was rejected before anything ran (also a ValueError, the
+    convention for bad input in Python)."""
 
 
 class AdamwHParams(ctypes.Structure):
@@ -96,7 +103,8 @@ def lib():
 
 def _check(status, what):
     if status != 0:
-        raise ZsError(what, status, lib().zs_last_error().decode(errors="replace"))
+        cls = ZsInvalidArgument if status == -1 else ZsError  # ZS_EINVAL
+        raise cls(what, status, lib().zs_last_error().decode(errors="replace"))
 
 
 def _ptr(x):
