@@ -56,6 +56,26 @@ def test_tiny_scale_sequence_matches_hand_table():
     assert [s.scale_gpu for s in rep.steps] == [2.0 ** 16, 2.0 ** 16, 2.0 ** 15, 2.0 ** 15, 2.0 ** 15]
 
 
+@pytest.mark.parametrize("name,interval,fault_steps", [("tiny", 2, (4, 9, 10)), ("moe_mini_dp4", 3, (2, 8)),
+                                                      ("tiny", 1, (3,))])
+def test_scale_growth_and_backoff_sequences(name, interval, fault_steps):
+    """Short growth windows, so the scale both doubles and halves within the run: the scale,
+    t, tracker and skip count match the oracle's scaler after every step."""
+    import dataclasses
+    from harness import run_parity
+    _z()
+    base = WORKLOADS[name]
+    faults = {s: [(0, 3, float("inf"))] for s in fault_steps}
+    wl = dataclasses.replace(base, growth_interval=interval, steps=12, faults=faults)
+    print(f"[case] growth {name} interval={interval} faults={fault_steps}", flush=True)
+    rep = run_parity(wl)
+    scales = [s.scale_gpu for s in rep.steps]
+    print(f"[growth] {name}: scales={scales}", flush=True)
+    assert [s.step for s in rep.steps if s.overflow_gpu] == list(fault_steps)
+    assert any(b == 2 * a for a, b in zip(scales, scales[1:]))  # the scale did grow
+    assert any(b == a / 2 for a, b in zip(scales, scales[1:]))  # and did back off
+
+
 @pytest.mark.parametrize("rank", [0, 1, 2])
 def test_dp_virtual_ranks_every_rank(rank):
     from harness import run_parity
