@@ -743,59 +743,59 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const void* __res
   auto update_quads = [&](auto per_elem) {
     constexpr bool PER_ELEM = decltype(per_elem)::value;
 #pragma unroll
-  for (int u = 0; u < kQuadsPerThread; ++u) {
-    const int cnt = cnts[u];
-    if (cnt <= 0) continue;
-    const int64_t q = base + int64_t(u) * (kThreads * 4) + int64_t(threadIdx.x) * 4;
-    float p[4], m[4], v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      p[j] = pv[u][j];
-      m[j] = mv[u][j];
-      v[j] = vv[u][j];
-    }
-    double dec[4] = {tile_decay, tile_decay, tile_decay, tile_decay};
-    if constexpr (PER_ELEM) {
-      int s = seg_find(mp, ts.lo, ts.hi, q);
+    for (int u = 0; u < kQuadsPerThread; ++u) {
+      const int cnt = cnts[u];
+      if (cnt <= 0) continue;
+      const int64_t q = base + int64_t(u) * (kThreads * 4) + int64_t(threadIdx.x) * 4;
+      float p[4], m[4], v[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (j >= cnt) break;
-        while (mp.seg_begin[s + 1] <= q + j) ++s;
-        dec[j] = mp.seg_nodecay[s] ? 1.0 : k.decay;
+        p[j] = pv[u][j];
+        m[j] = mv[u][j];
+        v[j] = vv[u][j];
       }
-    }
-    G16 out = g16_zero();
+      double dec[4] = {tile_decay, tile_decay, tile_decay, tile_decay};
+      if constexpr (PER_ELEM) {
+        int s = seg_find(mp, ts.lo, ts.hi, q);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      adamw_elem(k, dec[j], gv[u][j], p[j], m[j], v[j]);
-      out.set(j, f2h<PDT>(p[j]));
-    }
-    if (cnt == 4) {
-      st_v4f(master + q, v4f{p[0], p[1], p[2], p[3]});
-      st_v4f(mom1 + q, v4f{m[0], m[1], m[2], m[3]});
-      st_v4f(mom2 + q, v4f{v[0], v[1], v[2], v[3]});
-      if (FLAT_OUT) st_v2u(flat_out + q, v2u{out.w[0], out.w[1]});
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (j < cnt) {
-          master[q + j] = p[j];
-          mom1[q + j] = m[j];
-          mom2[q + j] = v[j];
+        for (int j = 0; j < 4; ++j) {
+          if (j >= cnt) break;
+          while (mp.seg_begin[s + 1] <= q + j) ++s;
+          dec[j] = mp.seg_nodecay[s] ? 1.0 : k.decay;
         }
       }
-      if (FLAT_OUT) st16_elem(flat_out + q, out, cnt);
-    }
-    if (SCATTER) {
-      if (pdelta != 0) {
-        const int e = u * kThreads * 4 + threadIdx.x * 4;  // tile-relative; cnt == 4 here
-        pstage[e / 2] = out.w[0];
-        pstage[e / 2 + 1] = out.w[1];
+      G16 out = g16_zero();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        adamw_elem(k, dec[j], gv[u][j], p[j], m[j], v[j]);
+        out.set(j, f2h<PDT>(p[j]));
+      }
+      if (cnt == 4) {
+        st_v4f(master + q, v4f{p[0], p[1], p[2], p[3]});
+        st_v4f(mom1 + q, v4f{m[0], m[1], m[2], m[3]});
+        st_v4f(mom2 + q, v4f{v[0], v[1], v[2], v[3]});
+        if (FLAT_OUT) st_v2u(flat_out + q, v2u{out.w[0], out.w[1]});
       } else {
-        scatter<4>(mp, ptrs, ts, q, cnt, out);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (j < cnt) {
+            master[q + j] = p[j];
+            mom1[q + j] = m[j];
+            mom2[q + j] = v[j];
+          }
+        }
+        if (FLAT_OUT) st16_elem(flat_out + q, out, cnt);
+      }
+      if (SCATTER) {
+        if (pdelta != 0) {
+          const int e = u * kThreads * 4 + threadIdx.x * 4;  // tile-relative; cnt == 4 here
+          pstage[e / 2] = out.w[0];
+          pstage[e / 2 + 1] = out.w[1];
+        } else {
+          scatter<4>(mp, ptrs, ts, q, cnt, out);
+        }
       }
     }
-  }
   };
   if (groups && !ts.uniform)  // uniform across the workgroup
     update_quads(std::true_type{});
