@@ -10,10 +10,17 @@
 
 #include "zs_host.h"
 
+#include <unistd.h>
+
 #include <algorithm>
+#include <atomic>
 #include <cmath>
+#include <condition_variable>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
+#include <memory>
+#include <mutex>
 #include <thread>
 #include <vector>
 
@@ -155,6 +162,92 @@ int default_threads() {
 
 namespace {
 
+// Worker threads kept for the life of the process, so that a pipelined step can hand many
+// chunks to the host without starting threads for each.  One job at a time: run() hands
+// out the part indices 0..parts-1 to the workers and the calling thread and returns when
+// every part is done.  Each job carries its own counters, so a worker that wakes late
+// finds its job's indices used up and calls nothing.  A process forked after the pool
+// started gets a pool of its own.
+class Pool {
+ public:
+  static Pool& get() {
+    static std::mutex make;
+    static Pool* pool = nullptr;
+    std::lock_guard<std::mutex> lk(make);
+    if (pool == nullptr || pool->pid_ != getpid()) pool = new Pool();  // a forked child's old pool has no threads
+    return *pool;
+  }
+
+  void run(int parts, const std::function<void(int)>& fn) {
+    std::lock_guard<std::mutex> one_job(job_mu_);
+    grow(parts - 1);
+    auto job = std::make_shared<Job>();
+    job->fn = &fn;
+    job->parts = parts;
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      current_ = job;
+      ++generation_;
+    }
+    wake_.notify_all();
+    work(*job);
+    std::unique_lock<std::mutex> lk(mu_);
+    finished_.wait(lk, [&] { return job->done.load() == parts; });
+    current_.reset();
+  }
+
+ private:
+  struct Job {
+    const std::function<void(int)>* fn = nullptr;
+    int parts = 0;
+    std::atomic<int> next{0};
+    std::atomic<int> done{0};
+  };
+
+  Pool() : pid_(getpid()) {}
+
+  void grow(int want) {
+    while (n_workers_ < want) {
+      std::thread([this] { loop(); }).detach();
+      ++n_workers_;
+    }
+  }
+
+  void loop() {
+    uint64_t seen = 0;
+    for (;;) {
+      std::shared_ptr<Job> job;
+      {
+        std::unique_lock<std::mutex> lk(mu_);
+        wake_.wait(lk, [&] { return generation_ != seen; });
+        seen = generation_;
+        job = current_;
+      }
+      if (job) work(*job);
+    }
+  }
+
+  void work(Job& job) {
+    int did = 0;
+    for (int i = job.next.fetch_add(1); i < job.parts; i = job.next.fetch_add(1)) {
+      (*job.fn)(i);
+      ++did;
+    }
+    if (did > 0 && job.done.fetch_add(did) + did == job.parts) {
+      std::lock_guard<std::mutex> lk(mu_);
+      finished_.notify_all();
+    }
+  }
+
+  const pid_t pid_;
+  std::mutex job_mu_;
+  std::mutex mu_;
+  std::condition_variable wake_, finished_;
+  std::shared_ptr<Job> current_;
+  uint64_t generation_ = 0;
+  int n_workers_ = 0;
+};
+
 // Elements [lo, hi) of one thread's part: plain runs with `k`, no-decay runs with `knd`.
 void update_part(RangeFn fn, const Scalars& k, const Scalars& knd, const void* grad, float* master, float* m,
                  float* v, uint16_t* pout, int64_t lo, int64_t hi, const int64_t* runs, int64_t n_runs) {
@@ -197,16 +290,15 @@ void adamw(const Scalars& k, int grad_dt, const void* grad, float* master, float
   const int64_t max_parts = (count + kGrain - 1) / kGrain;
   const int parts = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(n_threads, max_parts)));
   const int64_t per = ((count + parts - 1) / parts + 63) / 64 * 64;
-  std::vector<std::thread> pool;
-  pool.reserve(parts - 1);
-  for (int p = 1; p < parts; ++p) {
+  auto part = [&](int p) {
     const int64_t lo = std::min(count, p * per), hi = std::min(count, (p + 1) * per);
-    if (lo < hi)
-      pool.emplace_back(update_part, fn, std::cref(k), std::cref(knd), grad, master, m, v, pout, lo, hi, nd_runs,
-                        n_runs);
+    if (lo < hi) update_part(fn, k, knd, grad, master, m, v, pout, lo, hi, nd_runs, n_runs);
+  };
+  if (parts == 1) {
+    part(0);
+    return;
   }
-  update_part(fn, k, knd, grad, master, m, v, pout, 0, std::min(count, per), nd_runs, n_runs);
-  for (auto& t : pool) t.join();
+  Pool::get().run(parts, part);
 }
 
 }  // namespace zs_host
