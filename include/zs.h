@@ -26,9 +26,11 @@
  *   - Pointer tables (`src_ptrs`, `param_ptrs`, `dst_ptrs`) are DEVICE arrays of n_tensors
  *     device pointers (uint64 each), in parameter-list order, owned by the caller; an entry
  *     for a tensor with zero elements is never read through.
- *   - `stream` is a hipStream_t (NULL = the null stream). Every step call only enqueues
- *     kernels on it and never synchronises the host; results live in device memory.
- *     zs_state_read and zs_state_write are the only calls that synchronise.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Every device step call only
+ *     enqueues kernels on it and never synchronises the host; results live in device
+ *     memory. The calls that synchronise are zs_state_read and zs_state_write (their
+ *     stream), zs_offload_adamw_step (its stream: the host needs the step's scalars) and
+ *     zs_layout_set_no_decay (the device, at set-up).
  *   - Flat buffers, shard-sized fp32 arrays and flat parameter outputs must be 16-byte
  *     aligned (any PyTorch allocation is); a shard view into a flat buffer may start at
  *     any element.
@@ -38,8 +40,10 @@
  *     call or at zs_state_read. zs_last_error() gives a message for the calling thread.
  *   - Non-finite gradients are data, not errors: they set the overflow flag and make the
  *     AdamW and unpack kernels skip the update.
- *   - The library keeps no global mutable state besides the per-thread error message;
- *     a layout or state must not be used from two streams at once without ordering them.
+ *   - The library's only global state is the per-thread error message and the pool of
+ *     host threads that the host AdamW update uses (started on first use; calls from
+ *     several threads take turns on it). A layout or state must not be used from two
+ *     streams at once without ordering them.
  */
 #ifndef ZS_H
 #define ZS_H
