@@ -222,6 +222,8 @@ def main():
     ap.add_argument("--offload-threads", type=int, default=0, help="host threads (0: OMP_NUM_THREADS or all)")
     ap.add_argument("--no-decay", choices=["none", "1d"], default="none",
                     help="1d: tensors with at most one dimension (biases, norm weights) take no weight decay")
+    ap.add_argument("--state-spacing-gib", type=float, default=0.0,
+                    help="place master, m and v this many GiB apart in one allocation (0: three allocations)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the single-rank step captured once in a HIP graph and replayed, against the "
                          "same step issued call by call (launch-bound small lists)")
@@ -268,7 +270,8 @@ def main():
                              weight_decay=hp["weight_decay"], max_norm=hp["max_norm"], dp_world=wl.dp_world,
                              dp_rank=wl.dp_rank, align=wl.align, dynamic_loss_scale=wl.dynamic,
                              init_scale=wl.init_scale, growth_interval=wl.growth_interval, accum_dtype=accum,
-                             no_decay="1d" if args.no_decay == "1d" else None)
+                             no_decay="1d" if args.no_decay == "1d" else None,
+                             state_spacing=int(args.state_spacing_gib * (1 << 30)) or None)
     S = opt.shard_numel
     N = wl.n_elems
     d, r = wl.dp_world, wl.dp_rank
@@ -429,7 +432,7 @@ def main():
                    "shard_elements": S, "grad_dtype": wl.dtype, "align": wl.align, "grad_accum": G,
                    "accum_dtype": ("fp32" if accum is not None else wl.dtype),
                    "bucket_numel": args.bucket_numel or None, "buckets": len(buckets) if buckets else None,
-                   "no_decay": args.no_decay},
+                   "no_decay": args.no_decay, "state_spacing_gib": args.state_spacing_gib or None},
         "achieved_hbm_gbps": step_gbps,
         "hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": step_bytes,

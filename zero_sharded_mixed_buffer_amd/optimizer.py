@@ -32,7 +32,7 @@ class ZeroShardedAdamW:
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, max_norm=1.0,
                  dp_world=1, dp_rank=0, align=1, dynamic_loss_scale=None, init_scale=None, scale_floor=1.0,
                  growth_interval=1000, grad_dtype=None, accum_dtype=None, offload=False,
-                 offload_chunk=1 << 24, offload_threads=0, no_decay=None):
+                 offload_chunk=1 << 24, offload_threads=0, no_decay=None, state_spacing=None):
         params = list(params)
         if not params:
             raise ValueError("empty parameter list")
@@ -72,7 +72,18 @@ class ZeroShardedAdamW:
         self._grad_key = None
         self._grad_ptrs = None
         S = self.shard_numel
-        if not self.offload:
+        if not self.offload and state_spacing:
+            # master, m and v carved from one allocation, `state_spacing` bytes apart (at
+            # least their own size): on MI355X, arrays streamed together run faster when
+            # they sit some GiB apart in HBM than when they sit back to back
+            gap = max(int(state_spacing), 4 * S)
+            gap = (gap + (1 << 21) - 1) // (1 << 21) * (1 << 21) // 4   # 2 MiB steps, in floats
+            self._state_arena = torch.zeros(2 * gap + S, dtype=torch.float32, device=dev)
+            self.master = self._state_arena[0:S]
+            self.m = self._state_arena[gap:gap + S]
+            self.v = self._state_arena[2 * gap:2 * gap + S]
+            A.zs_pack(self.layout, self.param_ptrs, self.param_dtype, self.master, torch.float32, whole_flat=False)
+        elif not self.offload:
             self.master = torch.empty(S, dtype=torch.float32, device=dev)
             self.m = torch.zeros(S, dtype=torch.float32, device=dev)
             self.v = torch.zeros(S, dtype=torch.float32, device=dev)
