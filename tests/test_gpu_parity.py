@@ -602,3 +602,26 @@ def test_step_captures_into_a_hip_graph():
         assert sa["step_t"] == sb["step_t"] == replay + 2 and sa["sumsq"] == sb["sumsq"]
     graph_opt.close()
     eager_opt.close()
+
+
+def test_spaced_state_placement_gives_the_same_results():
+    """master, m and v carved from one allocation at a chosen distance (state_spacing) hold
+    exactly what three separate allocations hold."""
+    from harness import bits
+    Z = _z()
+    wl = WORKLOADS["llama_mini"]
+    dev = torch.device("cuda", 0)
+    p0 = gen.make_params(wl, dev)
+    a = Z.ZeroShardedAdamW([p.clone() for p in p0])
+    b = Z.ZeroShardedAdamW([p.clone() for p in p0], state_spacing=64 << 20)
+    assert b.m.data_ptr() - b.master.data_ptr() == 64 << 20
+    for step in range(1, 4):
+        grads = gen.make_grads(wl, step, 1.0, dev, with_faults=False)
+        a.step(grads)
+        b.step(grads)
+    torch.cuda.synchronize()
+    for x, y in ((a.master, b.master), (a.m, b.m), (a.v, b.v)):
+        assert torch.equal(bits(x), bits(y))
+    assert all(torch.equal(bits(x), bits(y)) for x, y in zip(a.params, b.params))
+    a.close()
+    b.close()
