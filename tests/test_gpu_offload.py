@@ -92,3 +92,83 @@ def test_offload_invalid_arguments():
         assert e.value.status == -1
     Z.zs_state_destroy(st)
     Z.zs_layout_destroy(lay)
+
+
+def test_every_variant_together():
+    """fp16 with a dynamic scale, 4 ranks (this is rank 2), 3 accumulated micro-steps in an
+    fp32 buffer packed bucket by bucket, no-decay 1-D tensors and the offloaded update, with
+    injected overflows: against the oracle step by step."""
+    import math
+
+    import oracle as O
+    from harness import REL_TOL, bits, oracle_scaler, rel_err
+    Z = _z()
+    wl = WORKLOADS["moe_mini_dp4"]
+    dev = torch.device("cuda", 0)
+    d, r = wl.dp_world, wl.dp_rank
+    hp = wl.hparams
+    flags = [len(shape) <= 1 for _, shape in wl.shapes]
+    params = gen.make_params(wl, dev)
+    opt = Z.ZeroShardedAdamW(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                             weight_decay=hp["weight_decay"], max_norm=hp["max_norm"], dp_world=d, dp_rank=r,
+                             dynamic_loss_scale=True, init_scale=wl.init_scale, accum_dtype=torch.float32,
+                             offload=True, offload_chunk=50_000, offload_threads=3, no_decay=flags)
+    ref = O.OracleRank(wl.numels, d, r, [p.cpu() for p in params], oracle_scaler(wl), hp, no_decay=flags)
+    lay = ref.layout
+    S = lay.shard_numel
+    others = []
+    for q in range(d):
+        if q != r:
+            lq = Z.zs_layout_create(wl.numels, d, q)
+            others.append((q, lq, Z.zs_state_create(lq, Z.state_host(wl.init_scale, 1.0, True))))
+    exch = torch.zeros(d, dtype=torch.float64, device=dev)
+    buckets = opt.buckets(40_000)
+    faults = {2: [(0, 5, float("inf"))], 5: [(3, 1, float("nan"))]}
+    skipped = []
+    try:
+        for step in range(1, 7):
+            scale = ref.scaler.loss_scale
+            micro = [gen.make_grads(wl, step * 10 + k, scale, dev, with_faults=False) for k in range(3)]
+            for t, kk, val in faults.get(step, []):
+                micro[-1][t].view(-1)[kk] = val
+            for k, g in enumerate(micro):
+                for b in buckets[::-1] if k % 2 else buckets:
+                    opt.pack_bucket(g, b, accumulate=k > 0)
+            opt.check(local_sumsq_out=exch[r:r + 1])
+            for q, lq, sq in others:
+                Z.zs_unscale_check(lq, opt.flat[q * S:(q + 1) * S], torch.float32, sq, None, exch[q:q + 1])
+            opt.norm(rank_sumsq=exch)
+            for q, lq, sq in others:
+                Z.zs_grad_norm(lq, None, torch.float32, sq, opt.hp, exch, None)
+                Z.zs_scaler_update(sq)
+            prev = [p.cpu() for p in params]
+            opt.update()
+            torch.cuda.synchronize()
+            acc = O.pack([x.cpu() for x in micro[0]], lay, torch.float32)
+            for g in micro[1:]:
+                acc = O.accumulate(acc, [x.cpu() for x in g], lay)
+            got = opt.flat.cpu()
+            # bit-exact, NaN payloads aside (any NaN skips the step)
+            differ = (bits(got) != bits(acc)) & ~(torch.isnan(got) & torch.isnan(acc))
+            assert not bool(differ.any()), f"step {step}: accumulated buffer differs"
+            other, ext = [], False
+            for q in range(d):
+                sq_ = acc[q * S:(q + 1) * S]
+                bad = O.nonfinite_any(sq_)
+                other.append(math.inf if bad else O.sumsq_unscaled(sq_, scale))
+                ext = ext or (bad and q != r)
+            rec = ref.step(O.shard_of(acc, lay), ext_overflow=ext, other_sumsq=other)
+            st = opt.read_state()
+            skipped.append(int(rec["overflow"]))
+            assert st["loss_scale"] == ref.scaler.loss_scale and st["step_t"] == ref.scaler.step_t
+            assert st["skipped_total"] == ref.scaler.skipped_total
+            for a, b in ((opt.master, ref.master), (opt.m, ref.m), (opt.v, ref.v)):
+                assert rel_err(a, b) <= REL_TOL
+            want = prev if rec["overflow"] else O.unpack(opt.master, lay, prev, False)
+            assert all(torch.equal(bits(a.cpu()), bits(b)) for a, b in zip(params, want))
+        assert skipped == [0, 1, 0, 0, 1, 0]
+    finally:
+        for _, lq, sq in others:
+            Z.zs_state_destroy(sq)
+            Z.zs_layout_destroy(lq)
+        opt.close()
