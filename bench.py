@@ -224,6 +224,9 @@ def main():
                     help="1d: tensors with at most one dimension (biases, norm weights) take no weight decay")
     ap.add_argument("--state-spacing-gib", type=float, default=0.0,
                     help="place master, m and v this many GiB apart in one allocation (0: three allocations)")
+    ap.add_argument("--log-steps", type=int, default=0,
+                    help="after the timed region, run this many more steps reading the state after each and "
+                         "print one [zs_step k] line per step (scale, skips, norm, clip, time)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the single-rank step captured once in a HIP graph and replayed, against the "
                          "same step issued call by call (launch-bound small lists)")
@@ -420,6 +423,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "steps_per_s": 1e3 / ms_per_step,
         "step_ms_events": {"median": step_median, "p90": step_p90, "min": step_ms[0], "max": step_ms[-1]},
         "higher_is_better": True,
         "scaling": "weak",
@@ -450,6 +454,19 @@ def main():
                      "bytes_per_launch": adamw_bytes, "avg_launch_ms": adamw_ms,
                      "traffic_over_algorithmic": None if traffic is None else traffic / adamw_bytes},
     }
+    if args.log_steps > 0 and d == 1 and G == 1 and buckets is None:
+        # untimed: each step is followed by a synchronising state read
+        for k in range(args.log_steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            one_step()
+            e1.record(stream)
+            st_k = opt.read_state(stream)
+            log(f"[zs_step {st_k['step_t']}] scale={st_k['loss_scale']:g} skipped={st_k['skipped_total']} "
+                f"norm={st_k['grad_norm']:.6g} clip={st_k['clip_coef']:.6g} ms={e0.elapsed_time(e1):.3f} "
+                f"elems/s={S / (e0.elapsed_time(e1) * 1e-3):.4g}")
+    out["memory"] = {"max_allocated_gb": torch.cuda.max_memory_allocated() / 1e9,
+                     "device_total_gb": torch.cuda.get_device_properties(0).total_memory / 1e9}
     opt.close()
     del params, grads, opt
     torch.cuda.empty_cache()
