@@ -29,6 +29,24 @@ def pointer_table(tensors, device):
 
 
 class ZeroShardedAdamW:
+    """One data-parallel rank's ZeRO-1/2 AdamW over bf16/fp16 parameters on one GPU.
+
+    params: the model-dtype parameter tensors (contiguous, on the GPU), in a fixed order.
+    lr, betas, eps, weight_decay: torch.optim.AdamW's; max_norm: global clipping
+        threshold (<= 0: no clipping).
+    dp_world, dp_rank: the data-parallel group; this object owns shard dp_rank of the
+        flat buffer.  align: per-tensor alignment of the flat layout in elements.
+    dynamic_loss_scale, init_scale, scale_floor, growth_interval: the loss scaler
+        (dynamic by default for fp16, a static scale of 1 for bf16).
+    grad_dtype: the dtype of the incoming gradients (default: the parameters').
+    accum_dtype: torch.float32 for an fp32 accumulation buffer (default: grad_dtype).
+    offload, offload_chunk, offload_threads: keep master / m / v in host memory and run
+        the update on the host CPU in chunks.
+    no_decay: one flag per tensor (True: no weight decay), or "1d" for every tensor with
+        at most one dimension.
+    state_spacing: carve master / m / v from one allocation this many bytes apart.
+    """
+
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, max_norm=1.0,
                  dp_world=1, dp_rank=0, align=1, dynamic_loss_scale=None, init_scale=None, scale_floor=1.0,
                  growth_interval=1000, grad_dtype=None, accum_dtype=None, offload=False,
