@@ -129,7 +129,7 @@ def run_parity_sampled(wl, steps=None, log=print):
     hp = wl.hparams
     lay = O.plan_layout(wl.numels, d, rank, align)
     S = lay.shard_numel
-    wins = sample_windows(lay, seed=wl.seed)
+    wins = sample_windows(lay, width=1 << 20, n_random=48, seed=wl.seed)
     params = gen.make_params(wl, dev)
     params_cpu0 = [p.cpu() for p in params]
     opt = Z.ZeroShardedAdamW(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
