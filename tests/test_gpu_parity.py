@@ -246,37 +246,38 @@ def test_determinism_two_runs_bit_identical():
     assert a[3]["sumsq"] == b[3]["sumsq"] and a[3]["clip_coef"] == b[3]["clip_coef"]
 
 
-def test_checkpoint_resume_bit_identical():
-    """6 steps straight == 3 steps, save (state + master/m/v), restore into a new object, 3 steps."""
+@pytest.mark.parametrize("resume_offloaded", [False, True])
+def test_checkpoint_resume_bit_identical(resume_offloaded):
+    """6 steps straight == 3 steps, save (state + master/m/v + params), restore into a new
+    object, 3 steps.  The restored object may also be an offloaded one: the saved device
+    state continues on the host with the same bits."""
     from harness import bits
     Z = _z()
-    wl = WORKLOADS["moe_mini_dp4"]
-    wl1 = WORKLOADS["llama_mini"]
+    w = WORKLOADS["llama_mini"]
     dev = torch.device("cuda", 0)
-    for w in (wl1,):
-        p0 = gen.make_params(w, dev)
-        a = Z.ZeroShardedAdamW([p.clone() for p in p0])
-        for s in range(1, 7):
-            a.step(gen.make_grads(w, s, 1.0, dev))
-        b = Z.ZeroShardedAdamW([p.clone() for p in p0])
-        for s in range(1, 4):
-            b.step(gen.make_grads(w, s, 1.0, dev))
-        saved = (b.read_state(), b.master.clone(), b.m.clone(), b.v.clone(), [p.clone() for p in b.params])
-        b.close()
-        c = Z.ZeroShardedAdamW(saved[4])
-        c.write_state(saved[0])
-        c.master.copy_(saved[1])
-        c.m.copy_(saved[2])
-        c.v.copy_(saved[3])
-        for s in range(4, 7):
-            c.step(gen.make_grads(w, s, 1.0, dev))
-        for x, y in ((a.master, c.master), (a.m, c.m), (a.v, c.v)):
-            assert torch.equal(bits(x), bits(y))
-        assert all(torch.equal(bits(x), bits(y)) for x, y in zip(a.params, c.params))
-        assert a.read_state()["step_t"] == c.read_state()["step_t"] == 6
-        a.close()
-        c.close()
-    del wl
+    p0 = gen.make_params(w, dev)
+    a = Z.ZeroShardedAdamW([p.clone() for p in p0])
+    for s in range(1, 7):
+        a.step(gen.make_grads(w, s, 1.0, dev))
+    b = Z.ZeroShardedAdamW([p.clone() for p in p0])
+    for s in range(1, 4):
+        b.step(gen.make_grads(w, s, 1.0, dev))
+    saved = (b.read_state(), b.master.clone(), b.m.clone(), b.v.clone(), [p.clone() for p in b.params])
+    b.close()
+    c = Z.ZeroShardedAdamW(saved[4], offload=resume_offloaded, offload_chunk=100_000)
+    c.write_state(saved[0])
+    c.master.copy_(saved[1])
+    c.m.copy_(saved[2])
+    c.v.copy_(saved[3])
+    for s in range(4, 7):
+        c.step(gen.make_grads(w, s, 1.0, dev))
+    torch.cuda.synchronize()
+    for x, y in ((a.master, c.master), (a.m, c.m), (a.v, c.v)):
+        assert torch.equal(bits(x.cpu()), bits(y.cpu()))
+    assert all(torch.equal(bits(x), bits(y)) for x, y in zip(a.params, c.params))
+    assert a.read_state()["step_t"] == c.read_state()["step_t"] == 6
+    a.close()
+    c.close()
 
 
 def test_unpack_whole_flat_and_shard():
