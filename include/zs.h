@@ -292,6 +292,28 @@ zs_status zs_unpack(const zs_layout* layout, const void* src, zs_dtype src_dtype
  * Errors: ZS_EINVAL on a NULL state. */
 zs_status zs_scaler_update(zs_state* state, void* stream);
 
+/* The whole single-rank step in one call: zs_pack (whole flat buffer, fused check) ->
+ * zs_grad_norm -> zs_adamw_step (scatter into the parameters) -> zs_scaler_update ("nano-
+ * deepspeed", section 2: the stage-2 packed buffer with local scatter-back and dynamic loss
+ * scaling; "Deep dive: Megatron", section "Distributed optimizer" with one rank;
+ * "ZeRO-Offload and ZeRO-Infinity": clipping and the loss-scale window).  It enqueues the
+ * same kernels as those four calls, so the results are the same bit for bit; a small
+ * list's step then costs its kernel launches instead of four calls through the caller's
+ * binding.
+ *   layout: dp_world must be 1.
+ *   grad_ptrs: device pointer table of the gradients, grad_dtype (bf16 or fp16).
+ *   flat: device buffer of flat_numel elements of grad_dtype, 16-byte aligned; receives
+ *         the packed gradients (and keeps them).
+ *   master, m, v: device fp32 arrays of shard_numel elements, 16-byte aligned, updated in
+ *         place unless the step overflows.
+ *   param_ptrs: device pointer table of the parameters (param_dtype, bf16 or fp16), which
+ *         receive the cast of the new master.
+ * Errors: ZS_EINVAL on dp_world != 1, NULL pointers, dtypes, misalignment, a state of
+ * another layout or invalid hyper-parameters; nothing is enqueued then. */
+zs_status zs_step(const zs_layout* layout, const void* grad_ptrs, zs_dtype grad_dtype, void* flat,
+                  zs_state* state, const zs_adamw_hparams* hp, float* master, float* m, float* v,
+                  const void* param_ptrs, zs_dtype param_dtype, void* stream);
+
 /* Offloaded optimizer step: the fp32 master, m and v live in host memory and the host CPU
  * runs the update, which is bound by memory bandwidth, not by arithmetic ("3.7
  * Megatron-LM, DeepSpeed & Parallelism in Practice", section "ZeRO-Offload and

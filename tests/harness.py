@@ -246,11 +246,12 @@ def run_parity_sampled(wl, steps=None, log=print):
 
 
 def run_parity(wl, steps=None, align=None, dp_rank=None, check_every_step=True, offload=False,
-               offload_chunk=1 << 24, no_decay=None):
+               offload_chunk=1 << 24, no_decay=None, use_step=False):
     """Run `steps` optimizer steps of workload `wl` on cuda:0 and in the oracle, checking
     every stage each step.  offload=True keeps master / m / v in host memory and runs the
     update on the host (zs_offload_adamw_step, in chunks of offload_chunk elements).
     no_decay: per-tensor flags of tensors that take no weight decay (or None).
+    use_step=True (one rank): each step is the single zs_step call (ZeroShardedAdamW.step).
     Returns a RunReport; raises AssertionError on a mismatch of the bit-exact quantities."""
     steps = wl.steps if steps is None else steps
     align = wl.align if align is None else align
@@ -292,8 +293,16 @@ def run_parity(wl, steps=None, align=None, dp_rank=None, check_every_step=True, 
             prev_params = [p.cpu() for p in params_gpu]
 
             # ---- GPU path
-            opt.pack(grads)
-            if d == 1:
+            if use_step:
+                # the single call: the flag, norm and clip it leaves in the state are the
+                # ones the update used (the scaler commit changes only the scale and counts)
+                opt.step(grads)
+                st_before = st = opt.read_state()
+            else:
+                opt.pack(grads)
+            if use_step:
+                pass
+            elif d == 1:
                 opt.norm()
             else:
                 for q in range(d):
@@ -307,9 +316,10 @@ def run_parity(wl, steps=None, align=None, dp_rank=None, check_every_step=True, 
                 for lq, sq in others.values():
                     Z.zs_grad_norm(lq, None, dt, sq, opt.hp, exchange, None)
                     Z.zs_scaler_update(sq)
-            st_before = opt.read_state()
-            opt.update()
-            st = opt.read_state()
+            if not use_step:
+                st_before = opt.read_state()
+                opt.update()
+                st = opt.read_state()
             for lq, sq in others.values():
                 assert Z.zs_state_read(sq).loss_scale == st["loss_scale"]
 

@@ -35,6 +35,7 @@ from ._abi import (  # noqa: F401
     zs_plan,
     zs_plan_segments,
     zs_scaler_update,
+    zs_step,
     zs_state_create,
     zs_state_destroy,
     zs_state_read,

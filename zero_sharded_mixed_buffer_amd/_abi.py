@@ -73,6 +73,8 @@ _SIGS = {
                       c_void_p, c_void_p, c_int32, c_void_p],
     "zs_unpack": [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_void_p],
     "zs_scaler_update": [c_void_p, c_void_p],
+    "zs_step": [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, POINTER(AdamwHParams), c_void_p, c_void_p,
+                c_void_p, c_void_p, c_int32, c_void_p],
     "zs_host_adamw_step": [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_int64, POINTER(AdamwHParams),
                            POINTER(StateHost), c_void_p, c_int32, c_int32],
     "zs_offload_adamw_step": [c_void_p, c_void_p, c_int32, c_void_p, POINTER(AdamwHParams), c_void_p, c_void_p,
@@ -290,6 +292,14 @@ def zs_unpack(layout, src, src_dtype, whole_flat, dst_ptrs, dst_dtype, honour_sk
 
 def zs_scaler_update(state, stream=None):
     _check(lib().zs_scaler_update(state, _stream(stream)), "zs_scaler_update")
+
+
+def zs_step(layout, grad_ptrs, grad_dtype, flat, state, hp: AdamwHParams, master, m, v, param_ptrs,
+            param_dtype=ZS_BF16, stream=None):
+    """The whole single-rank step: pack, check, norm, AdamW with scatter, scaler commit."""
+    _check(lib().zs_step(layout, _ptr(grad_ptrs), dtype_code(grad_dtype), _ptr(flat), state, byref(hp),
+                         _ptr(master), _ptr(m), _ptr(v), _ptr(param_ptrs), dtype_code(param_dtype),
+                         _stream(stream)), "zs_step")
 
 
 def zs_last_error():

@@ -601,6 +601,45 @@ extern "C" zs_status zs_scaler_update(zs_state* state, void* stream) {
   return ok();
 }
 
+extern "C" zs_status zs_step(const zs_layout* l, const void* grad_ptrs, zs_dtype grad_dtype, void* flat,
+                             zs_state* state, const zs_adamw_hparams* hp, float* master, float* m, float* v,
+                             const void* param_ptrs, zs_dtype param_dtype, void* stream) {
+  const TraceRange trace("zs_step");
+  zs_status st = check_layout(l);
+  if (st != ZS_OK) return st;
+  st = check_state(l, state);
+  if (st != ZS_OK) return st;
+  st = check_hparams(hp);
+  if (st != ZS_OK) return st;
+  if (l->plan.dp_world != 1) return fail(ZS_EINVAL, "zs_step is the single-rank step: dp_world must be 1");
+  if (grad_ptrs == nullptr || flat == nullptr || param_ptrs == nullptr)
+    return fail(ZS_EINVAL, "grad_ptrs, flat and param_ptrs must not be NULL");
+  if (master == nullptr || m == nullptr || v == nullptr) return fail(ZS_EINVAL, "master, m and v must not be NULL");
+  if (!is_half_dtype(grad_dtype) || !is_half_dtype(param_dtype))
+    return fail(ZS_EINVAL, "grad_dtype and param_dtype must be bf16 or fp16");
+  if (!aligned16(flat)) return fail(ZS_EINVAL, "the flat buffer must be 16-byte aligned");
+  if (!aligned16(master) || !aligned16(m) || !aligned16(v)) return fail(ZS_EINVAL, "master, m, v must be 16-byte aligned");
+  hipStream_t s = as_stream(stream);
+  // The kernels of zs_pack (fused check), zs_grad_norm, zs_adamw_step and zs_scaler_update,
+  // enqueued by one call: a small list's step costs the launches, not four trips through
+  // the caller's binding.
+  hipError_t e = zs::launch_pack(l->map_full, static_cast<const uint64_t*>(grad_ptrs), grad_dtype, flat, grad_dtype,
+                                 false, state->partials, s);
+  if (e != hipSuccess) return hip_fail(e, "launching pack");
+  e = zs::launch_reduce_finalize(state->partials, zs::reduction_blocks(l->map_full.len),
+                                 state->partials + state->nparts, state->dev, nullptr, zs::kFlagSet, nullptr, s);
+  if (e != hipSuccess) return hip_fail(e, "launching the overflow finalize");
+  e = zs::launch_norm_finalize(state->dev, nullptr, 1, 0, nullptr, hp->max_norm, s);
+  if (e != hipSuccess) return hip_fail(e, "launching the norm finalize");
+  const zs::AdamwArgs a{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
+  e = zs::launch_adamw(l->map_shard, flat, grad_dtype, master, m, v, a, state->dev,
+                       static_cast<const uint64_t*>(param_ptrs), nullptr, param_dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "launching adamw");
+  e = zs::launch_scaler_update(state->dev, s);
+  if (e != hipSuccess) return hip_fail(e, "launching the scaler update");
+  return ok();
+}
+
 extern "C" const char* zs_last_error(void) { return g_last_error.c_str(); }
 
 // ---------------------------------------------------------------------------- offloaded step

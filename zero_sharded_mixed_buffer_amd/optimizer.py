@@ -5,7 +5,8 @@ buffer, fp32 master / m / v of its shard, device pointer tables) and issues the
 step as a fixed sequence of ABI calls on one stream:
 
     zs_pack -> zs_unscale_check -> zs_grad_norm -> zs_adamw_step -> zs_scaler_update
-    (dp_world == 1: the check is fused into the pack pass)
+    (dp_world == 1: the check is fused into the pack pass, and a step of one
+    micro-step is the single call zs_step)
 
 It makes no decisions of its own and never synchronises; the skip on overflow,
 the clip and the scaler all happen on the device.  With offload=True the fp32
@@ -198,6 +199,11 @@ class ZeroShardedAdamW:
             raise ValueError("step() is the single-rank sequence; call pack/check/norm/update with the "
                              "other ranks' flag and partial sums for dp_world > 1")
         micro = grads if (grads and isinstance(grads[0], (list, tuple))) else [grads]
+        if len(micro) == 1 and not self.offload and self.grad_dtype == self.model_grad_dtype:
+            # one call enqueueing the kernels of the sequence below (same results, fewer calls)
+            A.zs_step(self.layout, self._grad_table(micro[0]), self.model_grad_dtype, self.flat, self.state,
+                      self.hp, self.master, self.m, self.v, self.param_ptrs, self.param_dtype, stream=stream)
+            return
         for i, g in enumerate(micro):
             self.pack(g, stream, accumulate=i > 0, last=i == len(micro) - 1)
         self.norm(stream=stream)
