@@ -761,7 +761,10 @@ extern "C" zs_status zs_offload_adamw_step(const zs_layout* l, const void* shard
     e = hipMemcpyAsync(pdst + off * pb, pslot, static_cast<size_t>(n) * pb, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipEventRecord(ev_p[slot], s);
   }
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e == hipSuccess)
+    e = hipStreamSynchronize(s);
+  else
+    (void)hipStreamSynchronize(s);  // no copy may still touch the caller's buffers after return
   for (int i = 0; i < 2; ++i) {
     if (ev_g[i]) (void)hipEventDestroy(ev_g[i]);
     if (ev_p[i]) (void)hipEventDestroy(ev_p[i]);
