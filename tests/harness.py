@@ -86,15 +86,17 @@ def oracle_scaler(wl):
     return O.OracleScaler(wl.init_scale, 1.0, wl.dynamic, wl.growth_interval)
 
 
-def sample_windows(lay, width=1 << 16, n_random=24, seed=0):
+def sample_windows(lay, width=1 << 16, n_random=24, seed=0, centres=()):
     """Deterministic shard windows [a, b) (shard-relative): the first and last `width`
     elements, windows across the first and last four tensor boundaries inside the shard,
-    and n_random seeded ones."""
+    windows centred on the given shard-relative positions, and n_random seeded ones."""
     import random
     S = lay.shard_numel
     lo, hi = lay.shard_begin, lay.shard_begin + S
     w = min(width, S)
     starts = {0, S - w}
+    for c in centres:
+        starts.add(min(max(c - w // 2, 0), S - w))
     inside = [off for off in lay.offsets if lo < off < hi]
     for off in inside[:4] + inside[-4:]:
         starts.add(min(max(off - lo - w // 2, 0), S - w))
@@ -116,7 +118,7 @@ def _window_values(tensors_cpu, lay, a, b, dtype):
     return out
 
 
-def run_parity_sampled(wl, steps=None, log=print):
+def run_parity_sampled(wl, steps=None, log=print, centres=(), n_random=48):
     """Full-size parity on sampled outputs.  The GPU runs the whole step at the workload's
     real size in the same launch configuration as bench.py; the oracle computes every
     step's flag, scaler and global norm from all gradients (streamed to the host one
@@ -129,7 +131,7 @@ def run_parity_sampled(wl, steps=None, log=print):
     hp = wl.hparams
     lay = O.plan_layout(wl.numels, d, rank, align)
     S = lay.shard_numel
-    wins = sample_windows(lay, width=1 << 20, n_random=48, seed=wl.seed)
+    wins = sample_windows(lay, width=1 << 20, n_random=n_random, seed=wl.seed, centres=centres)
     params = gen.make_params(wl, dev)
     params_cpu0 = [p.cpu() for p in params]
     opt = Z.ZeroShardedAdamW(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],

@@ -30,6 +30,26 @@ def test_fullsize_sampled_parity(name, steps):
           flush=True)
 
 
+def test_tensor_beyond_int32_element_indices():
+    """One tensor of 2^31 + 4099 elements between two small ones: element indices above 2^31
+    and fp32 byte offsets above 2^32 in every array.  Sampled windows sit across those
+    boundaries (elements 2^30 and 2^31 of the shard) and at the ends; two steps."""
+    import math
+    import zero_sharded_mixed_buffer_amd as Z
+    from harness import run_parity_sampled
+    from workloads.configs import Workload
+    Z.lib()
+    shapes = (("a", (3,)), ("big", (2 ** 31 + 4099,)), ("c", (5,)))
+    wl = Workload("beyond_int32", shapes, "bf16", 1, 0, False, 1.0, 1e-3, 0.02, 2, 77)
+    print(f"[case] fullsize beyond_int32: N={wl.n_elems}", flush=True)
+    t0 = time.time()
+    centres = (2 ** 30, 2 ** 31, 2 ** 31 + 3, 2 ** 32 // 3)
+    worst, ndiff, wins = run_parity_sampled(wl, log=lambda s: print(s, flush=True), centres=centres, n_random=8)
+    assert any(a < 2 ** 31 < b for a, b in wins) and wl.n_elems > 2 ** 31 and not math.isnan(worst["master"])
+    print(f"[fullsize] beyond_int32: {len(wins)} windows, worst={worst}, ndiff={ndiff}, {time.time() - t0:.1f} s",
+          flush=True)
+
+
 @pytest.mark.parametrize("name,flat_kind", [("llama3_8b", "model"), ("llama3_8b", "fp32"), ("ragged_20k", "model")])
 def test_fullsize_bucketed_pack(name, flat_kind):
     """The full-size gradient list packed in 5e8-element buckets (the pages' reduce_bucket_size),
