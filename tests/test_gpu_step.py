@@ -1,8 +1,10 @@
 """The single-call step zs_step (ZeroShardedAdamW.step with one rank and one micro-step).
 
 zs_step enqueues the kernels of zs_pack (fused check), zs_grad_norm, zs_adamw_step and
-zs_scaler_update.  Checked here on both sides of 4096 pack blocks (16,777,216 elements),
-where the fold of the partial sums switches from one finalize workgroup to two levels:
+zs_scaler_update.  Checked here on both sides of 256 tiles (1,048,576 elements), below
+which the AdamW kernel runs four workgroups per tile, and of 4096 pack blocks (16,777,216
+elements), where the fold of the partial sums switches from one finalize workgroup to two
+levels:
 - parity with the CPU oracle, at the bar of the other parity tests;
 - bit-identity with the four-call sequence, step by step, through overflow skips and
   scale growth;
@@ -21,6 +23,7 @@ from workloads.configs import Workload
 pytestmark = pytest.mark.gpu
 
 FOLD_ELEMS = 4096 * 4096  # the largest pack whose partial sums one finalize workgroup folds
+SPLIT_ELEMS = 256 * 4096  # the largest shard whose AdamW runs four workgroups per tile
 
 
 def _z():
@@ -47,11 +50,21 @@ def _over_one_level():
     return _sized("over_one_level", [("w", (4096, 4096)), ("b", (1000,)), ("c", (7,))], seed=41)
 
 
+def _at_split():  # 256 tiles of 4096: the largest shard whose AdamW runs four workgroups per tile
+    return _sized("at_split", [("w", (1024, 1000)), ("b", (24576,))], seed=42)
+
+
+def _over_split():
+    return _sized("over_split", [("w", (1024, 1000)), ("b", (24577,))], seed=43)
+
+
 CASES = {
     "tiny": lambda: WORKLOADS["tiny"],
     "llama_mini": lambda: WORKLOADS["llama_mini"],
     "ragged_mini": lambda: WORKLOADS["ragged_mini"],
     "ragged_mini_a64": lambda: WORKLOADS["ragged_mini_a64"],
+    "at_split": _at_split,
+    "over_split": _over_split,
     "at_one_level": _at_one_level,
     "over_one_level": _over_one_level,
 }
@@ -63,6 +76,8 @@ def test_step_parity_with_oracle(name):
     _z()
     wl = CASES[name]()
     assert (wl.n_elems <= FOLD_ELEMS) == (name != "over_one_level")
+    if "split" in name:
+        assert (wl.n_elems <= SPLIT_ELEMS) == (name == "at_split")
     print(f"[case] zs_step parity {name} N={wl.n_elems} T={len(wl.numels)} steps={wl.steps}", flush=True)
     rep = run_parity(wl, use_step=True)
     print(f"[parity] {name}: master_err={rep.master_err:.3e} m_err={rep.m_err:.3e} v_err={rep.v_err:.3e} "
@@ -94,7 +109,7 @@ def _assert_same(a, b, tag):
         assert same, f"{tag}: state {k} {sa[k]} != {sb[k]}"
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged_mini", "at_one_level", "over_one_level"])
+@pytest.mark.parametrize("name", ["tiny", "ragged_mini", "at_split", "over_split", "at_one_level", "over_one_level"])
 def test_step_bit_identical_to_the_call_sequence(name):
     Z = _z()
     dev = torch.device("cuda", 0)

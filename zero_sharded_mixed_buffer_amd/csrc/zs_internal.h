@@ -22,6 +22,8 @@ constexpr int kUnroll = 2;
 constexpr int64_t kTile = int64_t(kThreads) * kGroup * kUnroll;
 constexpr int64_t kPackBlock = int64_t(kThreads) * kGroup * 2;
 constexpr int kLevel2 = 1024;  // first-level partial-sum workgroups of the two-level reduction
+// A shard of at most this many tiles runs the AdamW kernel with four workgroups per tile.
+constexpr int64_t kSplitTiles = 256;
 
 // Workgroups (and partial sums) of a pack or check pass over len elements.
 inline int64_t reduction_blocks(int64_t len) { return (len + kPackBlock - 1) / kPackBlock; }

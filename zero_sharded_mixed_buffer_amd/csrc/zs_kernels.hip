@@ -683,25 +683,30 @@ __device__ __forceinline__ v4f load_grad4(const void* shard, int64_t q, int cnt,
 }
 
 // GROUPS: the map carries no-decay flags (a separate instantiation, so that the common
-// single-group kernel keeps its registers).
-template <int GDT, int PDT, bool SCATTER, bool FLAT_OUT, bool GROUPS>
+// single-group kernel keeps its registers).  SPLIT: workgroups per tile, each taking
+// kTile / SPLIT consecutive elements (one quad per thread at SPLIT = 4).  A small shard
+// runs split: its few tiles would otherwise sit on a few CUs, each thread working through
+// four quads of fp64 arithmetic in turn.
+template <int GDT, int PDT, bool SCATTER, bool FLAT_OUT, bool GROUPS, int SPLIT>
 __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const void* __restrict__ shard,
                                                     float* __restrict__ master, float* __restrict__ mom1,
                                                     float* __restrict__ mom2, AdamwArgs hp,
                                                     const DevState* __restrict__ st,
                                                     const uint64_t* __restrict__ ptrs,
                                                     uint16_t* __restrict__ flat_out) {
+  static_assert(SPLIT == 1 || SPLIT == kQuadsPerThread, "a split workgroup takes one quad per thread");
+  constexpr int kQuads = kQuadsPerThread / SPLIT;
   if (st->h.overflow) return;  // device-side skip: nothing changes on an overflowed step
   const StepScalars k = step_scalars(hp, st);
   const bool g_vec = (GDT == ZS_FP32) ? aligned16(shard) : aligned8(shard);
   const int64_t n = mp.len;
-  const int64_t tile = work_unit();
-  const int64_t base = tile * kTile;
-  v4f gv[kQuadsPerThread];
-  v4f pv[kQuadsPerThread], mv[kQuadsPerThread], vv[kQuadsPerThread];
-  int cnts[kQuadsPerThread];
+  const int64_t tile = work_unit() / SPLIT;
+  const int64_t base = tile * kTile + (work_unit() % SPLIT) * (kTile / SPLIT);
+  v4f gv[kQuads];
+  v4f pv[kQuads], mv[kQuads], vv[kQuads];
+  int cnts[kQuads];
 #pragma unroll
-  for (int u = 0; u < kQuadsPerThread; ++u) {
+  for (int u = 0; u < kQuads; ++u) {
     const int64_t q = base + int64_t(u) * (kThreads * 4) + int64_t(threadIdx.x) * 4;
     const int64_t rem = n - q;
     const int cnt = rem >= 4 ? 4 : (rem > 0 ? static_cast<int>(rem) : 0);
@@ -734,16 +739,16 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const void* __res
   // A full tile inside one parameter tensor whose address is not 16-byte aligned (ragged
   // lists): the cast parameters go through LDS and leave as destination-aligned 16-byte
   // chunks; only the at most 15 elements at the two ends of the tile are written singly.
-  __shared__ uint32_t pstage[kTile / 2];
+  __shared__ uint32_t pstage[SPLIT == 1 ? kTile / 2 : 1];
   int pdelta = 0;
-  if (SCATTER && ts.uniform && ts.base != nullptr && base + kTile <= n)
+  if (SPLIT == 1 && SCATTER && ts.uniform && ts.base != nullptr && base + kTile <= n)
     pdelta = int((reinterpret_cast<uintptr_t>(ts.base + base) >> 1) & 7);
   // The quads of the tile; PER_ELEM (a tile across segments with no-decay flags, rare) looks
   // each element's decay up, every other tile uses the tile's one multiplier.
   auto update_quads = [&](auto per_elem) {
     constexpr bool PER_ELEM = decltype(per_elem)::value;
 #pragma unroll
-    for (int u = 0; u < kQuadsPerThread; ++u) {
+    for (int u = 0; u < kQuads; ++u) {
       const int cnt = cnts[u];
       if (cnt <= 0) continue;
       const int64_t q = base + int64_t(u) * (kThreads * 4) + int64_t(threadIdx.x) * 4;
@@ -787,7 +792,7 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const void* __res
         if (FLAT_OUT) st16_elem(flat_out + q, out, cnt);
       }
       if (SCATTER) {
-        if (pdelta != 0) {
+        if (SPLIT == 1 && pdelta != 0) {
           const int e = u * kThreads * 4 + threadIdx.x * 4;  // tile-relative; cnt == 4 here
           pstage[e / 2] = out.w[0];
           pstage[e / 2 + 1] = out.w[1];
@@ -801,7 +806,7 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const void* __res
     update_quads(std::true_type{});
   else
     update_quads(std::false_type{});
-  if (SCATTER && pdelta != 0) {  // uniform across the workgroup
+  if (SPLIT == 1 && SCATTER && pdelta != 0) {  // uniform across the workgroup
     __syncthreads();
     const v4u* L = reinterpret_cast<const v4u*>(pstage);
     uint16_t* D = ts.base + base;            // destination of tile element 0
@@ -959,13 +964,14 @@ hipError_t launch_scaler_update(DevState* st, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int GDT, int PDT, bool GROUPS>
-static void adamw_dispatch_g(const dim3& G, hipStream_t s, const DevMap& map, const void* shard, float* master,
+template <int GDT, int PDT, bool GROUPS, int SPLIT>
+static void adamw_dispatch_s(const dim3& G, hipStream_t s, const DevMap& map, const void* shard, float* master,
                              float* m, float* v, const AdamwArgs& hp, const DevState* st, const uint64_t* ptrs,
                              uint16_t* flat_out) {
   const dim3 B(kThreads);
-#define ZS_ADAMW(SC, FO) \
-  hipLaunchKernelGGL((k_adamw<GDT, PDT, SC, FO, GROUPS>), G, B, 0, s, map, shard, master, m, v, hp, st, ptrs, flat_out)
+#define ZS_ADAMW(SC, FO)                                                                                         \
+  hipLaunchKernelGGL((k_adamw<GDT, PDT, SC, FO, GROUPS, SPLIT>), G, B, 0, s, map, shard, master, m, v, hp, st, \
+                     ptrs, flat_out)
   if (ptrs != nullptr && flat_out != nullptr)
     ZS_ADAMW(true, true);
   else if (ptrs != nullptr)
@@ -975,6 +981,17 @@ static void adamw_dispatch_g(const dim3& G, hipStream_t s, const DevMap& map, co
   else
     ZS_ADAMW(false, false);
 #undef ZS_ADAMW
+}
+
+template <int GDT, int PDT, bool GROUPS>
+static void adamw_dispatch_g(const dim3& G, hipStream_t s, const DevMap& map, const void* shard, float* master,
+                             float* m, float* v, const AdamwArgs& hp, const DevState* st, const uint64_t* ptrs,
+                             uint16_t* flat_out) {
+  if (map.ntiles <= kSplitTiles)
+    adamw_dispatch_s<GDT, PDT, GROUPS, kQuadsPerThread>(dim3(G.x * kQuadsPerThread), s, map, shard, master, m, v,
+                                                         hp, st, ptrs, flat_out);
+  else
+    adamw_dispatch_s<GDT, PDT, GROUPS, 1>(G, s, map, shard, master, m, v, hp, st, ptrs, flat_out);
 }
 
 template <int GDT, int PDT>
