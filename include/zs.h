@@ -296,10 +296,12 @@ zs_status zs_scaler_update(zs_state* state, void* stream);
  * zs_grad_norm -> zs_adamw_step (scatter into the parameters) -> zs_scaler_update ("nano-
  * deepspeed", section 2: the stage-2 packed buffer with local scatter-back and dynamic loss
  * scaling; "Deep dive: Megatron", section "Distributed optimizer" with one rank;
- * "ZeRO-Offload and ZeRO-Infinity": clipping and the loss-scale window).  It enqueues the
- * same kernels as those four calls, so the results are the same bit for bit; a small
- * list's step then costs its kernel launches instead of four calls through the caller's
- * binding.
+ * "ZeRO-Offload and ZeRO-Infinity": clipping and the loss-scale window), with the same
+ * results bit for bit.  It enqueues three kernels instead of five: the pack with the
+ * check's partial sums, one workgroup for the flag, the norm and the scaler commit (the
+ * update reads a copy of the state taken before the commit), and the update.  A small
+ * list's step is bound by launches, so this and the single call through the caller's
+ * binding are what it saves.
  *   layout: dp_world must be 1.
  *   grad_ptrs: device pointer table of the gradients, grad_dtype (bf16 or fp16).
  *   flat: device buffer of flat_numel elements of grad_dtype, 16-byte aligned; receives

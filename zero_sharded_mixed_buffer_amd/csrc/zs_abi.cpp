@@ -164,7 +164,7 @@ struct zs_layout {
 };
 
 struct zs_state {
-  DevState* dev = nullptr;
+  DevState* dev = nullptr;     // the state, then one more DevState: zs_step's pre-commit copy
   double* partials = nullptr;  // nparts slots, then kLevel2 second-level slots
   int64_t nparts = 0;
   int device = 0;
@@ -354,16 +354,16 @@ extern "C" zs_status zs_state_create(const zs_layout* l, const zs_state_host* in
   if (s == nullptr) return fail(ZS_ENOMEM, "host allocation of the state failed");
   s->device = l->device;
   s->nparts = l->nparts;
-  hipError_t e = hipMalloc(reinterpret_cast<void**>(&s->dev), sizeof(DevState));
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(&s->dev), 2 * sizeof(DevState));
   const size_t part_bytes = sizeof(double) * static_cast<size_t>(s->nparts + zs::kLevel2);
   if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&s->partials), part_bytes);
   if (e != hipSuccess) {
     zs_state_destroy(s);
     return fail(ZS_ENOMEM, "hipMalloc for the state: %s", hipGetErrorString(e));
   }
-  DevState h{};
-  h.h = *init;
-  e = hipMemcpy(s->dev, &h, sizeof h, hipMemcpyHostToDevice);
+  DevState h[2]{};
+  h[0].h = *init;
+  e = hipMemcpy(s->dev, h, sizeof h, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemset(s->partials, 0, part_bytes);
   if (e != hipSuccess) {
     zs_state_destroy(s);
@@ -620,23 +620,20 @@ extern "C" zs_status zs_step(const zs_layout* l, const void* grad_ptrs, zs_dtype
   if (!aligned16(flat)) return fail(ZS_EINVAL, "the flat buffer must be 16-byte aligned");
   if (!aligned16(master) || !aligned16(m) || !aligned16(v)) return fail(ZS_EINVAL, "master, m, v must be 16-byte aligned");
   hipStream_t s = as_stream(stream);
-  // The kernels of zs_pack (fused check), zs_grad_norm, zs_adamw_step and zs_scaler_update,
-  // enqueued by one call: a small list's step costs the launches, not four trips through
-  // the caller's binding.
+  // Three launches: the pack with the check's partial sums; one workgroup that sets the
+  // flag, takes the norm, keeps the pre-commit state and commits the scaler; the update,
+  // which reads that pre-commit state.  The arithmetic is the four calls', step for step.
+  DevState* pre = state->dev + 1;
   hipError_t e = zs::launch_pack(l->map_full, static_cast<const uint64_t*>(grad_ptrs), grad_dtype, flat, grad_dtype,
                                  false, state->partials, s);
   if (e != hipSuccess) return hip_fail(e, "launching pack");
-  e = zs::launch_reduce_finalize(state->partials, zs::reduction_blocks(l->map_full.len),
-                                 state->partials + state->nparts, state->dev, nullptr, zs::kFlagSet, nullptr, s);
-  if (e != hipSuccess) return hip_fail(e, "launching the overflow finalize");
-  e = zs::launch_norm_finalize(state->dev, nullptr, 1, 0, nullptr, hp->max_norm, s);
-  if (e != hipSuccess) return hip_fail(e, "launching the norm finalize");
+  e = zs::launch_step_finalize(state->partials, zs::reduction_blocks(l->map_full.len), state->partials + state->nparts,
+                               state->dev, pre, hp->max_norm, s);
+  if (e != hipSuccess) return hip_fail(e, "launching the step finalize");
   const zs::AdamwArgs a{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
-  e = zs::launch_adamw(l->map_shard, flat, grad_dtype, master, m, v, a, state->dev,
-                       static_cast<const uint64_t*>(param_ptrs), nullptr, param_dtype, s);
+  e = zs::launch_adamw(l->map_shard, flat, grad_dtype, master, m, v, a, pre, static_cast<const uint64_t*>(param_ptrs),
+                       nullptr, param_dtype, s);
   if (e != hipSuccess) return hip_fail(e, "launching adamw");
-  e = zs::launch_scaler_update(state->dev, s);
-  if (e != hipSuccess) return hip_fail(e, "launching the scaler update");
   return ok();
 }
 

@@ -71,6 +71,12 @@ hipError_t launch_reduce_finalize(const double* partials, int64_t nparts, double
                                   const int32_t* ext, int mode, double* local_out, hipStream_t s);
 hipError_t launch_norm_finalize(DevState* st, const double* rank_sumsq, int dp_world, int dp_rank,
                                 double* local_out, double max_norm, hipStream_t s);
+// The single-rank step's finalizers in one launch (after the same first-level fold as
+// launch_reduce_finalize): flag and local sum of squares (set mode, no other ranks), norm
+// and clip coefficient, a copy of the state to `pre`, then the scaler commit.  The AdamW
+// launch of that step takes `pre` as its state.
+hipError_t launch_step_finalize(const double* partials, int64_t nparts, double* level2, DevState* st,
+                                DevState* pre, double max_norm, hipStream_t s);
 hipError_t launch_adamw(const DevMap& map, const void* shard, int grad_dt, float* master, float* m, float* v,
                         const AdamwArgs& hp, const DevState* st, const uint64_t* param_ptrs, void* flat_out,
                         int param_dt, hipStream_t s);

@@ -541,37 +541,37 @@ __global__ __launch_bounds__(kThreads) void k_partial_reduce(const double* __res
 
 // ------------------------------------------------------------------ finalize kernels
 
-// One workgroup: add the block partials in a fixed order, set the overflow flag and this
-// rank's unscaled sum of squares.  Every element is finite iff the sum is finite: a finite
-// fp16/bf16 square is below 2^256 and at most 2^63 of them stay far below the fp64 range,
-// while inf or NaN anywhere propagates to the sum.
-__global__ __launch_bounds__(kThreads) void k_flag_finalize(const double* __restrict__ partials, int64_t nparts,
-                                                            DevState* __restrict__ st,
-                                                            const int32_t* __restrict__ ext, int mode,
-                                                            double* __restrict__ local_out) {
+// The fixed-order sum of n partials by one workgroup: per-thread strided sums, then
+// block_sum.  The result is valid in thread 0.
+__device__ __forceinline__ double fold_partials(const double* __restrict__ partials, int64_t n) {
   double acc = 0.0;
-  for (int64_t i = threadIdx.x; i < nparts; i += kThreads) acc += partials[i];
-  const double raw = block_sum(acc);
-  if (threadIdx.x == 0) {
-    const bool bad = !isfinite(raw);
-    const bool other = (ext != nullptr) && (*ext != 0);
-    if (mode == kFlagSet)
-      st->h.overflow = (bad || other) ? 1 : 0;
-    else if (bad)
-      st->h.overflow = 1;
-    st->raw_sumsq = raw;
-    const double inv = 1.0 / st->h.loss_scale;  // exact: the scale is a power of two
-    const double local = (raw * inv) * inv;
-    st->h.local_sumsq = local;
-    if (local_out != nullptr) *local_out = local;
-  }
+  for (int64_t i = threadIdx.x; i < n; i += kThreads) acc += partials[i];
+  return block_sum(acc);
 }
 
-// One thread: global sum of squares in rank order, norm and clip coefficient.  A non-finite
-// partial from any rank (its overflow) makes the global sum non-finite and sets the flag.
-__global__ void k_norm_finalize(DevState* __restrict__ st, const double* __restrict__ rank_sumsq, int dp_world,
-                                int dp_rank, double* __restrict__ local_out, double max_norm) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+// The overflow flag and this rank's unscaled sum of squares from the raw (scaled) sum of
+// squares.  Every element is finite iff the sum is finite: a finite fp16/bf16 square is
+// below 2^256 and at most 2^63 of them stay far below the fp64 range, while inf or NaN
+// anywhere propagates to the sum.
+__device__ __forceinline__ void flag_commit(DevState* st, double raw, const int32_t* ext, int mode,
+                                            double* local_out) {
+  const bool bad = !isfinite(raw);
+  const bool other = (ext != nullptr) && (*ext != 0);
+  if (mode == kFlagSet)
+    st->h.overflow = (bad || other) ? 1 : 0;
+  else if (bad)
+    st->h.overflow = 1;
+  st->raw_sumsq = raw;
+  const double inv = 1.0 / st->h.loss_scale;  // exact: the scale is a power of two
+  const double local = (raw * inv) * inv;
+  st->h.local_sumsq = local;
+  if (local_out != nullptr) *local_out = local;
+}
+
+// Global sum of squares in rank order, norm and clip coefficient.  A non-finite partial from
+// any rank (its overflow) makes the global sum non-finite and sets the flag.
+__device__ __forceinline__ void norm_commit(DevState* st, const double* rank_sumsq, int dp_world, int dp_rank,
+                                            double* local_out, double max_norm) {
   const double local = st->h.local_sumsq;
   double ss = 0.0;
   for (int q = 0; q < dp_world; ++q) ss += (q == dp_rank) ? local : rank_sumsq[q];
@@ -588,9 +588,10 @@ __global__ void k_norm_finalize(DevState* __restrict__ st, const double* __restr
   if (local_out != nullptr) *local_out = local;
 }
 
-// One thread: commit the step in the loss scaler.
-__global__ void k_scaler_update(DevState* __restrict__ st) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+// Commit the step in the loss scaler: an overflowed step is skipped and halves a dynamic
+// scale (not below the floor); an applied one counts and doubles the scale after
+// growth_interval of them.
+__device__ __forceinline__ void scaler_commit(DevState* st) {
   zs_state_host h = st->h;
   if (h.overflow) {
     h.skipped_total += 1;
@@ -610,6 +611,45 @@ __global__ void k_scaler_update(DevState* __restrict__ st) {
     }
   }
   st->h = h;
+}
+
+// One workgroup: add the block partials in a fixed order, set the overflow flag and this
+// rank's unscaled sum of squares.
+__global__ __launch_bounds__(kThreads) void k_flag_finalize(const double* __restrict__ partials, int64_t nparts,
+                                                            DevState* __restrict__ st,
+                                                            const int32_t* __restrict__ ext, int mode,
+                                                            double* __restrict__ local_out) {
+  const double raw = fold_partials(partials, nparts);
+  if (threadIdx.x == 0) flag_commit(st, raw, ext, mode, local_out);
+}
+
+// One thread: global sum of squares in rank order, norm and clip coefficient.
+__global__ void k_norm_finalize(DevState* __restrict__ st, const double* __restrict__ rank_sumsq, int dp_world,
+                                int dp_rank, double* __restrict__ local_out, double max_norm) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  norm_commit(st, rank_sumsq, dp_world, dp_rank, local_out, max_norm);
+}
+
+// One thread: commit the step in the loss scaler.
+__global__ void k_scaler_update(DevState* __restrict__ st) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  scaler_commit(st);
+}
+
+// The single-rank step's three finalizers in one workgroup: the flag and local sum of
+// squares, the norm and clip coefficient, then the scaler commit.  The state as it stands
+// before the commit (the flag, clip coefficient, scale and step count that the update
+// needs) is copied to `pre` first, and the AdamW launch that follows reads `pre`.
+__global__ __launch_bounds__(kThreads) void k_step_finalize(const double* __restrict__ partials, int64_t nparts,
+                                                            DevState* __restrict__ st, DevState* __restrict__ pre,
+                                                            double max_norm) {
+  const double raw = fold_partials(partials, nparts);
+  if (threadIdx.x == 0) {
+    flag_commit(st, raw, nullptr, kFlagSet, nullptr);
+    norm_commit(st, nullptr, 1, 0, nullptr, max_norm);
+    *pre = *st;
+    scaler_commit(st);
+  }
 }
 
 // ------------------------------------------------------------------ AdamW + cast + scatter
@@ -933,22 +973,34 @@ hipError_t launch_check(const void* shard, int64_t n, int dt, double* partials, 
   return hipGetLastError();
 }
 
+// Up to 16 partials per thread go straight to the single finalize workgroup; more are
+// first folded by up to kLevel2 workgroups, each over a contiguous range, in fixed order.
+// Returns the launch status; *partials / *nparts then name what the finalize folds.
+static hipError_t reduce_level2(const double** partials, int64_t* nparts, double* level2, hipStream_t s) {
+  if (*nparts <= int64_t(kThreads) * 16) return hipSuccess;
+  const int64_t per0 = (*nparts + kLevel2 - 1) / kLevel2;
+  const int64_t per = per0 < int64_t(kThreads) * 4 ? int64_t(kThreads) * 4 : per0;
+  const int64_t nb = (*nparts + per - 1) / per;
+  hipLaunchKernelGGL(k_partial_reduce, dim3(static_cast<unsigned>(nb)), dim3(kThreads), 0, s, *partials, *nparts,
+                     per, level2);
+  *partials = level2;
+  *nparts = nb;
+  return hipGetLastError();
+}
+
 hipError_t launch_reduce_finalize(const double* partials, int64_t nparts, double* level2, DevState* st,
                                   const int32_t* ext, int mode, double* local_out, hipStream_t s) {
-  // Up to 16 partials per thread go straight to the single finalize workgroup; more are
-  // first folded by up to kLevel2 workgroups, each over a contiguous range, in fixed order.
-  if (nparts > int64_t(kThreads) * 16) {
-    const int64_t per0 = (nparts + kLevel2 - 1) / kLevel2;
-    const int64_t per = per0 < int64_t(kThreads) * 4 ? int64_t(kThreads) * 4 : per0;
-    const int64_t nb = (nparts + per - 1) / per;
-    hipLaunchKernelGGL(k_partial_reduce, dim3(static_cast<unsigned>(nb)), dim3(kThreads), 0, s, partials, nparts,
-                       per, level2);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    partials = level2;
-    nparts = nb;
-  }
+  hipError_t e = reduce_level2(&partials, &nparts, level2, s);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_flag_finalize, dim3(1), dim3(kThreads), 0, s, partials, nparts, st, ext, mode, local_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_finalize(const double* partials, int64_t nparts, double* level2, DevState* st,
+                                DevState* pre, double max_norm, hipStream_t s) {
+  hipError_t e = reduce_level2(&partials, &nparts, level2, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_step_finalize, dim3(1), dim3(kThreads), 0, s, partials, nparts, st, pre, max_norm);
   return hipGetLastError();
 }
 
