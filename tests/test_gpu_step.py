@@ -85,9 +85,9 @@ def test_step_parity_with_oracle(name):
     assert [s.step for s in rep.steps if s.overflow_gpu] == sorted(wl.faults)
 
 
-def _pair(Z, wl, dev):
+def _pair(Z, wl, dev, **extra):
     p0 = gen.make_params(wl, dev)
-    kw = dict(dynamic_loss_scale=wl.dynamic, init_scale=wl.init_scale, growth_interval=wl.growth_interval)
+    kw = dict(dynamic_loss_scale=wl.dynamic, init_scale=wl.init_scale, growth_interval=wl.growth_interval, **extra)
     return (Z.ZeroShardedAdamW([p.clone() for p in p0], **kw), Z.ZeroShardedAdamW([p.clone() for p in p0], **kw))
 
 
@@ -130,6 +130,40 @@ def test_step_bit_identical_to_the_call_sequence(name):
     assert st["skipped_total"] == len(wl.faults) and st["step_t"] == wl.steps - len(wl.faults)
     if wl.dynamic:
         assert len(set(scales)) > 1, scales  # the scale moved: backoff and growth both ran
+    one.close()
+    seq.close()
+
+
+@pytest.mark.parametrize("name,variant", [("llama_mini", "no_decay"), ("ragged_mini", "no_decay"),
+                                          ("tiny", "bf16_params"), ("llama_mini", "fp16_grads")])
+def test_step_variants_bit_identical_to_the_call_sequence(name, variant):
+    """zs_step with tensors that take no weight decay, and with gradient and parameter dtypes
+    that differ, against the four calls on the same optimizer settings."""
+    Z = _z()
+    dev = torch.device("cuda", 0)
+    wl = CASES[name]()
+    extra = {}
+    if variant == "no_decay":
+        extra["no_decay"] = "1d" if name == "llama_mini" else [i % 3 == 0 for i in range(len(wl.numels))]
+    one, seq = _pair(Z, wl, dev, **extra)
+    if variant != "no_decay":  # parameters in the other 2-byte dtype, gradients as the workload draws them
+        pdt = torch.bfloat16 if variant == "bf16_params" else torch.float16
+        gdt = gen.TORCH_DTYPE[wl.dtype] if variant == "bf16_params" else torch.float16
+        p0 = [p.to(pdt) for p in gen.make_params(wl, dev)]
+        kw = dict(dynamic_loss_scale=wl.dynamic or gdt == torch.float16,
+                  init_scale=wl.init_scale if wl.dynamic else 2.0 ** 12, growth_interval=2, grad_dtype=gdt)
+        one.close()
+        seq.close()
+        one = Z.ZeroShardedAdamW([p.clone() for p in p0], **kw)
+        seq = Z.ZeroShardedAdamW([p.clone() for p in p0], **kw)
+    for step in range(1, 5):
+        print(f"[case] {name} {variant} step {step}", flush=True)
+        scale = one.read_state()["loss_scale"]
+        grads = [g.to(one.model_grad_dtype) for g in gen.make_grads(wl, step, scale, dev)]
+        one.step(grads)
+        _sequence_step(seq, grads)
+        torch.cuda.synchronize()
+        _assert_same(one, seq, f"{name} {variant} step {step}")
     one.close()
     seq.close()
 
