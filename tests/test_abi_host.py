@@ -205,3 +205,24 @@ def test_invalid_arguments_raise_value_errors():
     with pytest.raises(Z.ZsError) as e:
         Z.zs_plan_buckets([4, 5], 0)
     assert isinstance(e.value, ValueError) and e.value.status == -1
+
+
+def test_c_consumer_is_built_and_fails_cleanly_without_gpu(tmp_path):
+    """The torch-free C++ consumer of the ABI (tests/c/abi_gpu, built with the library)
+    loads libzs.so; without arguments it prints its usage, and with no GPU its first
+    device call fails with the library's message instead of crashing."""
+    import struct
+    import subprocess
+    import torch
+    exe = os.path.join(os.path.dirname(__file__), "c", "abi_gpu")
+    assert os.path.exists(exe), "build the package first"
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "usage" in r.stderr
+    if torch.cuda.is_available():
+        return
+    inp = tmp_path / "in.bin"
+    with open(inp, "wb") as f:
+        f.write(struct.pack("<iii", 1, 0, 0) + struct.pack("<q", 4) + struct.pack("<6d", 1e-3, 0.9, 0.999, 1e-8, 0.0, 1.0))
+        f.write(struct.pack("<ddii", 1.0, 1.0, 0, 1000) + bytes(8))
+    r = subprocess.run([exe, str(inp), str(tmp_path / "out.bin")], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "zs_layout_create" in r.stderr, r.stderr

@@ -65,7 +65,23 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-pthread", "-o", tmp, *objs, *LINK_LIBS], verbose)
     os.replace(tmp, LIB)
+    build_c_consumer(verbose)
     return LIB
+
+
+# A plain C++ program that drives the library through zs.h and the HIP runtime only, with
+# no Python (tests/test_gpu_c_abi.py runs it); host code, so the host compiler builds it.
+C_CONSUMER_SRC = os.path.join(ROOT, "tests", "c", "abi_gpu.cpp")
+C_CONSUMER = os.path.join(ROOT, "tests", "c", "abi_gpu")
+
+
+def build_c_consumer(verbose: bool = False) -> str:
+    tmp = C_CONSUMER + ".tmp"
+    _run([cxx(), "-O2", "-std=c++17", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include", "-I", INCLUDE,
+          C_CONSUMER_SRC, "-o", tmp, "-L", PKG, "-lzs", "-Wl,-rpath,$ORIGIN/../../zero_sharded_mixed_buffer_amd",
+          "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"], verbose)
+    os.replace(tmp, C_CONSUMER)
+    return C_CONSUMER
 
 
 def _run(cmd, verbose):
