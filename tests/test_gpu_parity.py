@@ -626,3 +626,27 @@ def test_spaced_state_placement_gives_the_same_results():
     assert all(torch.equal(bits(x), bits(y)) for x, y in zip(a.params, b.params))
     a.close()
     b.close()
+
+
+@pytest.mark.parametrize("d", [1, 2, 4, 8])
+def test_device_memory_matches_the_pages_byte_ledger(d):
+    """Bytes per parameter on one rank against the page's table of distributed bytes per
+    BF16 parameter with an FP32 main gradient (golden byte_ledger.json): the replicated
+    2-byte parameter and 4-byte gradient buffer plus 12/d bytes of fp32 master, m and v."""
+    Z = _z()
+    with open(os.path.join(GOLDEN, "byte_ledger.json")) as f:
+        ledger = json.load(f)
+    dev = torch.device("cuda", 0)
+    n = 1 << 24
+    params = [torch.zeros(n - 1000, dtype=torch.bfloat16, device=dev), torch.zeros(1000, dtype=torch.bfloat16,
+                                                                                       device=dev)]
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    opt = Z.ZeroShardedAdamW(params, dp_world=d, dp_rank=d - 1, accum_dtype=torch.float32)
+    torch.cuda.synchronize()
+    added = torch.cuda.memory_allocated() - before
+    per_param = (added + 2 * n) / n       # the parameters were there before the optimizer
+    want = ledger["bytes_by_group_size"][str(d)]
+    print(f"[ledger] d={d}: {per_param:.4f} bytes per parameter, the page's table {want}", flush=True)
+    assert abs(per_param - want) <= 0.01 * want
+    opt.close()
