@@ -227,6 +227,10 @@ def main():
     ap.add_argument("--log-steps", type=int, default=0,
                     help="after the timed region, run this many more steps reading the state after each and "
                          "print one [zs_step k] line per step (scale, skips, norm, clip, time)")
+    ap.add_argument("--flat-views", action="store_true",
+                    help="parameters and gradients as views into contiguous buffers (backward fills the "
+                         "gradient buffer): the step checks the buffer instead of packing, and the update "
+                         "writes the parameter buffer instead of scattering")
     ap.add_argument("--graph", action="store_true",
                     help="also time the single-rank step captured once in a HIP graph and replayed, against the "
                          "same step issued call by call (launch-bound small lists)")
@@ -274,7 +278,17 @@ def main():
                              dp_rank=wl.dp_rank, align=wl.align, dynamic_loss_scale=wl.dynamic,
                              init_scale=wl.init_scale, growth_interval=wl.growth_interval, accum_dtype=accum,
                              no_decay="1d" if args.no_decay == "1d" else None,
-                             state_spacing=int(args.state_spacing_gib * (1 << 30)) or None)
+                             state_spacing=int(args.state_spacing_gib * (1 << 30)) or None,
+                             flat_views=args.flat_views)
+    views = args.flat_views
+    if views:
+        if wl.dp_world != 1 or G != 1 or args.bucket_numel or args.graph:
+            print(json.dumps({"error": "--flat-views times the single-rank step of one micro-step, call by call"}))
+            sys.exit(2)
+        with torch.no_grad():  # what backward leaves in the gradient buffer
+            for p, g in zip(params, grads):
+                p.grad.copy_(g)
+        torch.cuda.synchronize()
     S = opt.shard_numel
     N = wl.n_elems
     d, r = wl.dp_world, wl.dp_rank
@@ -305,7 +319,9 @@ def main():
 
     def pack_pass(k):
         last = k == G - 1
-        if buckets is None:
+        if views:  # the gradients are already in the buffer: check it
+            opt.check(stream=stream)
+        elif buckets is None:
             opt.pack(grads, stream, accumulate=k > 0, last=last)
         else:
             for b in buckets:
@@ -329,8 +345,12 @@ def main():
         opt.norm(rank_sumsq=exchange, stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        Z.zs_adamw_step(lay, opt.shard, opt.grad_dtype, opt.master, opt.m, opt.v, opt.hp, st,
-                        opt.param_ptrs if d == 1 else None, flat_param, opt.param_dtype, stream)
+        if views:  # new parameters straight into the parameter buffer
+            Z.zs_adamw_step(lay, opt.shard, opt.grad_dtype, opt.master, opt.m, opt.v, opt.hp, st, None,
+                            opt.flat_params, opt.param_dtype, stream)
+        else:
+            Z.zs_adamw_step(lay, opt.shard, opt.grad_dtype, opt.master, opt.m, opt.v, opt.hp, st,
+                            opt.param_ptrs if d == 1 else None, flat_param, opt.param_dtype, stream)
         if ev is not None:
             ev[3].record(stream)
         Z.zs_scaler_update(st, stream)
@@ -398,7 +418,7 @@ def main():
     step_p90 = step_ms[min(len(step_ms) - 1, int(math.ceil(0.9 * len(step_ms))) - 1)]
     gb = 4 if accum is not None else 2            # bytes per element of the flat gradient buffer
     adamw_bytes = (gb + 26) * S   # read g + master/m/v 12, write master/m/v 12 + param 2
-    first_bytes = (2 + gb) * N    # read the tensors, write the buffer
+    first_bytes = gb * N if views else (2 + gb) * N  # views: the check reads the buffer; else read tensors, write it
     acc_bytes = (2 + 2 * gb) * N  # read the tensors and the buffer, write the buffer
     check_bytes = gb * S if separate_check else 0  # the separate check re-reads the shard
     pack_bytes = first_bytes + (G - 1) * acc_bytes + check_bytes
@@ -445,7 +465,8 @@ def main():
                    "shard_elements": S, "grad_dtype": wl.dtype, "align": wl.align, "grad_accum": G,
                    "accum_dtype": ("fp32" if accum is not None else wl.dtype),
                    "bucket_numel": args.bucket_numel or None, "buckets": len(buckets) if buckets else None,
-                   "no_decay": args.no_decay, "state_spacing_gib": args.state_spacing_gib or None},
+                   "no_decay": args.no_decay, "state_spacing_gib": args.state_spacing_gib or None,
+                   "flat_views": views},
         "achieved_hbm_gbps": step_gbps,
         "hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": step_bytes,

@@ -1,0 +1,119 @@
+"""ZeroShardedAdamW(flat_views=True): parameters and their .grad are views into a contiguous
+parameter buffer and a contiguous gradient buffer laid out like the flat buffer ("Deep
+dive: Megatron", section "Distributed optimizer": backward fills a contiguous gradient
+buffer and the update rebuilds a contiguous 2-byte parameter buffer), so the step needs no
+pack and no scatter.  Checked against the oracle at the bar of the other parity tests, and
+with autograd writing the gradients through the views."""
+
+import pytest
+import torch
+
+import oracle as O
+from workloads import WORKLOADS, gen
+
+pytestmark = pytest.mark.gpu
+
+
+def _z():
+    import zero_sharded_mixed_buffer_amd as Z
+    Z.lib()
+    return Z
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama_mini", "ragged_mini", "ragged_mini_a64"])
+def test_flat_views_step_against_the_oracle(name):
+    from harness import REL_TOL, bits, rel_err
+    Z = _z()
+    wl = WORKLOADS[name]
+    dt = gen.TORCH_DTYPE[wl.dtype]
+    hp = wl.hparams
+    dev = torch.device("cuda", 0)
+    params = gen.make_params(wl, dev)
+    ref = O.OracleRank(wl.numels, 1, 0, [p.cpu() for p in params],
+                       O.OracleScaler(wl.init_scale, 1.0, wl.dynamic, wl.growth_interval), hp, wl.align)
+    opt = Z.ZeroShardedAdamW(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                             weight_decay=hp["weight_decay"], max_norm=hp["max_norm"], align=wl.align,
+                             dynamic_loss_scale=wl.dynamic, init_scale=wl.init_scale,
+                             growth_interval=wl.growth_interval, flat_views=True)
+    base = opt.flat_params.data_ptr()
+    for p, off in zip(params, ref.layout.offsets):  # every parameter now lives in the buffer
+        assert p.data_ptr() == base + 2 * off and p.grad.data_ptr() == opt.flat.data_ptr() + 2 * off
+    print(f"[case] flat views {name}: {len(wl.numels)} tensors, align {wl.align}, {wl.steps} steps", flush=True)
+    for step in range(1, wl.steps + 1):
+        grads = gen.make_grads(wl, step, ref.scaler.loss_scale, dev)
+        opt.zero_grad()
+        for p, g in zip(params, grads):
+            p.grad.add_(g)  # what backward's accumulation into the views does
+        opt.step()
+        rec = ref.step(O.shard_of(O.pack([g.cpu() for g in grads], ref.layout), ref.layout))
+        st = opt.read_state()
+        assert st["overflow"] == int(rec["overflow"]) and st["loss_scale"] == ref.scaler.loss_scale
+        assert st["step_t"] == ref.scaler.step_t and st["skipped_total"] == ref.scaler.skipped_total
+    for got, want, what in ((opt.master, ref.master, "master"), (opt.m, ref.m, "m"), (opt.v, ref.v, "v")):
+        err = rel_err(got.cpu(), want)
+        assert err <= REL_TOL, f"{what}: {err}"
+    # the parameter buffer holds the cast of the master, padding included (zero there)
+    assert torch.equal(bits(opt.flat_params.cpu()), bits(O.cast_to(opt.master.cpu(), dt)))
+    for p, off, n in zip(params, ref.layout.offsets, ref.layout.numels):
+        assert torch.equal(bits(p.detach().reshape(-1).cpu()), bits(opt.flat_params[off:off + n].cpu()))
+    opt.close()
+
+
+def test_flat_views_take_the_gradients_from_autograd():
+    """A small bf16 model (elementwise, no matrix products): backward accumulates into the
+    .grad views, so the gradient buffer holds exactly the gradients autograd computes for an
+    independent copy of the model, and the step then matches the oracle fed those
+    gradients."""
+    from harness import REL_TOL, bits, rel_err
+    Z = _z()
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    shapes = [(64, 33), (33,), (1,), (17, 5, 3)]
+    init = [torch.randn(s, generator=g, device=dev).to(torch.bfloat16) for s in shapes]
+    xs = [torch.randn(s, generator=g, device=dev).to(torch.bfloat16) for s in shapes]
+
+    def loss_of(ps):
+        return sum(((p.float() * x.float()) ** 2).sum() * (i + 1) for i, (p, x) in enumerate(zip(ps, xs)))
+
+    model = [torch.nn.Parameter(t.clone()) for t in init]
+    twin = [torch.nn.Parameter(t.clone()) for t in init]
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_norm=1.0)
+    opt = Z.ZeroShardedAdamW(model, lr=hp["lr"], weight_decay=hp["weight_decay"], max_norm=hp["max_norm"],
+                             align=8, flat_views=True)
+    numels = [t.numel() for t in init]
+    ref = O.OracleRank(numels, 1, 0, [t.cpu() for t in init], O.OracleScaler(1.0, dynamic=False), hp, 8)
+    for step in range(3):
+        opt.zero_grad()
+        loss_of(model).backward()
+        for p in twin:
+            p.grad = None
+        loss_of(twin).backward()
+        for p, q, off, n in zip(model, twin, ref.layout.offsets, numels):
+            assert p.grad.data_ptr() == opt.flat.data_ptr() + 2 * off  # still the view
+            assert torch.equal(bits(opt.flat[off:off + n].cpu()), bits(q.grad.reshape(-1).cpu()))
+        opt.step()
+        ref.step(O.shard_of(O.pack([q.grad.cpu() for q in twin], ref.layout), ref.layout))
+        with torch.no_grad():  # the twin follows the oracle's parameters
+            for q, r in zip(twin, ref.params):
+                q.copy_(r.view(q.shape))
+    for got, want in ((opt.master, ref.master), (opt.m, ref.m), (opt.v, ref.v)):
+        assert rel_err(got.cpu(), want) <= REL_TOL
+    for p, r in zip(model, ref.params):
+        assert torch.equal(bits(p.detach().reshape(-1).cpu()), bits(r.reshape(-1)))
+    opt.close()
+
+
+def test_flat_views_reject_what_they_cannot_hold():
+    Z = _z()
+    dev = torch.device("cuda", 0)
+    mixed = [torch.zeros(8, dtype=torch.bfloat16, device=dev), torch.zeros(8, dtype=torch.float16, device=dev)]
+    with pytest.raises(ValueError):
+        Z.ZeroShardedAdamW(mixed, flat_views=True)
+    with pytest.raises(ValueError):
+        Z.ZeroShardedAdamW([torch.zeros(8, dtype=torch.bfloat16, device=dev)], flat_views=True,
+                           accum_dtype=torch.float32)
+    opt = Z.ZeroShardedAdamW([torch.zeros(8, dtype=torch.bfloat16, device=dev)])
+    with pytest.raises(ValueError):
+        opt.step()  # no gradients and no views
+    opt.close()

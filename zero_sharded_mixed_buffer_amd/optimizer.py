@@ -46,12 +46,18 @@ class ZeroShardedAdamW:
     no_decay: one flag per tensor (True: no weight decay), or "1d" for every tensor with
         at most one dimension.
     state_spacing: carve master / m / v from one allocation this many bytes apart.
+    flat_views: the parameters and their .grad become views into two flat buffers laid out
+        like the gradient buffer (a contiguous parameter buffer and a contiguous gradient
+        buffer that backward fills in place).  step() with no gradient list then checks the
+        buffer and writes the new parameters straight into the parameter buffer: no pack
+        and no scatter.
     """
 
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, max_norm=1.0,
                  dp_world=1, dp_rank=0, align=1, dynamic_loss_scale=None, init_scale=None, scale_floor=1.0,
                  growth_interval=1000, grad_dtype=None, accum_dtype=None, offload=False,
-                 offload_chunk=1 << 24, offload_threads=0, no_decay=None, state_spacing=None):
+                 offload_chunk=1 << 24, offload_threads=0, no_decay=None, state_spacing=None,
+                 flat_views=False):
         params = list(params)
         if not params:
             raise ValueError("empty parameter list")
@@ -86,6 +92,21 @@ class ZeroShardedAdamW:
         dev = self.device
         self.offload = bool(offload)
         self.flat = torch.zeros(self.flat_numel, dtype=self.grad_dtype, device=dev)
+        self.flat_views = bool(flat_views)
+        self.flat_params = None
+        if self.flat_views:
+            if self.offload or self.grad_dtype != self.param_dtype:
+                raise ValueError("flat_views needs the device update and gradients in the parameter dtype")
+            if any(p.dtype != self.param_dtype or p.device != dev for p in params):
+                raise ValueError("flat_views needs every parameter in one dtype on one device")
+            offsets = A.zs_plan(self.numels, dp_world, dp_rank, align)[0]
+            self.flat_params = torch.zeros(self.flat_numel, dtype=self.param_dtype, device=dev)
+            with torch.no_grad():
+                for p, off, n in zip(params, offsets, self.numels):
+                    view = self.flat_params[off:off + n].view(p.shape)
+                    view.copy_(p)
+                    p.data = view
+                    p.grad = self.flat[off:off + n].view(p.shape)
         self.param_ptrs = pointer_table(params, dev)
         self.local_sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
         self._grad_key = None
@@ -192,12 +213,29 @@ class ZeroShardedAdamW:
                             stream=stream)
         A.zs_scaler_update(self.state, stream=stream)
 
-    def step(self, grads, stream=None):
+    def zero_grad(self):
+        """Zero the gradient buffer (with flat_views, every parameter's .grad), on the current
+        stream."""
+        self.flat.zero_()
+
+    def step(self, grads=None, stream=None):
         """Whole single-rank step (dp_world == 1).  `grads` is one gradient list, or a list of
-        micro-step gradient lists accumulated into the flat buffer before the step."""
+        micro-step gradient lists accumulated into the flat buffer before the step.  With
+        flat_views and no `grads`, the gradients are already in the buffer (backward wrote
+        them through the .grad views): the step checks the buffer, takes the norm, and the
+        update writes the new parameters into the flat parameter buffer."""
         if self.dp_world != 1:
             raise ValueError("step() is the single-rank sequence; call pack/check/norm/update with the "
                              "other ranks' flag and partial sums for dp_world > 1")
+        if grads is None:
+            if not self.flat_views:
+                raise ValueError("step() needs the gradients unless the optimizer was built with flat_views")
+            self.check(stream=stream)
+            self.norm(stream=stream)
+            A.zs_adamw_step(self.layout, self.shard, self.grad_dtype, self.master, self.m, self.v, self.hp,
+                            self.state, None, self.flat_params, self.param_dtype, stream=stream)
+            A.zs_scaler_update(self.state, stream=stream)
+            return
         micro = grads if (grads and isinstance(grads[0], (list, tuple))) else [grads]
         if len(micro) == 1 and not self.offload and self.grad_dtype == self.model_grad_dtype:
             # one call enqueueing the kernels of the sequence below (same results, fewer calls)
