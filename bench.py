@@ -282,8 +282,8 @@ def main():
                              flat_views=args.flat_views)
     views = args.flat_views
     if views:
-        if wl.dp_world != 1 or G != 1 or args.bucket_numel or args.graph:
-            print(json.dumps({"error": "--flat-views times the single-rank step of one micro-step, call by call"}))
+        if G != 1 or args.bucket_numel or args.graph:
+            print(json.dumps({"error": "--flat-views times the step of one micro-step, call by call"}))
             sys.exit(2)
         with torch.no_grad():  # what backward leaves in the gradient buffer
             for p, g in zip(params, grads):
@@ -303,9 +303,10 @@ def main():
     # partial sums come from their shards of the same buffer, computed once beforehand
     # (on a real group the other GPUs compute them).
     exchange = torch.zeros(d, dtype=torch.float64, device=dev) if d > 1 else None
-    flat_param = torch.empty(S, dtype=opt.param_dtype, device=dev) if d > 1 else None
+    flat_param = torch.empty(S, dtype=opt.param_dtype, device=dev) if d > 1 and not views else None
     if d > 1:
-        opt.pack(grads, stream)
+        if not views:
+            opt.pack(grads, stream)
         for q in range(d):
             if q == r:
                 continue
@@ -315,13 +316,14 @@ def main():
             torch.cuda.synchronize()
             Z.zs_state_destroy(sq)
             Z.zs_layout_destroy(lq)
-    separate_check = buckets is not None or d > 1
+    separate_check = (buckets is not None or d > 1) and not views
 
     def pack_pass(k):
         last = k == G - 1
-        if views:  # the gradients are already in the buffer: check it
-            opt.check(stream=stream)
-        elif buckets is None:
+        if views:  # the gradients are already in the buffer (the shard: after the reduce-scatter)
+            opt.check(local_sumsq_out=exchange[r:r + 1] if d > 1 else None, stream=stream)
+            return
+        if buckets is None:
             opt.pack(grads, stream, accumulate=k > 0, last=last)
         else:
             for b in buckets:
@@ -345,9 +347,9 @@ def main():
         opt.norm(rank_sumsq=exchange, stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        if views:  # new parameters straight into the parameter buffer
+        if views:  # new parameters straight into the rank's slice of the parameter buffer
             Z.zs_adamw_step(lay, opt.shard, opt.grad_dtype, opt.master, opt.m, opt.v, opt.hp, st, None,
-                            opt.flat_params, opt.param_dtype, stream)
+                            opt.param_shard, opt.param_dtype, stream)
         else:
             Z.zs_adamw_step(lay, opt.shard, opt.grad_dtype, opt.master, opt.m, opt.v, opt.hp, st,
                             opt.param_ptrs if d == 1 else None, flat_param, opt.param_dtype, stream)
@@ -418,7 +420,7 @@ def main():
     step_p90 = step_ms[min(len(step_ms) - 1, int(math.ceil(0.9 * len(step_ms))) - 1)]
     gb = 4 if accum is not None else 2            # bytes per element of the flat gradient buffer
     adamw_bytes = (gb + 26) * S   # read g + master/m/v 12, write master/m/v 12 + param 2
-    first_bytes = gb * N if views else (2 + gb) * N  # views: the check reads the buffer; else read tensors, write it
+    first_bytes = gb * S if views else (2 + gb) * N  # views: the check reads the shard; else read tensors, write it
     acc_bytes = (2 + 2 * gb) * N  # read the tensors and the buffer, write the buffer
     check_bytes = gb * S if separate_check else 0  # the separate check re-reads the shard
     pack_bytes = first_bytes + (G - 1) * acc_bytes + check_bytes
@@ -427,7 +429,7 @@ def main():
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     traffic = measured_traffic(wl.name) if G == 1 else None
     unpack = None
-    if d > 1:
+    if d > 1 and not views:  # with views the all-gather fills the parameter buffer: nothing to unpack
         # After the all-gather every rank scatters the whole model-dtype buffer into its
         # parameters: timed on its own, outside the step (4 B per element of the buffer).
         gathered = torch.empty(opt.flat_numel, dtype=opt.param_dtype, device=dev)

@@ -5,6 +5,8 @@ buffer and the update rebuilds a contiguous 2-byte parameter buffer), so the ste
 pack and no scatter.  Checked against the oracle at the bar of the other parity tests, and
 with autograd writing the gradients through the views."""
 
+import math
+
 import pytest
 import torch
 
@@ -117,3 +119,62 @@ def test_flat_views_reject_what_they_cannot_hold():
     with pytest.raises(ValueError):
         opt.step()  # no gradients and no views
     opt.close()
+
+
+@pytest.mark.parametrize("name", ["qwen_mini_dp2", "moe_mini_dp4"])
+def test_flat_views_every_virtual_rank_against_the_oracle(name):
+    """Several ranks in one process, each with its own copy of the model in flat views.
+    Every rank's gradient buffer holds the same gradients, so its shard stands in for the
+    reduce-scatter output; the ranks exchange their local sums of squares, each update
+    writes its slice of its parameter buffer, and copying every slice into the other ranks'
+    buffers stands in for the all-gather.  Every rank's state shard and whole parameter
+    buffer match the oracle's ranks."""
+    from harness import REL_TOL, bits, rel_err
+    Z = _z()
+    wl = WORKLOADS[name]
+    d = wl.dp_world
+    dt = gen.TORCH_DTYPE[wl.dtype]
+    hp = wl.hparams
+    dev = torch.device("cuda", 0)
+    p0 = gen.make_params(wl, dev)
+    kw = dict(lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"], weight_decay=hp["weight_decay"],
+              max_norm=hp["max_norm"], dp_world=d, align=wl.align, dynamic_loss_scale=wl.dynamic,
+              init_scale=wl.init_scale, growth_interval=wl.growth_interval, flat_views=True)
+    models = [[p.clone() for p in p0] for _ in range(d)]
+    opts = [Z.ZeroShardedAdamW(models[r], dp_rank=r, **kw) for r in range(d)]
+    refs = [O.OracleRank(wl.numels, d, r, [p.cpu() for p in p0],
+                         O.OracleScaler(wl.init_scale, 1.0, wl.dynamic, wl.growth_interval), hp, wl.align)
+            for r in range(d)]
+    S = opts[0].shard_numel
+    exchange = torch.zeros(d, dtype=torch.float64, device=dev)
+    print(f"[case] flat views {name}: {d} ranks, {wl.steps} steps", flush=True)
+    for step in range(1, wl.steps + 1):
+        grads = gen.make_grads(wl, step, refs[0].scaler.loss_scale, dev)
+        for r in range(d):
+            opts[r].zero_grad()
+            for p, g in zip(models[r], grads):
+                p.grad.add_(g)
+            opts[r].check(local_sumsq_out=exchange[r:r + 1])
+        for r in range(d):
+            opts[r].norm(rank_sumsq=exchange)
+            opts[r].update()
+        for q in range(d):  # the all-gather's stand-in
+            for r in range(d):
+                if q != r:
+                    opts[q].flat_params[r * S:(r + 1) * S].copy_(opts[r].param_shard)
+        # the oracle ranks: every rank's flag and partial sum feed every rank's step
+        flat = O.pack([g.cpu() for g in grads], refs[0].layout)
+        shards = [O.shard_of(flat, refs[r].layout) for r in range(d)]
+        bad = [O.nonfinite_any(x) for x in shards]
+        sums = [math.inf if b else O.sumsq_unscaled(x, refs[0].scaler.loss_scale) for b, x in zip(bad, shards)]
+        for r in range(d):  # other_sumsq is indexed by rank; the rank's own entry is not read
+            rec = refs[r].step(shards[r], ext_overflow=any(bad[q] for q in range(d) if q != r), other_sumsq=sums)
+            st = opts[r].read_state()
+            assert st["overflow"] == int(rec["overflow"]) and st["loss_scale"] == refs[r].scaler.loss_scale
+    for r in range(d):
+        for got, want in ((opts[r].master, refs[r].master), (opts[r].m, refs[r].m), (opts[r].v, refs[r].v)):
+            assert rel_err(got.cpu(), want) <= REL_TOL
+        full = torch.cat([O.cast_to(opts[q].master.cpu(), dt) for q in range(d)])
+        assert torch.equal(bits(opts[r].flat_params.cpu()), bits(full))
+    for o in opts:
+        o.close()

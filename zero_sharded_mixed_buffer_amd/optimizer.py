@@ -151,6 +151,14 @@ class ZeroShardedAdamW:
         """This rank's partition of the flat gradient buffer (a view)."""
         return self.flat[self.shard_begin:self.shard_begin + self.shard_numel]
 
+    @property
+    def param_shard(self):
+        """With flat_views: this rank's partition of the parameter buffer (a view), which its
+        update writes and the all-gather of the other ranks' partitions completes."""
+        if self.flat_params is None:
+            raise ValueError("the optimizer was built without flat_views")
+        return self.flat_params[self.shard_begin:self.shard_begin + self.shard_numel]
+
     def _grad_table(self, grads):
         key = tuple(g.data_ptr() for g in grads)
         if key != self._grad_key:
@@ -207,6 +215,10 @@ class ZeroShardedAdamW:
             if scatter:
                 A.zs_unpack(self.layout, self.flat_param, self.param_dtype, False, self.param_ptrs, self.param_dtype,
                             self.state, stream=stream)
+        elif self.flat_views and scatter and flat_param_out is None:
+            # the parameters are views of the parameter buffer: write the shard's slice of it
+            A.zs_adamw_step(self.layout, self.shard, self.grad_dtype, self.master, self.m, self.v, self.hp,
+                            self.state, None, self.param_shard, self.param_dtype, stream=stream)
         else:
             A.zs_adamw_step(self.layout, self.shard, self.grad_dtype, self.master, self.m, self.v, self.hp,
                             self.state, self.param_ptrs if scatter else None, flat_param_out, self.param_dtype,
@@ -232,9 +244,7 @@ class ZeroShardedAdamW:
                 raise ValueError("step() needs the gradients unless the optimizer was built with flat_views")
             self.check(stream=stream)
             self.norm(stream=stream)
-            A.zs_adamw_step(self.layout, self.shard, self.grad_dtype, self.master, self.m, self.v, self.hp,
-                            self.state, None, self.flat_params, self.param_dtype, stream=stream)
-            A.zs_scaler_update(self.state, stream=stream)
+            self.update(stream=stream)
             return
         micro = grads if (grads and isinstance(grads[0], (list, tuple))) else [grads]
         if len(micro) == 1 and not self.offload and self.grad_dtype == self.model_grad_dtype:
