@@ -22,8 +22,12 @@ def _z():
     return Z
 
 
-@pytest.mark.parametrize("name", ["tiny", "llama_mini", "ragged_mini", "ragged_mini_a64"])
-def test_flat_views_step_against_the_oracle(name):
+@pytest.mark.parametrize("name,offload", [("tiny", False), ("llama_mini", False), ("ragged_mini", False),
+                                          ("ragged_mini_a64", False), ("ragged_mini_a64", True),
+                                          ("tiny", True)])
+def test_flat_views_step_against_the_oracle(name, offload):
+    """offload=True: the host update writes the new parameters straight into the parameter
+    buffer (no unpack)."""
     from harness import REL_TOL, bits, rel_err
     Z = _z()
     wl = WORKLOADS[name]
@@ -36,7 +40,8 @@ def test_flat_views_step_against_the_oracle(name):
     opt = Z.ZeroShardedAdamW(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
                              weight_decay=hp["weight_decay"], max_norm=hp["max_norm"], align=wl.align,
                              dynamic_loss_scale=wl.dynamic, init_scale=wl.init_scale,
-                             growth_interval=wl.growth_interval, flat_views=True)
+                             growth_interval=wl.growth_interval, flat_views=True, offload=offload,
+                             offload_chunk=50_001, offload_threads=3)
     base = opt.flat_params.data_ptr()
     for p, off in zip(params, ref.layout.offsets):  # every parameter now lives in the buffer
         assert p.data_ptr() == base + 2 * off and p.grad.data_ptr() == opt.flat.data_ptr() + 2 * off
@@ -54,6 +59,8 @@ def test_flat_views_step_against_the_oracle(name):
     for got, want, what in ((opt.master, ref.master, "master"), (opt.m, ref.m, "m"), (opt.v, ref.v, "v")):
         err = rel_err(got.cpu(), want)
         assert err <= REL_TOL, f"{what}: {err}"
+    if offload:
+        assert opt.flat_param.data_ptr() == opt.flat_params.data_ptr()  # no separate output buffer
     # the parameter buffer holds the cast of the master, padding included (zero there)
     assert torch.equal(bits(opt.flat_params.cpu()), bits(O.cast_to(opt.master.cpu(), dt)))
     for p, off, n in zip(params, ref.layout.offsets, ref.layout.numels):

@@ -95,8 +95,8 @@ class ZeroShardedAdamW:
         self.flat_views = bool(flat_views)
         self.flat_params = None
         if self.flat_views:
-            if self.offload or self.grad_dtype != self.param_dtype:
-                raise ValueError("flat_views needs the device update and gradients in the parameter dtype")
+            if self.grad_dtype != self.param_dtype:
+                raise ValueError("flat_views needs the gradient buffer in the parameter dtype")
             if any(p.dtype != self.param_dtype or p.device != dev for p in params):
                 raise ValueError("flat_views needs every parameter in one dtype on one device")
             offsets = A.zs_plan(self.numels, dp_world, dp_rank, align)[0]
@@ -140,7 +140,9 @@ class ZeroShardedAdamW:
             c = min(self.offload_chunk, max(S, 1))
             self.grad_stage = torch.empty(2 * c, dtype=self.grad_dtype, pin_memory=True)
             self.param_stage = torch.empty(2 * c, dtype=self.param_dtype, pin_memory=True)
-            self.flat_param = torch.empty(S, dtype=self.param_dtype, device=dev)
+            # with flat_views the host's new parameters go straight into the parameter buffer
+            self.flat_param = self.param_shard if self.flat_views else torch.empty(S, dtype=self.param_dtype,
+                                                                                   device=dev)
             seed = torch.empty(S, dtype=torch.float32, device=dev)
             A.zs_pack(self.layout, self.param_ptrs, self.param_dtype, seed, torch.float32, whole_flat=False)
             self.master.copy_(seed)  # synchronous: complete on return
@@ -203,6 +205,9 @@ class ZeroShardedAdamW:
         A.zs_grad_norm(self.layout, None, self.grad_dtype, self.state, self.hp, rank_sumsq, None, stream=stream)
 
     def update(self, scatter=True, flat_param_out=None, stream=None):
+        """AdamW on the shard, then the new parameters: scattered into the parameter tensors
+        (scatter), written to flat_param_out, or with flat_views written into the rank's slice
+        of the parameter buffer; then the scaler commit."""
         if self.offload:
             # The host updates the state chunk by chunk; the new parameters of the shard land
             # in self.flat_param (the all-gather input with several ranks) and are scattered.
@@ -212,7 +217,7 @@ class ZeroShardedAdamW:
                                     self.param_dtype, self.offload_threads, stream=stream)
             if flat_param_out is not None:
                 flat_param_out.copy_(self.flat_param)
-            if scatter:
+            if scatter and not self.flat_views:  # views: the parameters are the buffer just written
                 A.zs_unpack(self.layout, self.flat_param, self.param_dtype, False, self.param_ptrs, self.param_dtype,
                             self.state, stream=stream)
         elif self.flat_views and scatter and flat_param_out is None:
