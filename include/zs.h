@@ -316,6 +316,27 @@ zs_status zs_step(const zs_layout* layout, const void* grad_ptrs, zs_dtype grad_
                   zs_state* state, const zs_adamw_hparams* hp, float* master, float* m, float* v,
                   const void* param_ptrs, zs_dtype param_dtype, void* stream);
 
+/* The single-rank step over contiguous buffers, in one call: the gradients are already in
+ * the flat buffer (backward wrote them there) and the parameters are the flat parameter
+ * buffer ("Deep dive: Megatron", section "Distributed optimizer": backward fills a
+ * contiguous gradient buffer; the update rebuilds the contiguous 2-byte parameter buffer).
+ * The same results, bit for bit, as zs_unscale_check (no other ranks) -> zs_grad_norm ->
+ * zs_adamw_step (flat_param_out, no pointer table) -> zs_scaler_update, in three launches:
+ * the check's partial sums, one finalize workgroup (flag, norm, a copy of the pre-commit
+ * state for the update, scaler commit), and the update.  No pack and no scatter: 30 bytes
+ * per element instead of zs_step's 32.
+ *   layout: dp_world must be 1.
+ *   flat: device buffer of flat_numel elements of grad_dtype (bf16 or fp16), 16-byte
+ *         aligned, holding the gradients in the layout's order (zero in the padding).
+ *   master, m, v: device fp32 arrays of shard_numel elements, 16-byte aligned.
+ *   flat_param_out: device buffer of flat_numel elements of param_dtype (bf16 or fp16),
+ *         16-byte aligned; receives the cast of the new master unless the step overflows.
+ * Errors: ZS_EINVAL on dp_world != 1, NULL pointers, dtypes, misalignment, a state of
+ * another layout or invalid hyper-parameters; nothing is enqueued then. */
+zs_status zs_step_flat(const zs_layout* layout, const void* flat, zs_dtype grad_dtype, zs_state* state,
+                       const zs_adamw_hparams* hp, float* master, float* m, float* v, void* flat_param_out,
+                       zs_dtype param_dtype, void* stream);
+
 /* Offloaded optimizer step: the fp32 master, m and v live in host memory and the host CPU
  * runs the update, which is bound by memory bandwidth, not by arithmetic ("3.7
  * Megatron-LM, DeepSpeed & Parallelism in Practice", section "ZeRO-Offload and

@@ -129,6 +129,9 @@ def test_device_calls_fail_cleanly_without_gpu():
     with pytest.raises(Z.ZsError) as e:
         Z.zs_step(None, 0, 0, 0, None, Z.hparams(), 0, 0, 0, 0, stream=0)
     assert e.value.status == -1
+    with pytest.raises(Z.ZsError) as e:
+        Z.zs_step_flat(None, 0, 0, None, Z.hparams(), 0, 0, 0, 0, stream=0)
+    assert e.value.status == -1
 
 
 @pytest.mark.parametrize("seed", range(8))

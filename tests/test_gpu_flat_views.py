@@ -185,3 +185,41 @@ def test_flat_views_every_virtual_rank_against_the_oracle(name):
         assert torch.equal(bits(opts[r].flat_params.cpu()), bits(full))
     for o in opts:
         o.close()
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged_mini_a64", "over_one_level"])
+def test_step_flat_bit_identical_to_the_call_sequence(name):
+    """step() with flat views is the single call zs_step_flat; it equals the four calls
+    (check, norm, update into the parameter buffer, scaler commit) bit for bit, through a
+    skipped step and scale growth, on both sides of the two-level fold of the partial sums."""
+    import dataclasses
+    from harness import bits
+    from test_gpu_step import CASES
+    Z = _z()
+    dev = torch.device("cuda", 0)
+    wl = dataclasses.replace(CASES[name](), growth_interval=2)
+    p0 = gen.make_params(wl, dev)
+    kw = dict(align=wl.align, dynamic_loss_scale=wl.dynamic, init_scale=wl.init_scale,
+              growth_interval=wl.growth_interval, flat_views=True)
+    ma, mb = [p.clone() for p in p0], [p.clone() for p in p0]
+    one, seq = Z.ZeroShardedAdamW(ma, **kw), Z.ZeroShardedAdamW(mb, **kw)
+    for step in range(1, wl.steps + 1):
+        print(f"[case] zs_step_flat {name} step {step}", flush=True)
+        grads = gen.make_grads(wl, step, one.read_state()["loss_scale"], dev)
+        for opt, model in ((one, ma), (seq, mb)):
+            opt.zero_grad()
+            for p, g in zip(model, grads):
+                p.grad.add_(g)
+        one.step()
+        seq.check()
+        seq.norm()
+        seq.update()
+        torch.cuda.synchronize()
+        for x, y in ((one.master, seq.master), (one.m, seq.m), (one.v, seq.v), (one.flat_params, seq.flat_params)):
+            assert torch.equal(bits(x), bits(y)), f"step {step}"
+        sa, sb = one.read_state(), seq.read_state()
+        for k in sa:
+            assert sa[k] == sb[k] or (isinstance(sa[k], float) and math.isnan(sa[k]) and math.isnan(sb[k])), k
+    assert one.read_state()["skipped_total"] == len(wl.faults)
+    one.close()
+    seq.close()

@@ -36,6 +36,7 @@ from ._abi import (  # noqa: F401
     zs_plan_segments,
     zs_scaler_update,
     zs_step,
+    zs_step_flat,
     zs_state_create,
     zs_state_destroy,
     zs_state_read,

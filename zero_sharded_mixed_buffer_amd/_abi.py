@@ -75,6 +75,8 @@ _SIGS = {
     "zs_scaler_update": [c_void_p, c_void_p],
     "zs_step": [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, POINTER(AdamwHParams), c_void_p, c_void_p,
                 c_void_p, c_void_p, c_int32, c_void_p],
+    "zs_step_flat": [c_void_p, c_void_p, c_int32, c_void_p, POINTER(AdamwHParams), c_void_p, c_void_p, c_void_p,
+                     c_void_p, c_int32, c_void_p],
     "zs_host_adamw_step": [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_int64, POINTER(AdamwHParams),
                            POINTER(StateHost), c_void_p, c_int32, c_int32],
     "zs_offload_adamw_step": [c_void_p, c_void_p, c_int32, c_void_p, POINTER(AdamwHParams), c_void_p, c_void_p,
@@ -300,6 +302,15 @@ def zs_step(layout, grad_ptrs, grad_dtype, flat, state, hp: AdamwHParams, master
     _check(lib().zs_step(layout, _ptr(grad_ptrs), dtype_code(grad_dtype), _ptr(flat), state, byref(hp),
                          _ptr(master), _ptr(m), _ptr(v), _ptr(param_ptrs), dtype_code(param_dtype),
                          _stream(stream)), "zs_step")
+
+
+def zs_step_flat(layout, flat, grad_dtype, state, hp: AdamwHParams, master, m, v, flat_param_out,
+                 param_dtype=ZS_BF16, stream=None):
+    """The single-rank step over contiguous gradient and parameter buffers: check, norm,
+    AdamW writing the parameter buffer, scaler commit."""
+    _check(lib().zs_step_flat(layout, _ptr(flat), dtype_code(grad_dtype), state, byref(hp), _ptr(master), _ptr(m),
+                              _ptr(v), _ptr(flat_param_out), dtype_code(param_dtype), _stream(stream)),
+           "zs_step_flat")
 
 
 def zs_last_error():

@@ -637,6 +637,41 @@ extern "C" zs_status zs_step(const zs_layout* l, const void* grad_ptrs, zs_dtype
   return ok();
 }
 
+extern "C" zs_status zs_step_flat(const zs_layout* l, const void* flat, zs_dtype grad_dtype, zs_state* state,
+                                  const zs_adamw_hparams* hp, float* master, float* m, float* v,
+                                  void* flat_param_out, zs_dtype param_dtype, void* stream) {
+  const TraceRange trace("zs_step_flat");
+  zs_status st = check_layout(l);
+  if (st != ZS_OK) return st;
+  st = check_state(l, state);
+  if (st != ZS_OK) return st;
+  st = check_hparams(hp);
+  if (st != ZS_OK) return st;
+  if (l->plan.dp_world != 1) return fail(ZS_EINVAL, "zs_step_flat is the single-rank step: dp_world must be 1");
+  if (flat == nullptr || flat_param_out == nullptr || master == nullptr || m == nullptr || v == nullptr)
+    return fail(ZS_EINVAL, "flat, flat_param_out, master, m and v must not be NULL");
+  if (!is_half_dtype(grad_dtype) || !is_half_dtype(param_dtype))
+    return fail(ZS_EINVAL, "grad_dtype and param_dtype must be bf16 or fp16");
+  if (!aligned16(flat) || !aligned16(flat_param_out))
+    return fail(ZS_EINVAL, "flat and flat_param_out must be 16-byte aligned");
+  if (!aligned16(master) || !aligned16(m) || !aligned16(v)) return fail(ZS_EINVAL, "master, m, v must be 16-byte aligned");
+  hipStream_t s = as_stream(stream);
+  // zs_unscale_check + zs_grad_norm + zs_adamw_step (flat output) + zs_scaler_update in three
+  // launches: the check's partial sums, the one-workgroup finalize (which keeps the
+  // pre-commit state for the update), and the update.
+  DevState* pre = state->dev + 1;
+  const int64_t n = l->plan.shard_numel;
+  hipError_t e = zs::launch_check(flat, n, grad_dtype, state->partials, s);
+  if (e != hipSuccess) return hip_fail(e, "launching check");
+  e = zs::launch_step_finalize(state->partials, zs::reduction_blocks(n), state->partials + state->nparts, state->dev,
+                               pre, hp->max_norm, s);
+  if (e != hipSuccess) return hip_fail(e, "launching the step finalize");
+  const zs::AdamwArgs a{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
+  e = zs::launch_adamw(l->map_shard, flat, grad_dtype, master, m, v, a, pre, nullptr, flat_param_out, param_dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "launching adamw");
+  return ok();
+}
+
 extern "C" const char* zs_last_error(void) { return g_last_error.c_str(); }
 
 // ---------------------------------------------------------------------------- offloaded step

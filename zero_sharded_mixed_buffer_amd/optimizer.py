@@ -247,9 +247,13 @@ class ZeroShardedAdamW:
         if grads is None:
             if not self.flat_views:
                 raise ValueError("step() needs the gradients unless the optimizer was built with flat_views")
-            self.check(stream=stream)
-            self.norm(stream=stream)
-            self.update(stream=stream)
+            if self.offload:
+                self.check(stream=stream)
+                self.norm(stream=stream)
+                self.update(stream=stream)
+            else:  # one call: check, norm, update into the parameter buffer, scaler commit
+                A.zs_step_flat(self.layout, self.flat, self.grad_dtype, self.state, self.hp, self.master, self.m,
+                               self.v, self.flat_params, self.param_dtype, stream=stream)
             return
         micro = grads if (grads and isinstance(grads[0], (list, tuple))) else [grads]
         if len(micro) == 1 and not self.offload and self.grad_dtype == self.model_grad_dtype:
