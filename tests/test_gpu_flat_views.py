@@ -126,6 +126,17 @@ def test_flat_views_reject_what_they_cannot_hold():
     with pytest.raises(ValueError):
         opt.step()  # no gradients and no views
     opt.close()
+    # a .grad set to None (as a model-level zero_grad does) is refused, and zero_grad() mends it
+    ps = [torch.nn.Parameter(torch.ones(8, dtype=torch.bfloat16, device=dev)) for _ in range(2)]
+    opt = Z.ZeroShardedAdamW(ps, flat_views=True)
+    ps[1].grad = None
+    with pytest.raises(ValueError, match="zero_grad"):
+        opt.step()
+    opt.zero_grad()
+    assert ps[1].grad.data_ptr() == opt.flat.data_ptr() + 2 * 8
+    opt.step()
+    assert opt.read_state()["step_t"] == 1
+    opt.close()
 
 
 @pytest.mark.parametrize("name", ["qwen_mini_dp2", "moe_mini_dp4"])

@@ -16,6 +16,8 @@ master / m / v live in host memory and update() runs the offloaded step
 
 from __future__ import annotations
 
+import operator
+
 import torch
 
 from . import _abi as A
@@ -101,12 +103,14 @@ class ZeroShardedAdamW:
                 raise ValueError("flat_views needs every parameter in one dtype on one device")
             offsets = A.zs_plan(self.numels, dp_world, dp_rank, align)[0]
             self.flat_params = torch.zeros(self.flat_numel, dtype=self.param_dtype, device=dev)
+            self._grad_views = []
             with torch.no_grad():
                 for p, off, n in zip(params, offsets, self.numels):
                     view = self.flat_params[off:off + n].view(p.shape)
                     view.copy_(p)
                     p.data = view
                     p.grad = self.flat[off:off + n].view(p.shape)
+                    self._grad_views.append(p.grad)
         self.param_ptrs = pointer_table(params, dev)
         self.local_sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
         self._grad_key = None
@@ -231,9 +235,21 @@ class ZeroShardedAdamW:
         A.zs_scaler_update(self.state, stream=stream)
 
     def zero_grad(self):
-        """Zero the gradient buffer (with flat_views, every parameter's .grad), on the current
-        stream."""
+        """Zero the gradient buffer (with flat_views, every parameter's .grad, which is made a
+        view of the buffer again if something replaced it), on the current stream."""
         self.flat.zero_()
+        if self.flat_views:
+            for p, g in zip(self.params, self._grad_views):
+                if p.grad is not g:
+                    p.grad = g
+
+    def _check_views(self):
+        """A parameter whose .grad is no longer its view of the buffer (set to None or
+        replaced, e.g. by a model-level zero_grad) would leave stale gradients in the buffer:
+        refuse to step."""
+        if not all(map(operator.is_, (p.grad for p in self.params), self._grad_views)):
+            raise ValueError("a parameter's .grad is no longer a view of the gradient buffer; zero the gradients "
+                             "with the optimizer's zero_grad(), which keeps the views")
 
     def step(self, grads=None, stream=None):
         """Whole single-rank step (dp_world == 1).  `grads` is one gradient list, or a list of
@@ -247,6 +263,7 @@ class ZeroShardedAdamW:
         if grads is None:
             if not self.flat_views:
                 raise ValueError("step() needs the gradients unless the optimizer was built with flat_views")
+            self._check_views()
             if self.offload:
                 self.check(stream=stream)
                 self.norm(stream=stream)
