@@ -1,7 +1,10 @@
 // A consumer of the C ABI with no Python and no torch: HIP runtime calls for device memory
 // and a stream, zs.h for everything else.  It reads a problem from a binary file, runs the
-// single-rank step (zs_step) on the GPU for every step's gradients, and writes the state,
-// master, m, v and the parameters to a binary file that the test compares with the oracle.
+// single-rank step on the GPU for every step's gradients, and writes the state, master, m,
+// v and the parameters to a binary file that the test compares with the oracle.  Mode
+// "tensors": one allocation per parameter and gradient tensor, zs_step (pack + scatter).
+// Mode "flat": one contiguous gradient buffer and one contiguous parameter buffer at the
+// offsets zs_plan gives, zs_step_flat.
 //
 // Input (little-endian): int32 n_tensors, int32 dtype (ZS_BF16 / ZS_FP16), int32 steps,
 //   int64 numels[n_tensors], double hparams[6] (lr, beta1, beta2, eps, weight_decay,
@@ -16,6 +19,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <string>
 #include <vector>
 
 #include "zs.h"
@@ -43,7 +47,10 @@ void read_into(std::FILE* f, T* dst, size_t count) {
 }  // namespace
 
 int main(int argc, char** argv) {
-  if (argc != 3) die("usage", "abi_gpu <input> <output>");
+  if (argc != 4) die("usage", "abi_gpu <input> <output> tensors|flat");
+  const std::string mode = argv[3];
+  if (mode != "tensors" && mode != "flat") die("usage", "the mode is tensors or flat");
+  const bool flat_mode = mode == "flat";
   std::FILE* in = std::fopen(argv[1], "rb");
   if (in == nullptr) die("opening the input", argv[1]);
   int32_t n = 0, dtype = 0, steps = 0;
@@ -72,23 +79,37 @@ int main(int argc, char** argv) {
   zs_state* state = nullptr;
   zs_ok(zs_state_create(layout, &init, &state), "zs_state_create");
 
-  // One device allocation per tensor for parameters and gradients, as a framework has them.
+  // Mode tensors: one device allocation per tensor, as a framework has them.  Mode flat:
+  // every tensor is a slice of one parameter buffer and one gradient buffer.
+  std::vector<int64_t> offsets(n, 0);
+  zs_ok(zs_plan(numels.data(), n, 1, 0, 1, offsets.data(), nullptr, nullptr, nullptr), "zs_plan");
+  void *flat_params = nullptr, *flat = nullptr;
+  hip_ok(hipMalloc(&flat, static_cast<size_t>(flat_numel) * 2 + 16), "hipMalloc flat");
+  hip_ok(hipMemset(flat, 0, static_cast<size_t>(flat_numel) * 2), "zero flat");
+  if (flat_mode) {
+    hip_ok(hipMalloc(&flat_params, static_cast<size_t>(flat_numel) * 2 + 16), "hipMalloc flat params");
+    hip_ok(hipMemset(flat_params, 0, static_cast<size_t>(flat_numel) * 2), "zero flat params");
+  }
   std::vector<void*> params(n, nullptr), grads(n, nullptr);
   std::vector<uint64_t> pptr(n, 0), gptr(n, 0);
   for (int32_t i = 0; i < n; ++i) {
     const size_t bytes = static_cast<size_t>(numels[i] > 0 ? numels[i] : 1) * 2;
-    hip_ok(hipMalloc(&params[i], bytes), "hipMalloc params");
-    hip_ok(hipMalloc(&grads[i], bytes), "hipMalloc grads");
+    if (flat_mode) {
+      params[i] = static_cast<char*>(flat_params) + offsets[i] * 2;
+      grads[i] = static_cast<char*>(flat) + offsets[i] * 2;
+    } else {
+      hip_ok(hipMalloc(&params[i], bytes), "hipMalloc params");
+      hip_ok(hipMalloc(&grads[i], bytes), "hipMalloc grads");
+    }
     pptr[i] = reinterpret_cast<uint64_t>(params[i]);
     gptr[i] = reinterpret_cast<uint64_t>(grads[i]);
   }
-  void *d_pptr = nullptr, *d_gptr = nullptr, *flat = nullptr;
+  void *d_pptr = nullptr, *d_gptr = nullptr;
   float *master = nullptr, *m = nullptr, *v = nullptr;
   hip_ok(hipMalloc(&d_pptr, n * sizeof(uint64_t)), "hipMalloc pointer table");
   hip_ok(hipMalloc(&d_gptr, n * sizeof(uint64_t)), "hipMalloc pointer table");
   hip_ok(hipMemcpy(d_pptr, pptr.data(), n * sizeof(uint64_t), hipMemcpyHostToDevice), "upload pointer table");
   hip_ok(hipMemcpy(d_gptr, gptr.data(), n * sizeof(uint64_t), hipMemcpyHostToDevice), "upload pointer table");
-  hip_ok(hipMalloc(&flat, static_cast<size_t>(flat_numel) * 2 + 16), "hipMalloc flat");
   const size_t sbytes = static_cast<size_t>(shard_numel > 0 ? shard_numel : 1) * sizeof(float);
   hip_ok(hipMalloc(reinterpret_cast<void**>(&master), sbytes), "hipMalloc master");
   hip_ok(hipMalloc(reinterpret_cast<void**>(&m), sbytes), "hipMalloc m");
@@ -113,9 +134,14 @@ int main(int argc, char** argv) {
   zs_ok(zs_pack(layout, d_pptr, static_cast<zs_dtype>(dtype), master, ZS_FP32, 0, nullptr, stream), "zs_pack");
   for (int32_t s = 0; s < steps; ++s) {
     upload(grads);
-    zs_ok(zs_step(layout, d_gptr, static_cast<zs_dtype>(dtype), flat, state, &hp, master, m, v, d_pptr,
-                  static_cast<zs_dtype>(dtype), stream),
-          "zs_step");
+    if (flat_mode)
+      zs_ok(zs_step_flat(layout, flat, static_cast<zs_dtype>(dtype), state, &hp, master, m, v, flat_params,
+                         static_cast<zs_dtype>(dtype), stream),
+            "zs_step_flat");
+    else
+      zs_ok(zs_step(layout, d_gptr, static_cast<zs_dtype>(dtype), flat, state, &hp, master, m, v, d_pptr,
+                    static_cast<zs_dtype>(dtype), stream),
+            "zs_step");
     hip_ok(hipStreamSynchronize(stream), "step");
   }
   std::fclose(in);
@@ -138,14 +164,18 @@ int main(int argc, char** argv) {
   if (std::fclose(out) != 0) die("writing the output", argv[2]);
 
   hip_ok(hipStreamDestroy(stream), "hipStreamDestroy");
-  for (int32_t i = 0; i < n; ++i) {
-    (void)hipFree(params[i]);
-    (void)hipFree(grads[i]);
+  if (!flat_mode) {
+    for (int32_t i = 0; i < n; ++i) {
+      (void)hipFree(params[i]);
+      (void)hipFree(grads[i]);
+    }
   }
-  for (void* p : {d_pptr, d_gptr, flat, static_cast<void*>(master), static_cast<void*>(m), static_cast<void*>(v)})
-    (void)hipFree(p);
+  for (void* p : {d_pptr, d_gptr, flat, flat_params, static_cast<void*>(master), static_cast<void*>(m),
+                  static_cast<void*>(v)})
+    if (p != nullptr) (void)hipFree(p);
   zs_state_destroy(state);
   zs_layout_destroy(layout);
-  std::printf("abi_gpu ok: %d tensors, %lld elements, %d steps\n", n, static_cast<long long>(total), steps);
+  std::printf("abi_gpu ok (%s): %d tensors, %lld elements, %d steps\n", mode.c_str(), n,
+              static_cast<long long>(total), steps);
   return 0;
 }

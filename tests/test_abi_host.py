@@ -227,5 +227,6 @@ def test_c_consumer_is_built_and_fails_cleanly_without_gpu(tmp_path):
     with open(inp, "wb") as f:
         f.write(struct.pack("<iii", 1, 0, 0) + struct.pack("<q", 4) + struct.pack("<6d", 1e-3, 0.9, 0.999, 1e-8, 0.0, 1.0))
         f.write(struct.pack("<ddii", 1.0, 1.0, 0, 1000) + bytes(8))
-    r = subprocess.run([exe, str(inp), str(tmp_path / "out.bin")], capture_output=True, text=True, timeout=60)
+    r = subprocess.run([exe, str(inp), str(tmp_path / "out.bin"), "flat"], capture_output=True, text=True,
+                       timeout=60)
     assert r.returncode == 1 and "zs_layout_create" in r.stderr, r.stderr

@@ -1,7 +1,8 @@
 """The C ABI from a C++ program with no Python and no torch (tests/c/abi_gpu.cpp, built by
 the package build): it allocates device memory and a stream with the HIP runtime, runs
-zs_step for every step, and writes its results, which are compared here with the oracle
-run on the same inputs.  Bar: the loss-scale sequence and skip count exactly; master, m and
+zs_step for every step (or, in flat mode, zs_step_flat over one gradient buffer and one
+parameter buffer), and writes its results, which are compared here with the oracle run on
+the same inputs.  Bar: the loss-scale sequence and skip count exactly; master, m and
 v within the 1e-5 relative contract; parameters equal to the cast of the program's master
 bit for bit."""
 
@@ -20,8 +21,9 @@ pytestmark = pytest.mark.gpu
 EXE = os.path.join(os.path.dirname(__file__), "c", "abi_gpu")
 
 
-@pytest.mark.parametrize("name", ["tiny", "llama_mini", "ragged_mini"])
-def test_c_program_runs_the_step_against_the_oracle(name, tmp_path):
+@pytest.mark.parametrize("name,mode", [("tiny", "tensors"), ("llama_mini", "tensors"), ("ragged_mini", "tensors"),
+                                       ("tiny", "flat"), ("ragged_mini", "flat")])
+def test_c_program_runs_the_step_against_the_oracle(name, mode, tmp_path):
     from harness import REL_TOL, bits, rel_err
     assert os.path.exists(EXE), f"{EXE} is missing: python -m zero_sharded_mixed_buffer_amd.build builds it"
     wl = WORKLOADS[name]
@@ -47,7 +49,7 @@ def test_c_program_runs_the_step_against_the_oracle(name, tmp_path):
             for t in tensors:
                 f.write(t.contiguous().view(torch.int16).numpy().tobytes())
     print(f"[case] C program {name}: {len(wl.numels)} tensors, {wl.n_elems} elements, {wl.steps} steps", flush=True)
-    res = subprocess.run([EXE, str(inp), str(out)], capture_output=True, text=True, timeout=120)
+    res = subprocess.run([EXE, str(inp), str(out), mode], capture_output=True, text=True, timeout=120)
     assert res.returncode == 0, res.stdout + res.stderr
     data = out.read_bytes()
     # zs_state_host: 2 doubles, 2 int32, 3 int64, 2 int32, 4 doubles
