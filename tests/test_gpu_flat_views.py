@@ -234,3 +234,57 @@ def test_step_flat_bit_identical_to_the_call_sequence(name):
     assert one.read_state()["skipped_total"] == len(wl.faults)
     one.close()
     seq.close()
+
+
+def test_step_flat_replays_in_a_hip_graph():
+    """The flat-views step captured once and replayed with new gradients in the buffer each
+    time (one replay overflowing), against the four calls run eagerly on a twin."""
+    import dataclasses
+    from harness import bits
+    Z = _z()
+    dev = torch.device("cuda", 0)
+    wl = dataclasses.replace(WORKLOADS["tiny"], growth_interval=2)
+    p0 = gen.make_params(wl, dev)
+    kw = dict(dynamic_loss_scale=wl.dynamic, init_scale=wl.init_scale, growth_interval=wl.growth_interval,
+              flat_views=True)
+    ma, mb = [p.clone() for p in p0], [p.clone() for p in p0]
+    gopt, eopt = Z.ZeroShardedAdamW(ma, **kw), Z.ZeroShardedAdamW(mb, **kw)
+
+    def load(model, opt, grads):
+        opt.zero_grad()
+        for p, g in zip(model, grads):
+            p.grad.add_(g)
+
+    grads = gen.make_grads(wl, 1, wl.init_scale, dev, with_faults=False)
+    load(ma, gopt, grads)
+    load(mb, eopt, grads)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        gopt.step()
+    torch.cuda.current_stream().wait_stream(s)
+    eopt.check()
+    eopt.norm()
+    eopt.update()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gopt.step()
+    torch.cuda.synchronize()
+    for replay in range(5):
+        grads = gen.make_grads(wl, 20 + replay, eopt.read_state()["loss_scale"], dev, with_faults=False)
+        if replay == 3:
+            grads[2].view(-1)[5] = math.inf
+        load(ma, gopt, grads)
+        load(mb, eopt, grads)
+        graph.replay()
+        eopt.check()
+        eopt.norm()
+        eopt.update()
+        torch.cuda.synchronize()
+        for x, y in ((gopt.master, eopt.master), (gopt.m, eopt.m), (gopt.v, eopt.v),
+                     (gopt.flat_params, eopt.flat_params)):
+            assert torch.equal(bits(x), bits(y)), f"replay {replay}"
+        assert gopt.read_state()["loss_scale"] == eopt.read_state()["loss_scale"]
+    assert gopt.read_state()["skipped_total"] == 1 and gopt.read_state()["step_t"] == 5
+    gopt.close()
+    eopt.close()
