@@ -126,6 +126,9 @@ def test_flat_views_reject_what_they_cannot_hold():
     with pytest.raises(ValueError):
         opt.step()  # no gradients and no views
     opt.close()
+    twice = torch.zeros(8, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError, match="more than once"):
+        Z.ZeroShardedAdamW([twice, twice])
     # a .grad set to None (as a model-level zero_grad does) is refused, and zero_grad() mends it
     ps = [torch.nn.Parameter(torch.ones(8, dtype=torch.bfloat16, device=dev)) for _ in range(2)]
     opt = Z.ZeroShardedAdamW(ps, flat_views=True)

@@ -63,6 +63,9 @@ class ZeroShardedAdamW:
         params = list(params)
         if not params:
             raise ValueError("empty parameter list")
+        if len({id(p) for p in params}) != len(params):
+            # two segments scattering into one tensor would race
+            raise ValueError("a tensor appears more than once in the parameter list")
         self.device = params[0].device
         self.param_dtype = params[0].dtype
         self.model_grad_dtype = grad_dtype or self.param_dtype
