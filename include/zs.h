@@ -25,7 +25,9 @@
  *     on `stream` has completed.
  *   - Pointer tables (`src_ptrs`, `param_ptrs`, `dst_ptrs`) are DEVICE arrays of n_tensors
  *     device pointers (uint64 each), in parameter-list order, owned by the caller; an entry
- *     for a tensor with zero elements is never read through.
+ *     for a tensor with zero elements is never read through.  The tensors a table writes
+ *     (`param_ptrs`, `dst_ptrs`) must not overlap one another or the flat buffers: their
+ *     elements are written concurrently, in no fixed order.
  *   - `stream` is a hipStream_t (NULL = the null stream). Every device step call only
  *     enqueues kernels on it and never synchronises the host; results live in device
  *     memory. The calls that synchronise are zs_state_read and zs_state_write (their
