@@ -44,4 +44,4 @@ from ._abi import (  # noqa: F401
     zs_unpack,
     zs_unscale_check,
 )
-from .optimizer import ZeroShardedAdamW, pointer_table  # noqa: F401
+from .optimizer import ZeroShardedAdamW, pointer_table, reshard_state_dicts  # noqa: F401

@@ -31,6 +31,61 @@ def pointer_table(tensors, device):
     return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
 
 
+# Checkpoint format of ZeroShardedAdamW.state_dict(), and the state fields it keeps (the
+# others are results of the latest check and norm, recomputed by the next step).
+STATE_FORMAT = "zs-rank-state-1"
+PERSISTENT_STATE = ("loss_scale", "scale_floor", "dynamic", "growth_interval", "growth_tracker", "step_t",
+                    "skipped_total")
+
+
+def reshard_state_dicts(state_dicts, dp_world, dp_rank):
+    """The state dict of rank dp_rank of a dp_world-way group, from every rank's
+    state_dict() of one checkpoint taken at any other group size (the same tensor list and
+    align).  Ranks own equal contiguous slices of one flat buffer whose layout does not
+    depend on the group size, only its zero tail padding does ("Deep dive: Megatron",
+    section "Distributed optimizer"), so re-sharding concatenates the old shards in rank
+    order, re-pads the tail with zeros and slices the new rank's range.  Padding elements
+    carry zero master, m and v and keep them: their gradient is zero.  The scaler and step
+    counters are replicated, so every rank must hold the same ones."""
+    sds = list(state_dicts)
+    if not sds:
+        raise ValueError("no state dicts")
+    for sd in sds:
+        if sd.get("format") != STATE_FORMAT:
+            raise ValueError(f"not a {STATE_FORMAT} state dict")
+    lay0 = sds[0]["layout"]
+    numels, align, d_old = list(lay0["numels"]), lay0["align"], lay0["dp_world"]
+    by_rank = {}
+    for sd in sds:
+        lay = sd["layout"]
+        if list(lay["numels"]) != numels or lay["align"] != align or lay["dp_world"] != d_old:
+            raise ValueError("the state dicts come from different layouts")
+        if lay["dp_rank"] in by_rank:
+            raise ValueError(f"rank {lay['dp_rank']} appears twice")
+        if sd["state"] != sds[0]["state"]:
+            raise ValueError("the ranks' scaler and step states differ")
+        by_rank[lay["dp_rank"]] = sd
+    if sorted(by_rank) != list(range(d_old)):
+        raise ValueError(f"need the state dicts of all {d_old} ranks")
+    offsets, flat_old, _, _ = A.zs_plan(numels, d_old, 0, align)
+    new_offsets, flat_new, begin, count = A.zs_plan(numels, dp_world, dp_rank, align)
+    if new_offsets != offsets:  # the planner places tensors independently of the group size
+        raise ValueError("tensor offsets differ between the two group sizes")
+    used = max((o + n for o, n in zip(offsets, numels)), default=0)
+    out = {"format": STATE_FORMAT,
+           "layout": {"numels": numels, "dp_world": dp_world, "dp_rank": dp_rank, "align": align,
+                      "flat_numel": flat_new, "shard_begin": begin, "shard_numel": count},
+           "state": dict(sds[0]["state"])}
+    for k in ("master", "m", "v"):
+        whole = torch.cat([by_rank[r][k].reshape(-1) for r in range(d_old)])
+        if whole.numel() != flat_old:
+            raise ValueError(f"{k}: the shards do not add up to the flat buffer")
+        new = torch.zeros(flat_new, dtype=torch.float32)
+        new[:used] = whole[:used]
+        out[k] = new[begin:begin + count].clone()
+    return out
+
+
 class ZeroShardedAdamW:
     """One data-parallel rank's ZeRO-1/2 AdamW over bf16/fp16 parameters on one GPU.
 
@@ -79,7 +134,7 @@ class ZeroShardedAdamW:
         self.params = params
         self.numels = [p.numel() for p in params]
         self.hp = A.hparams(lr, betas[0], betas[1], eps, weight_decay, max_norm)
-        self.dp_world, self.dp_rank = dp_world, dp_rank
+        self.dp_world, self.dp_rank, self.align = dp_world, dp_rank, align
         with torch.cuda.device(self.device):
             self.layout = A.zs_layout_create(self.numels, dp_world, dp_rank, align)
             self.flat_numel, self.shard_begin, self.shard_numel = A.zs_layout_info(self.layout)
@@ -294,6 +349,46 @@ class ZeroShardedAdamW:
         for k, v in values.items():
             setattr(s, k, v)
         A.zs_state_write(self.state, s, stream)
+
+    def state_dict(self, stream=None):
+        """Host copy of what resuming this rank needs: the scaler and step counters, and the
+        fp32 master, m and v of its shard, with the layout they belong to.  The model-dtype
+        parameters are the model's to save, as with torch.optim; they are the round-to-
+        nearest-even cast of the master.  Synchronises (reads the device state)."""
+        st = self.read_state(stream)
+        return {
+            "format": STATE_FORMAT,
+            "layout": {"numels": list(self.numels), "dp_world": self.dp_world, "dp_rank": self.dp_rank,
+                       "align": self.align, "flat_numel": self.flat_numel, "shard_begin": self.shard_begin,
+                       "shard_numel": self.shard_numel},
+            "state": {k: st[k] for k in PERSISTENT_STATE},
+            "master": self.master.detach().to("cpu", copy=True),
+            "m": self.m.detach().to("cpu", copy=True),
+            "v": self.v.detach().to("cpu", copy=True),
+        }
+
+    def load_state_dict(self, sd, stream=None):
+        """Restore a state_dict() of this rank's layout (the same tensor sizes, dp_world,
+        dp_rank and align; reshard_state_dicts() maps a checkpoint taken at another dp_world).
+        Writes the scaler and step counters and the master, m and v shard; the model-dtype
+        parameters are restored by the model, as with torch.optim."""
+        if sd.get("format") != STATE_FORMAT:
+            raise ValueError(f"not a {STATE_FORMAT} state dict")
+        lay = sd["layout"]
+        mine = (list(self.numels), self.dp_world, self.dp_rank, self.align)
+        theirs = (list(lay["numels"]), lay["dp_world"], lay["dp_rank"], lay["align"])
+        if mine != theirs:
+            raise ValueError("the state dict belongs to another layout (tensor sizes, dp_world, dp_rank or "
+                             "align); map it with reshard_state_dicts()")
+        for k in ("master", "m", "v"):
+            t = sd[k]
+            if t.dtype != torch.float32 or t.numel() != self.shard_numel:
+                raise ValueError(f"{k}: expected {self.shard_numel} fp32 elements")
+        self.write_state({k: sd["state"][k] for k in PERSISTENT_STATE}, stream)
+        for k in ("master", "m", "v"):
+            getattr(self, k).copy_(sd[k].reshape(-1))
+        if self.master.is_cuda:
+            torch.cuda.synchronize(self.device)
 
     def close(self):
         if getattr(self, "state", None):
