@@ -118,12 +118,15 @@ def _window_values(tensors_cpu, lay, a, b, dtype):
     return out
 
 
-def run_parity_sampled(wl, steps=None, log=print, centres=(), n_random=48):
+def run_parity_sampled(wl, steps=None, log=print, centres=(), n_random=48, views=False):
     """Full-size parity on sampled outputs.  The GPU runs the whole step at the workload's
     real size in the same launch configuration as bench.py; the oracle computes every
     step's flag, scaler and global norm from all gradients (streamed to the host one
     tensor at a time) and the AdamW state only on sampled shard windows, which are
-    compared element by element (master, m, v, params, packed buffer)."""
+    compared element by element (master, m, v, params, packed buffer).  views=True (one
+    rank): the parameters and gradients are views of two flat buffers, the gradients are
+    written through the .grad views as backward would, and each step is the single
+    zs_step_flat call."""
     steps = wl.steps if steps is None else steps
     d, rank, align = wl.dp_world, wl.dp_rank, wl.align
     dev = torch.device("cuda", 0)
@@ -137,7 +140,8 @@ def run_parity_sampled(wl, steps=None, log=print, centres=(), n_random=48):
     opt = Z.ZeroShardedAdamW(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
                              weight_decay=hp["weight_decay"], max_norm=hp["max_norm"], dp_world=d, dp_rank=rank,
                              align=align, dynamic_loss_scale=wl.dynamic, init_scale=wl.init_scale,
-                             growth_interval=wl.growth_interval)
+                             growth_interval=wl.growth_interval, flat_views=views)
+    assert not views or d == 1
     scaler = oracle_scaler(wl)
     # Oracle state on the windows only.
     ref = {}
@@ -168,8 +172,17 @@ def run_parity_sampled(wl, steps=None, log=print, centres=(), n_random=48):
         for step in range(1, steps + 1):
             scale = scaler.loss_scale
             grads = gen.make_grads(wl, step, scale, dev)
-            opt.pack(grads)
-            if d == 1:
+            if views:
+                with torch.no_grad():
+                    for p, g in zip(params, grads):
+                        p.grad.copy_(g)
+                opt.step()
+                st_before = st = opt.read_state()
+            else:
+                opt.pack(grads)
+            if views:
+                pass
+            elif d == 1:
                 opt.norm()
             else:
                 for q in range(d):
@@ -182,9 +195,10 @@ def run_parity_sampled(wl, steps=None, log=print, centres=(), n_random=48):
                 for lq, sq in others.values():
                     Z.zs_grad_norm(lq, None, dt, sq, opt.hp, exchange, None)
                     Z.zs_scaler_update(sq)
-            st_before = opt.read_state()
-            opt.update()
-            st = opt.read_state()
+            if not views:
+                st_before = opt.read_state()
+                opt.update()
+                st = opt.read_state()
 
             # Oracle: flag and global norm over every gradient element, one tensor at a time.
             overflow = False

@@ -30,6 +30,23 @@ def test_fullsize_sampled_parity(name, steps):
           flush=True)
 
 
+@pytest.mark.parametrize("name,steps", [("llama3_8b", 2), ("ragged_20k", 3)])
+def test_fullsize_flat_views_sampled_parity(name, steps):
+    """The flat-views step at full size: gradients written through the .grad views of the
+    gradient buffer, one zs_step_flat call per step (check, norm, AdamW into the parameter
+    buffer), against the oracle on sampled windows."""
+    import zero_sharded_mixed_buffer_amd as Z
+    from harness import run_parity_sampled
+    Z.lib()
+    wl = WORKLOADS[name]
+    print(f"[case] fullsize flat views {name}: N={wl.n_elems}, steps={steps}", flush=True)
+    t0 = time.time()
+    worst, ndiff, wins = run_parity_sampled(wl, steps=steps, log=lambda s: print(s, flush=True), n_random=16,
+                                            views=True)
+    print(f"[fullsize] flat views {name}: {len(wins)} windows, worst={worst}, ndiff={ndiff}, "
+          f"{time.time() - t0:.1f} s", flush=True)
+
+
 def test_tensor_beyond_int32_element_indices():
     """One tensor of 2^31 + 4099 elements between two small ones: element indices above 2^31
     and fp32 byte offsets above 2^32 in every array.  Sampled windows sit across those
