@@ -230,3 +230,16 @@ def test_c_consumer_is_built_and_fails_cleanly_without_gpu(tmp_path):
     r = subprocess.run([exe, str(inp), str(tmp_path / "out.bin"), "flat"], capture_output=True, text=True,
                        timeout=60)
     assert r.returncode == 1 and "zs_layout_create" in r.stderr, r.stderr
+
+
+def test_tensors_the_kernels_would_dereference_are_checked_first():
+    """Host or wrong-device tensors never reach a pointer table: a kernel would fault on them."""
+    import torch
+
+    import zero_sharded_mixed_buffer_amd as Z
+    with pytest.raises(ValueError, match="GPU"):
+        Z.ZeroShardedAdamW([torch.zeros(4, dtype=torch.bfloat16)])
+    with pytest.raises(ValueError, match="lives on cpu"):
+        Z.pointer_table([torch.zeros(4, dtype=torch.bfloat16)], torch.device("cuda", 0))
+    with pytest.raises(ValueError, match="contiguous"):
+        Z.pointer_table([torch.zeros(4, 4, dtype=torch.bfloat16).t()], "cpu")

@@ -225,6 +225,18 @@ def test_step_rejects_bad_arguments():
         Z.zs_step(**{**args, "layout": lay2, "state": st2})
     Z.zs_state_destroy(st2)
     Z.zs_layout_destroy(lay2)
+    # tensors the kernels would misread or fault on are refused before any launch
+    with pytest.raises(ValueError, match="lives on cpu"):
+        opt.step([g.cpu() for g in grads])
+    with pytest.raises(ValueError, match="gradients must be"):
+        opt.step([g.float() for g in grads])
+    params = gen.make_params(wl, dev)
+    with pytest.raises(ValueError, match="one dtype"):
+        Z.ZeroShardedAdamW(params[:-1] + [params[-1].half()])
+    with pytest.raises(ValueError, match="lives on cpu"):
+        Z.ZeroShardedAdamW(params[:-1] + [params[-1].cpu()])
+    with pytest.raises(ValueError, match="bf16 or fp16"):
+        Z.ZeroShardedAdamW([p.float() for p in params])
     torch.cuda.synchronize()
     assert opt.read_state()["step_t"] == 0  # nothing was enqueued
     opt.close()

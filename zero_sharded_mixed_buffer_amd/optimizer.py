@@ -24,10 +24,16 @@ from . import _abi as A
 
 
 def pointer_table(tensors, device):
-    """Device int64 array of the tensors' data pointers (the ABI's pointer tables)."""
+    """Device int64 array of the tensors' data pointers (the ABI's pointer tables).  The
+    kernels dereference every pointer of a non-empty tensor, so each must be contiguous and
+    live on `device` (a host or another GPU's pointer would fault the GPU)."""
+    device = torch.device(device)
     for t in tensors:
-        if t.numel() and not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
+        if t.numel():
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+            if t.device != device:
+                raise ValueError(f"a tensor lives on {t.device}, not on {device}")
     return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
 
 
@@ -123,6 +129,15 @@ class ZeroShardedAdamW:
             raise ValueError("a tensor appears more than once in the parameter list")
         self.device = params[0].device
         self.param_dtype = params[0].dtype
+        if self.device.type != "cuda":
+            raise ValueError("the parameters must live on a GPU")
+        if self.param_dtype not in (torch.bfloat16, torch.float16):
+            raise ValueError("the parameters must be bf16 or fp16")
+        if any(p.dtype != self.param_dtype for p in params):
+            raise ValueError("every parameter must have one dtype (the kernels cast to one model dtype)")
+        for p in params:
+            if p.device != self.device:
+                raise ValueError(f"a parameter lives on {p.device}, not on {self.device}")
         self.model_grad_dtype = grad_dtype or self.param_dtype
         # The flat buffer holds the model-dtype gradients, or an fp32 accumulation buffer
         # when accum_dtype=torch.float32 (gradient accumulation over micro-steps).
@@ -228,6 +243,8 @@ class ZeroShardedAdamW:
         if key != self._grad_key:
             if len(grads) != len(self.numels) or any(g.numel() != n for g, n in zip(grads, self.numels)):
                 raise ValueError("gradients must match the parameter list")
+            if any(g.dtype != self.model_grad_dtype for g in grads):
+                raise ValueError(f"gradients must be {self.model_grad_dtype}")
             self._grad_ptrs = pointer_table(grads, self.device)
             self._grad_key = key
         return self._grad_ptrs
