@@ -243,3 +243,31 @@ def test_tensors_the_kernels_would_dereference_are_checked_first():
         Z.pointer_table([torch.zeros(4, dtype=torch.bfloat16)], torch.device("cuda", 0))
     with pytest.raises(ValueError, match="contiguous"):
         Z.pointer_table([torch.zeros(4, 4, dtype=torch.bfloat16).t()], "cpu")
+
+
+def test_binding_refuses_tensors_in_the_wrong_memory():
+    """A host tensor passed where the library wants device memory (it would be dereferenced
+    by a kernel), or a device tensor where it wants host memory, is refused by the binding
+    before the library is called."""
+    import torch
+
+    import zero_sharded_mixed_buffer_amd as Z
+    host = torch.zeros(16)
+    hp = Z.hparams()
+    for call in (lambda: Z.zs_pack(None, host, torch.bfloat16, host, torch.bfloat16),
+                 lambda: Z.zs_unscale_check(None, host, torch.bfloat16, None),
+                 lambda: Z.zs_adamw_step(None, host, torch.bfloat16, host, host, host, hp, None),
+                 lambda: Z.zs_unpack(None, host, torch.float32, True, host, torch.bfloat16),
+                 lambda: Z.zs_step(None, host, torch.bfloat16, host, None, hp, host, host, host, host),
+                 lambda: Z.zs_step_flat(None, host, torch.bfloat16, None, hp, host, host, host, host)):
+        with pytest.raises(Z.ZsInvalidArgument, match="must be device memory"):
+            call()
+
+    class DeviceTensor:  # stands in for a GPU tensor on a machine without one
+        is_cuda = True
+
+        def data_ptr(self):
+            return 0
+
+    with pytest.raises(Z.ZsInvalidArgument, match="must be host memory"):
+        Z.zs_host_adamw_step(DeviceTensor(), torch.bfloat16, host, host, host, 16, hp, Z.state_host())

@@ -2,8 +2,11 @@
 
 Argument marshalling only: every computation runs in the HIP library.  Pointer
 arguments accept an int (a device or host address), None (NULL) or anything
-with .data_ptr() (a torch tensor); `stream` accepts a torch stream, an int
-handle or None (the current torch stream of the current device).  A non-zero
+with .data_ptr() (a torch tensor); a tensor in the wrong memory (a host tensor
+where the library wants device memory, or the reverse) is refused before the
+call, since it would be dereferenced on the wrong side.  `stream` accepts a
+torch stream, an int handle or None (the current torch stream of the current
+device).  A non-zero
 status raises ZsError carrying zs_last_error().  If the library is not built
 the first call raises ImportError; there is no fallback path.
 """
@@ -119,6 +122,21 @@ def _ptr(x):
     if isinstance(x, ctypes.Array):
         return ctypes.addressof(x)
     return int(x)
+
+
+def _dptr(x, what, where):
+    """A device-memory argument: a host tensor here would be dereferenced by a kernel and
+    fault the GPU, so it is refused before the call (raw integers pass unchecked)."""
+    if x is not None and hasattr(x, "data_ptr") and not x.is_cuda:
+        raise ZsInvalidArgument(where, -1, f"{what} must be device memory, got a host tensor")
+    return _ptr(x)
+
+
+def _hptr(x, what, where):
+    """A host-memory argument: a device tensor here would be dereferenced by the host."""
+    if x is not None and hasattr(x, "data_ptr") and x.is_cuda:
+        raise ZsInvalidArgument(where, -1, f"{what} must be host memory, got a device tensor")
+    return _ptr(x)
 
 
 def _stream(s):
@@ -254,42 +272,54 @@ def hparams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_no
 # ------------------------------------------------------------------------------ step calls
 
 def zs_pack(layout, src_ptrs, src_dtype, dst, dst_dtype, whole_flat=True, fuse_check=None, stream=None):
-    _check(lib().zs_pack(layout, _ptr(src_ptrs), dtype_code(src_dtype), _ptr(dst), dtype_code(dst_dtype),
-                         int(bool(whole_flat)), fuse_check, _stream(stream)), "zs_pack")
+    W = "zs_pack"
+    _check(lib().zs_pack(layout, _dptr(src_ptrs, "src_ptrs", W), dtype_code(src_dtype), _dptr(dst, "dst", W),
+                         dtype_code(dst_dtype), int(bool(whole_flat)), fuse_check, _stream(stream)), W)
 
 
 def zs_pack_accumulate(layout, src_ptrs, src_dtype, acc, acc_dtype, whole_flat=True, fuse_check=None, stream=None):
-    _check(lib().zs_pack_accumulate(layout, _ptr(src_ptrs), dtype_code(src_dtype), _ptr(acc), dtype_code(acc_dtype),
-                                    int(bool(whole_flat)), fuse_check, _stream(stream)), "zs_pack_accumulate")
+    W = "zs_pack_accumulate"
+    _check(lib().zs_pack_accumulate(layout, _dptr(src_ptrs, "src_ptrs", W), dtype_code(src_dtype),
+                                    _dptr(acc, "acc", W), dtype_code(acc_dtype), int(bool(whole_flat)), fuse_check,
+                                    _stream(stream)), W)
 
 
 def zs_pack_bucket(layout, src_ptrs, src_dtype, flat, flat_dtype, tensor_begin, tensor_end, accumulate=False,
                    stream=None):
-    _check(lib().zs_pack_bucket(layout, _ptr(src_ptrs), dtype_code(src_dtype), _ptr(flat), dtype_code(flat_dtype),
-                                tensor_begin, tensor_end, int(bool(accumulate)), _stream(stream)), "zs_pack_bucket")
+    W = "zs_pack_bucket"
+    _check(lib().zs_pack_bucket(layout, _dptr(src_ptrs, "src_ptrs", W), dtype_code(src_dtype), _dptr(flat, "flat", W),
+                                dtype_code(flat_dtype), tensor_begin, tensor_end, int(bool(accumulate)),
+                                _stream(stream)), W)
 
 
 def zs_unscale_check(layout, shard, grad_dtype, state, ext_overflow=None, local_sumsq_out=None, stream=None):
-    _check(lib().zs_unscale_check(layout, _ptr(shard), dtype_code(grad_dtype), state, _ptr(ext_overflow),
-                                  _ptr(local_sumsq_out), _stream(stream)), "zs_unscale_check")
+    W = "zs_unscale_check"
+    _check(lib().zs_unscale_check(layout, _dptr(shard, "shard", W), dtype_code(grad_dtype), state,
+                                  _dptr(ext_overflow, "ext_overflow", W),
+                                  _dptr(local_sumsq_out, "local_sumsq_out", W), _stream(stream)), W)
 
 
 def zs_grad_norm(layout, shard, grad_dtype, state, hp: AdamwHParams, rank_sumsq=None, local_sumsq_out=None,
                  stream=None):
-    _check(lib().zs_grad_norm(layout, _ptr(shard), dtype_code(grad_dtype), state, byref(hp), _ptr(rank_sumsq),
-                              _ptr(local_sumsq_out), _stream(stream)), "zs_grad_norm")
+    W = "zs_grad_norm"
+    _check(lib().zs_grad_norm(layout, _dptr(shard, "shard", W), dtype_code(grad_dtype), state, byref(hp),
+                              _dptr(rank_sumsq, "rank_sumsq", W), _dptr(local_sumsq_out, "local_sumsq_out", W),
+                              _stream(stream)), W)
 
 
 def zs_adamw_step(layout, shard, grad_dtype, master, m, v, hp: AdamwHParams, state, param_ptrs=None,
                   flat_param_out=None, param_dtype=ZS_BF16, stream=None):
-    _check(lib().zs_adamw_step(layout, _ptr(shard), dtype_code(grad_dtype), _ptr(master), _ptr(m), _ptr(v),
-                               byref(hp), state, _ptr(param_ptrs), _ptr(flat_param_out), dtype_code(param_dtype),
-                               _stream(stream)), "zs_adamw_step")
+    W = "zs_adamw_step"
+    _check(lib().zs_adamw_step(layout, _dptr(shard, "shard", W), dtype_code(grad_dtype), _dptr(master, "master", W),
+                               _dptr(m, "m", W), _dptr(v, "v", W), byref(hp), state,
+                               _dptr(param_ptrs, "param_ptrs", W), _dptr(flat_param_out, "flat_param_out", W),
+                               dtype_code(param_dtype), _stream(stream)), W)
 
 
 def zs_unpack(layout, src, src_dtype, whole_flat, dst_ptrs, dst_dtype, honour_skip=None, stream=None):
-    _check(lib().zs_unpack(layout, _ptr(src), dtype_code(src_dtype), int(bool(whole_flat)), _ptr(dst_ptrs),
-                           dtype_code(dst_dtype), honour_skip, _stream(stream)), "zs_unpack")
+    W = "zs_unpack"
+    _check(lib().zs_unpack(layout, _dptr(src, "src", W), dtype_code(src_dtype), int(bool(whole_flat)),
+                           _dptr(dst_ptrs, "dst_ptrs", W), dtype_code(dst_dtype), honour_skip, _stream(stream)), W)
 
 
 def zs_scaler_update(state, stream=None):
@@ -299,18 +329,21 @@ def zs_scaler_update(state, stream=None):
 def zs_step(layout, grad_ptrs, grad_dtype, flat, state, hp: AdamwHParams, master, m, v, param_ptrs,
             param_dtype=ZS_BF16, stream=None):
     """The whole single-rank step: pack, check, norm, AdamW with scatter, scaler commit."""
-    _check(lib().zs_step(layout, _ptr(grad_ptrs), dtype_code(grad_dtype), _ptr(flat), state, byref(hp),
-                         _ptr(master), _ptr(m), _ptr(v), _ptr(param_ptrs), dtype_code(param_dtype),
-                         _stream(stream)), "zs_step")
+    W = "zs_step"
+    _check(lib().zs_step(layout, _dptr(grad_ptrs, "grad_ptrs", W), dtype_code(grad_dtype), _dptr(flat, "flat", W),
+                         state, byref(hp), _dptr(master, "master", W), _dptr(m, "m", W), _dptr(v, "v", W),
+                         _dptr(param_ptrs, "param_ptrs", W), dtype_code(param_dtype), _stream(stream)), W)
 
 
 def zs_step_flat(layout, flat, grad_dtype, state, hp: AdamwHParams, master, m, v, flat_param_out,
                  param_dtype=ZS_BF16, stream=None):
     """The single-rank step over contiguous gradient and parameter buffers: check, norm,
     AdamW writing the parameter buffer, scaler commit."""
-    _check(lib().zs_step_flat(layout, _ptr(flat), dtype_code(grad_dtype), state, byref(hp), _ptr(master), _ptr(m),
-                              _ptr(v), _ptr(flat_param_out), dtype_code(param_dtype), _stream(stream)),
-           "zs_step_flat")
+    W = "zs_step_flat"
+    _check(lib().zs_step_flat(layout, _dptr(flat, "flat", W), dtype_code(grad_dtype), state, byref(hp),
+                              _dptr(master, "master", W), _dptr(m, "m", W), _dptr(v, "v", W),
+                              _dptr(flat_param_out, "flat_param_out", W), dtype_code(param_dtype),
+                              _stream(stream)), W)
 
 
 def zs_last_error():
@@ -323,15 +356,20 @@ def zs_host_adamw_step(grad, grad_dtype, master, m, v, count, hp: AdamwHParams, 
                        param_out=None, param_dtype=None, n_threads=0):
     """Host AdamW over `count` elements of host arrays (see zs.h)."""
     pdt = dtype_code(param_dtype) if param_dtype is not None else ZS_BF16
-    _check(lib().zs_host_adamw_step(_ptr(grad), dtype_code(grad_dtype), _ptr(master), _ptr(m), _ptr(v), int(count),
-                                    byref(hp), byref(scalars), _ptr(param_out), pdt, int(n_threads)),
+    W = "zs_host_adamw_step"
+    _check(lib().zs_host_adamw_step(_hptr(grad, "grad", W), dtype_code(grad_dtype), _hptr(master, "master", W),
+                                    _hptr(m, "m", W), _hptr(v, "v", W), int(count), byref(hp), byref(scalars),
+                                    _hptr(param_out, "param_out", W), pdt, int(n_threads)),
            "zs_host_adamw_step")
 
 
 def zs_offload_adamw_step(layout, shard, grad_dtype, state, hp: AdamwHParams, master, m, v, grad_stage, param_stage,
                           chunk_numel, flat_param_out, param_dtype, n_threads=0, stream=None):
     """Offloaded update of the rank's shard: chunks down, host update, parameters up (see zs.h)."""
-    _check(lib().zs_offload_adamw_step(layout, _ptr(shard), dtype_code(grad_dtype), state, byref(hp), _ptr(master),
-                                       _ptr(m), _ptr(v), _ptr(grad_stage), _ptr(param_stage), int(chunk_numel),
-                                       _ptr(flat_param_out), dtype_code(param_dtype), int(n_threads),
-                                       _stream(stream)), "zs_offload_adamw_step")
+    W = "zs_offload_adamw_step"
+    _check(lib().zs_offload_adamw_step(layout, _dptr(shard, "shard", W), dtype_code(grad_dtype), state, byref(hp),
+                                       _hptr(master, "master", W), _hptr(m, "m", W), _hptr(v, "v", W),
+                                       _hptr(grad_stage, "grad_stage", W), _hptr(param_stage, "param_stage", W),
+                                       int(chunk_numel), _dptr(flat_param_out, "flat_param_out", W),
+                                       dtype_code(param_dtype), int(n_threads), _stream(stream)),
+           "zs_offload_adamw_step")
