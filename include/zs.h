@@ -22,7 +22,10 @@
  * Conventions for every entry point:
  *   - Tensor data pointers are DEVICE pointers on the layout's GPU, owned by the caller
  *     (typically allocated through PyTorch). They must stay valid until the work enqueued
- *     on `stream` has completed.
+ *     on `stream` has completed. The library does not query the runtime for what a pointer
+ *     is (that would cost every call a runtime round trip, and the pointer tables live on
+ *     the device anyway): a host pointer passed as device memory is dereferenced by a
+ *     kernel and faults the GPU. The Python binding refuses host tensors in these places.
  *   - Pointer tables (`src_ptrs`, `param_ptrs`, `dst_ptrs`) are DEVICE arrays of n_tensors
  *     device pointers (uint64 each), in parameter-list order, owned by the caller; an entry
  *     for a tensor with zero elements is never read through.  The tensors a table writes
