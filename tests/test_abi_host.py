@@ -271,3 +271,22 @@ def test_binding_refuses_tensors_in_the_wrong_memory():
 
     with pytest.raises(Z.ZsInvalidArgument, match="must be host memory"):
         Z.zs_host_adamw_step(DeviceTensor(), torch.bfloat16, host, host, host, 16, hp, Z.state_host())
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without libzs.so every entry point raises ImportError: there is no other path."""
+    import torch
+
+    import zero_sharded_mixed_buffer_amd as Z
+    from zero_sharded_mixed_buffer_amd import _abi
+    monkeypatch.setattr(_abi, "LIB_PATH", str(tmp_path / "libzs.so"))
+    monkeypatch.setattr(_abi, "_lib", None)
+    with pytest.raises(ImportError, match="libzs.so is missing"):
+        Z.lib()
+    with pytest.raises(ImportError):
+        Z.zs_plan([4, 5], 1, 0)
+    with pytest.raises(ImportError):
+        Z.zs_scaler_update(None, stream=0)
+    with pytest.raises(ImportError):
+        Z.zs_host_adamw_step(torch.zeros(4, dtype=torch.bfloat16), torch.bfloat16, torch.zeros(4), torch.zeros(4),
+                             torch.zeros(4), 4, Z.hparams(), Z.state_host())
