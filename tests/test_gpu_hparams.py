@@ -38,3 +38,54 @@ def test_hyperparameter_parity(name, use_step, case):
     assert [s.step for s in rep.steps if s.overflow_gpu] == sorted(k for k in wl.faults if k <= 6)
     if case == "heavy_clip":
         assert all(s.clip_gpu < 1.0 for s in rep.steps if not s.overflow_gpu)
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama_mini"])
+def test_per_step_schedule_matches_the_oracle(name):
+    """Hyper-parameters changed before each step, as a training schedule does: a linear
+    learning-rate warmup then cosine decay, with the weight decay and the clipping
+    threshold changed part-way.  The oracle applies the same values step by step."""
+    import math
+
+    import torch
+
+    import oracle as O
+    import zero_sharded_mixed_buffer_amd as Z
+    from harness import bits, rel_err
+    from workloads import gen
+    Z.lib()
+    wl = WORKLOADS[name]
+    dev = torch.device("cuda", 0)
+    print(f"[case] schedule on {name}", flush=True)
+    hp = dict(HPARAMS)
+    params = gen.make_params(wl, dev)
+    opt = Z.ZeroShardedAdamW(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                             weight_decay=hp["weight_decay"], max_norm=hp["max_norm"], align=wl.align,
+                             dynamic_loss_scale=wl.dynamic, init_scale=wl.init_scale)
+    ref = O.OracleRank(wl.numels, 1, 0, [p.cpu() for p in params],
+                       O.OracleScaler(wl.init_scale, dynamic=wl.dynamic), hp, wl.align)
+    steps, warm = 8, 3
+    for s in range(1, steps + 1):
+        lr = 2e-3 * (s / warm if s <= warm else 0.5 * (1 + math.cos(math.pi * (s - warm) / (steps - warm))))
+        change = dict(lr=lr)
+        if s == 5:
+            change.update(weight_decay=0.1, max_norm=0.05)
+        opt.set_hparams(**change)
+        ref.hp.update(change)
+        grads = gen.make_grads(wl, s, ref.scaler.loss_scale, dev)
+        opt.step(grads)
+        ref.step(O.shard_of(O.pack([g.cpu() for g in grads], ref.layout), ref.layout))
+        st = opt.read_state()
+        assert st["loss_scale"] == ref.scaler.loss_scale and st["step_t"] == ref.scaler.step_t, s
+    torch.cuda.synchronize()
+    pairs = ((opt.master, ref.master), (opt.m, ref.m), (opt.v, ref.v))
+    errs = [rel_err(a.cpu(), b) for a, b in pairs]
+    nd = [int((bits(a.cpu()) != bits(b)).sum()) for a, b in pairs]
+    print(f"[parity] schedule {name}: errs={errs} diff={nd} final lr={opt.hp.lr}", flush=True)
+    assert max(errs) <= 1e-5
+    assert opt.hp.weight_decay == 0.1 and opt.hp.max_norm == 0.05 and opt.hp.beta2 == hp["beta2"]
+    with pytest.raises(Z.ZsInvalidArgument):
+        opt.set_hparams(lr=-1.0)
+        opt.step(gen.make_grads(wl, steps + 1, ref.scaler.loss_scale, dev))
+    assert opt.read_state()["step_t"] == ref.scaler.step_t  # the refused step enqueued nothing
+    opt.close()

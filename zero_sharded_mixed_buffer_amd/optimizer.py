@@ -358,6 +358,17 @@ class ZeroShardedAdamW:
         self.norm(stream=stream)
         self.update(stream=stream)
 
+    def set_hparams(self, lr=None, betas=None, eps=None, weight_decay=None, max_norm=None):
+        """Change the AdamW hyper-parameters or the clipping threshold for the steps that
+        follow, e.g. the learning rate of a warmup-and-decay schedule before each step.
+        Every step call hands them to the library when it is enqueued; the library checks
+        them there (an invalid value raises ZsInvalidArgument with nothing enqueued)."""
+        hp = self.hp
+        b1, b2 = (hp.beta1, hp.beta2) if betas is None else betas
+        self.hp = A.hparams(hp.lr if lr is None else lr, b1, b2, hp.eps if eps is None else eps,
+                            hp.weight_decay if weight_decay is None else weight_decay,
+                            hp.max_norm if max_norm is None else max_norm)
+
     def read_state(self, stream=None):
         return A.zs_state_read(self.state, stream).as_dict()
 
