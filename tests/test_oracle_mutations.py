@@ -180,3 +180,68 @@ def test_no_decay_mistakes_are_caught(monkeypatch, kind):
         return real(master, m, v, x, loss_scale, clip, t, hp, decay)
     _patch(monkeypatch, "adamw_update", wrong)
     assert _fails(P.test_no_decay_tensors_closed_form, P.test_no_decay_group_matches_torch_param_groups), kind
+
+
+ACCUMULATE_PINS = (P.test_accumulate_fp32_matches_exact_sums, P.test_accumulate_model_dtype_rounds_to_nearest_even,
+                   P.test_accumulate_then_step_equals_step_on_summed_gradient)
+
+
+@pytest.mark.parametrize("kind", ["overwrite", "subtract", "truncate", "sum_in_model_dtype_twice"])
+def test_accumulate_mistakes_are_caught(monkeypatch, kind):
+    real_pack = Z.pack
+
+    def wrong(acc, tensors, layout):
+        packed = real_pack(tensors, layout, acc.dtype)
+        if kind == "overwrite":
+            return packed
+        if kind == "subtract":
+            return (acc.double() - packed.double()).to(acc.dtype)
+        s = acc.double() + packed.double()
+        if kind == "truncate":  # round toward zero instead of to nearest even
+            f = s.to(acc.dtype)
+            over = (f.double().abs() > s.abs())
+            step = torch.nextafter(f, torch.zeros_like(f))
+            return torch.where(over, step, f)
+        # the sum rounded to the model dtype first, then to the buffer's (two roundings)
+        return s.to(torch.bfloat16).to(acc.dtype)
+    _patch(monkeypatch, "accumulate", wrong)
+    assert _fails(*ACCUMULATE_PINS), kind
+
+
+@pytest.mark.parametrize("kind", ["shifted", "ignores_shard_begin", "truncating_cast"])
+def test_unpack_mistakes_are_caught(monkeypatch, kind):
+    real_cast = Z.cast_to
+
+    def wrong(src, layout, tensors, whole_flat):
+        lo = 0 if (whole_flat or kind == "ignores_shard_begin") else layout.shard_begin
+        hi = lo + src.numel()
+        out = []
+        for t, off, n in zip(tensors, layout.offsets, layout.numels):
+            t = t.clone()
+            a, b = max(off, lo), min(off + n, hi)
+            if kind == "shifted":
+                a = min(a + 1, b)
+            if a < b:
+                x = src[a - lo:b - lo]
+                t.view(-1)[a - off:b - off] = x.to(t.dtype) if kind != "truncating_cast" else \
+                    (x.view(torch.int32) & ~0xFFFF).view(torch.float32).to(t.dtype) if x.dtype == torch.float32 \
+                    else real_cast(x, t.dtype)
+            out.append(t)
+        return out
+    _patch(monkeypatch, "unpack", wrong)
+    pins = [lambda: P.test_layout_pack_unpack_roundtrip(1, 2), lambda: P.test_layout_pack_unpack_roundtrip(8, 3),
+            P.test_dp_split_equals_single_rank_when_unclipped, P.test_unpack_rounds_each_shard_to_nearest_even]
+    assert _fails(*pins), kind
+
+
+@pytest.mark.parametrize("kind", ["off_by_one", "first_shard_always"])
+def test_shard_mistakes_are_caught(monkeypatch, kind):
+    def wrong(flat, layout):
+        b = 0 if kind == "first_shard_always" else layout.shard_begin + (1 if layout.shard_begin else 0)
+        out = flat[b:b + layout.shard_numel]
+        if out.numel() < layout.shard_numel:
+            out = torch.cat([out, torch.zeros(layout.shard_numel - out.numel(), dtype=flat.dtype)])
+        return out
+    _patch(monkeypatch, "shard_of", wrong)
+    assert _fails(lambda: P.test_layout_pack_unpack_roundtrip(1, 2), P.test_dp_split_equals_single_rank_when_unclipped,
+                  P.test_page_sharded_sgd_example_through_adamw_limit), kind

@@ -325,6 +325,25 @@ def test_layout_pack_unpack_roundtrip(align, dp_world):
     assert all(torch.equal(a, b) for a, b in zip(out2, tensors))
 
 
+def test_unpack_rounds_each_shard_to_nearest_even():
+    """The scatter-back of fp32 master shards into bf16 and fp16 tensors, by hand: every value
+    is rounded to nearest even (ties included), each rank writes only the elements of its own
+    shard, and the rest of each tensor keeps its old value."""
+    numels = [3, 5]
+    lay0, lay1 = O.plan_layout(numels, 2, 0), O.plan_layout(numels, 2, 1)  # shards [0, 4) and [4, 8)
+    t = 2 ** -8  # half a bf16 ulp at 1
+    master = _f32([1 + t, 1 + 3 * t, -(1 + t), 1 + t + 2 ** -20, 1 + 2 ** -11, 1 + 3 * 2 ** -11, 65519.0, 2.5])
+    old = [torch.full((3,), 9.0, dtype=torch.bfloat16), torch.full((5,), 9.0, dtype=torch.float16)]
+    out = O.unpack(master[:4], lay0, old, whole_flat=False)
+    assert out[0].float().tolist() == [1.0, 1 + 2 ** -6, -1.0]
+    # fp16 keeps 10 fraction bits: 1 + 2^-8 + 2^-20 is 4 ulps and a sliver above 1
+    assert out[1].float().tolist() == [1 + 2 ** -8, 9.0, 9.0, 9.0, 9.0]
+    out = O.unpack(master[4:], lay1, out, whole_flat=False)
+    assert out[0].float().tolist() == [1.0, 1 + 2 ** -6, -1.0]
+    # 1 + 2^-11 is a tie (to 1), 1 + 3 * 2^-11 rounds up to 1 + 2^-9, 65519 stays below the overflow at 65520
+    assert out[1].float().tolist() == [1 + 2 ** -8, 1.0, 1 + 2 ** -9, 65504.0, 2.5]
+
+
 def test_layout_rejects_bad_arguments():
     with pytest.raises(ValueError):
         O.plan_layout([4], 2, 2)
