@@ -245,3 +245,46 @@ def test_shard_mistakes_are_caught(monkeypatch, kind):
     _patch(monkeypatch, "shard_of", wrong)
     assert _fails(lambda: P.test_layout_pack_unpack_roundtrip(1, 2), P.test_dp_split_equals_single_rank_when_unclipped,
                   P.test_page_sharded_sgd_example_through_adamw_limit), kind
+
+
+@pytest.mark.parametrize("kind", ["gaps_not_zeroed", "offset_off_by_one", "rounds_on_widening"])
+def test_pack_mistakes_are_caught(monkeypatch, kind):
+    def wrong(tensors, layout, dtype=None):
+        if dtype is None:
+            dtype = tensors[0].dtype
+        flat = torch.full((layout.flat_numel,), 3.0, dtype=dtype) if kind == "gaps_not_zeroed" else \
+            torch.zeros(layout.flat_numel, dtype=dtype)
+        for t, off, n in zip(tensors, layout.offsets, layout.numels):
+            if n:
+                o = off + 1 if (kind == "offset_off_by_one" and off + n < layout.flat_numel) else off
+                x = t.reshape(-1)
+                if kind == "rounds_on_widening" and dtype == torch.float32:
+                    x = x.to(torch.float16)  # a lossy detour for bf16 sources
+                flat[o:o + n] = x.to(dtype)
+        return flat
+    _patch(monkeypatch, "pack", wrong)
+    pins = [lambda: P.test_layout_pack_unpack_roundtrip(8, 2), lambda: P.test_layout_pack_unpack_roundtrip(1, 3),
+            P.test_page_sharded_sgd_example_through_adamw_limit, P.test_pack_widening_to_fp32_is_exact]
+    assert _fails(*pins), kind
+
+
+@pytest.mark.parametrize("kind", ["whole_pack", "range_one_short"])
+def test_pack_bucket_mistakes_are_caught(monkeypatch, kind):
+    def wrong(flat, tensors, layout, tensor_begin, tensor_end, accumulate_into=False):
+        begin, end = Z.bucket_range(layout, tensor_begin, tensor_end)
+        if kind == "whole_pack":
+            begin, end = 0, layout.flat_numel
+        else:
+            end = max(begin, end - 1)
+        full = Z.accumulate(flat, tensors, layout) if accumulate_into else Z.pack(tensors, layout, flat.dtype)
+        out = flat.clone()
+        out[begin:end] = full[begin:end]
+        return out
+    _patch(monkeypatch, "pack_bucket", wrong)
+    assert _fails(lambda: P.test_buckets_in_any_order_rebuild_the_whole_pack(False),
+                  lambda: P.test_buckets_in_any_order_rebuild_the_whole_pack(True)), kind
+
+
+def test_global_sum_dropping_a_rank_is_caught(monkeypatch):
+    _patch(monkeypatch, "global_sumsq", lambda parts: sum(parts[1:]))
+    assert _fails(P.test_sumsq_special_cases_and_invariants)

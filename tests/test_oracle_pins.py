@@ -325,6 +325,18 @@ def test_layout_pack_unpack_roundtrip(align, dp_world):
     assert all(torch.equal(a, b) for a, b in zip(out2, tensors))
 
 
+def test_pack_widening_to_fp32_is_exact():
+    """Seeding the fp32 master widens bf16 and fp16 values exactly: bf16 shares fp32's
+    exponent range (values near 2^127 and subnormals down to 2^-133 survive), fp16's
+    largest and smallest values are far inside it."""
+    bf = [2.0 ** 100, -(2.0 ** -130), 3 * 2.0 ** -133, 1 + 2.0 ** -7, -1.5 * 2.0 ** 127, 0.0]
+    hf = [65504.0, -(2.0 ** -24), 1 + 2.0 ** -10, -3 * 2.0 ** -20]
+    lay = O.plan_layout([len(bf), len(hf)], 1, 0)
+    src = [torch.tensor(bf, dtype=torch.bfloat16), torch.tensor(hf, dtype=torch.float16)]
+    assert src[0].double().tolist() == bf and src[1].double().tolist() == hf  # the inputs are exact
+    assert O.pack(src, lay, torch.float32).double().tolist() == bf + hf
+
+
 def test_unpack_rounds_each_shard_to_nearest_even():
     """The scatter-back of fp32 master shards into bf16 and fp16 tensors, by hand: every value
     is rounded to nearest even (ties included), each rank writes only the elements of its own
