@@ -331,6 +331,26 @@ def test_cast_rounding_ties_on_gpu():
         Z.zs_layout_destroy(lay)
 
 
+def test_master_seeding_widens_extremes_exactly_on_gpu():
+    """The pack into fp32 (how the master is seeded) widens bf16 and fp16 extremes exactly:
+    values near 2^127, subnormals, signed zeros; the same bits as the oracle's pack."""
+    from harness import bits
+    Z = _z()
+    dev = torch.device("cuda", 0)
+    bf = [2.0 ** 100, -(2.0 ** -130), 3 * 2.0 ** -133, 1 + 2.0 ** -7, -1.5 * 2.0 ** 127, 0.0, -0.0, 2.0 ** -126]
+    hf = [65504.0, -(2.0 ** -24), 1 + 2.0 ** -10, -3 * 2.0 ** -20, -0.0, 2.0 ** -14]
+    for dt, vals in ((torch.bfloat16, bf), (torch.float16, hf)):
+        src = [torch.tensor(vals[:3], dtype=dt), torch.tensor(vals[3:], dtype=dt)]
+        lay = Z.zs_layout_create([3, len(vals) - 3], 1, 0)
+        olay = O.plan_layout([3, len(vals) - 3], 1, 0)
+        dsrc = [t.to(dev) for t in src]
+        out = torch.full((olay.flat_numel,), 7.0, dtype=torch.float32, device=dev)
+        Z.zs_pack(lay, Z.pointer_table(dsrc, dev), dt, out, torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(out.cpu()), bits(O.pack(src, olay, torch.float32))), dt
+        Z.zs_layout_destroy(lay)
+
+
 def test_overflow_forms_nan_inf_neg_inf_and_ext_flag():
     Z = _z()
     dev = torch.device("cuda", 0)
