@@ -89,3 +89,46 @@ def test_per_step_schedule_matches_the_oracle(name):
         opt.step(gen.make_grads(wl, steps + 1, ref.scaler.loss_scale, dev))
     assert opt.read_state()["step_t"] == ref.scaler.step_t  # the refused step enqueued nothing
     opt.close()
+
+
+@pytest.mark.parametrize("dtype,max_norm", [("bf16", 0.0), ("bf16", 1.0), ("fp16", 0.0), ("fp16", 1.0)])
+def test_extreme_gradient_values_match_the_oracle(dtype, max_norm):
+    """Gradients at the edges of the 2-byte formats: the largest finite value (for bf16 its
+    square overflows fp32, so v rounds to inf without clipping), subnormals (m and v become fp32
+    subnormals or underflow), signed zeros, and ordinary values beside them.  The update,
+    its fp32 roundings and the casts back must match the oracle bit for bit."""
+    import torch
+
+    import oracle as O
+    import zero_sharded_mixed_buffer_amd as Z
+    from harness import bits
+    Z.lib()
+    dev = torch.device("cuda", 0)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    big, tiny = (3.3895313892515355e38, 2.0 ** -133) if dt == torch.bfloat16 else (65504.0, 2.0 ** -24)
+    row = [big, -big, tiny, -tiny, 3 * tiny, 0.0, -0.0, 1.0, -0.5, 1e-3, 2.0 ** -20, 7.0]
+    numels = [5, 7]
+    hp = dict(HPARAMS, max_norm=max_norm)
+    params = [torch.tensor([0.5, -0.25, 1.0, 0.0, 3.0], dtype=dt, device=dev),
+              torch.tensor([2.0, -1.0, 0.125, 0.0, -0.0, 1e-3, 4.0], dtype=dt, device=dev)]
+    print(f"[case] extreme gradients {dtype} max_norm={max_norm}", flush=True)
+    opt = Z.ZeroShardedAdamW(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                             weight_decay=hp["weight_decay"], max_norm=max_norm, dynamic_loss_scale=False,
+                             init_scale=1.0)
+    ref = O.OracleRank(numels, 1, 0, [p.cpu() for p in params], O.OracleScaler(1.0, dynamic=False), hp)
+    for s in range(3):
+        vals = torch.tensor(row[s:] + row[:s], dtype=dt)  # rotate so every value meets every slot
+        grads = [vals[:5].clone().to(dev), vals[5:].clone().to(dev)]
+        opt.step(grads)
+        rec = ref.step(O.shard_of(O.pack([g.cpu() for g in grads], ref.layout), ref.layout))
+        st = opt.read_state()
+        assert st["overflow"] == int(rec["overflow"]) == 0 and st["step_t"] == s + 1
+        assert st["grad_norm"] == rec["norm"] or abs(st["grad_norm"] - rec["norm"]) <= 1e-12 * rec["norm"]
+    torch.cuda.synchronize()
+    for name, a, b in (("master", opt.master, ref.master), ("m", opt.m, ref.m), ("v", opt.v, ref.v)):
+        assert torch.equal(bits(a.cpu()), bits(b)), (name, a.cpu().tolist(), b.tolist())
+    for a, b in zip(opt.params, ref.params):
+        assert torch.equal(bits(a.cpu()), bits(b))
+    if max_norm == 0.0 and dt == torch.bfloat16:
+        assert torch.isinf(ref.v).any()  # the square of bf16's largest value overflows fp32
+    opt.close()
