@@ -91,12 +91,14 @@ def test_per_step_schedule_matches_the_oracle(name):
     opt.close()
 
 
-@pytest.mark.parametrize("dtype,max_norm", [("bf16", 0.0), ("bf16", 1.0), ("fp16", 0.0), ("fp16", 1.0)])
-def test_extreme_gradient_values_match_the_oracle(dtype, max_norm):
+@pytest.mark.parametrize("dtype,max_norm,offload", [("bf16", 0.0, False), ("bf16", 1.0, False), ("fp16", 0.0, False),
+                                                    ("fp16", 1.0, False), ("bf16", 0.0, True), ("fp16", 1.0, True)])
+def test_extreme_gradient_values_match_the_oracle(dtype, max_norm, offload):
     """Gradients at the edges of the 2-byte formats: the largest finite value (for bf16 its
     square overflows fp32, so v rounds to inf without clipping), subnormals (m and v become fp32
     subnormals or underflow), signed zeros, and ordinary values beside them.  The update,
-    its fp32 roundings and the casts back must match the oracle bit for bit."""
+    its fp32 roundings and the casts back must match the oracle bit for bit, on the device
+    and in the offloaded host update."""
     import torch
 
     import oracle as O
@@ -111,10 +113,10 @@ def test_extreme_gradient_values_match_the_oracle(dtype, max_norm):
     hp = dict(HPARAMS, max_norm=max_norm)
     params = [torch.tensor([0.5, -0.25, 1.0, 0.0, 3.0], dtype=dt, device=dev),
               torch.tensor([2.0, -1.0, 0.125, 0.0, -0.0, 1e-3, 4.0], dtype=dt, device=dev)]
-    print(f"[case] extreme gradients {dtype} max_norm={max_norm}", flush=True)
+    print(f"[case] extreme gradients {dtype} max_norm={max_norm} offload={offload}", flush=True)
     opt = Z.ZeroShardedAdamW(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
                              weight_decay=hp["weight_decay"], max_norm=max_norm, dynamic_loss_scale=False,
-                             init_scale=1.0)
+                             init_scale=1.0, offload=offload)
     ref = O.OracleRank(numels, 1, 0, [p.cpu() for p in params], O.OracleScaler(1.0, dynamic=False), hp)
     for s in range(3):
         vals = torch.tensor(row[s:] + row[:s], dtype=dt)  # rotate so every value meets every slot
