@@ -585,6 +585,38 @@ def test_gradient_accumulation_parity(name, accum):
     assert [i + 1 for i, f in enumerate(flags) if f] == [s for s in sorted(wl.faults) if s <= min(wl.steps, 6)]
 
 
+@pytest.mark.parametrize("accum", [None, torch.float32])
+def test_accumulation_that_overflows_skips_the_step(accum):
+    """Finite fp16 micro-step gradients whose sum leaves fp16's range: in a model-dtype buffer
+    the accumulated value rounds to inf, the step is skipped and the scale halves; in an
+    fp32 buffer the same sum stays finite and the step is applied.  Both against the oracle."""
+    from harness import bits
+    Z = _z()
+    dev = torch.device("cuda", 0)
+    numels = [6, 3]
+    params = [torch.tensor([0.5, -0.25, 1.0, 0.0, 3.0, 2.0], dtype=torch.float16, device=dev),
+              torch.tensor([1.0, -1.0, 0.125], dtype=torch.float16, device=dev)]
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_norm=1.0)
+    opt = Z.ZeroShardedAdamW(params, dynamic_loss_scale=True, init_scale=2.0 ** 16, accum_dtype=accum)
+    ref = O.OracleRank(numels, 1, 0, [p.cpu() for p in params], O.OracleScaler(2.0 ** 16), hp)
+    micro = [[torch.tensor([40000.0, 1.0, -3.0, 0.5, 2.0, 60000.0], dtype=torch.float16),
+              torch.tensor([7.0, -7.0, 1.0], dtype=torch.float16)],
+             [torch.tensor([40000.0, 2.0, 3.0, 0.5, -2.0, 10000.0], dtype=torch.float16),
+              torch.tensor([1.0, 1.0, 1.0], dtype=torch.float16)]]
+    opt.step([[t.to(dev) for t in m] for m in micro])
+    buf_dt = accum if accum is not None else torch.float16
+    acc = O.pack(micro[0], ref.layout, buf_dt)
+    acc = O.accumulate(acc, micro[1], ref.layout)
+    assert torch.equal(bits(opt.flat.cpu()), bits(acc))
+    rec = ref.step(O.shard_of(acc, ref.layout))
+    st = opt.read_state()
+    assert st["overflow"] == int(rec["overflow"]) and rec["overflow"] == (accum is None)
+    assert st["loss_scale"] == ref.scaler.loss_scale == (2.0 ** 15 if accum is None else 2.0 ** 16)
+    for a, b in ((opt.master, ref.master), (opt.m, ref.m), (opt.v, ref.v)):
+        assert torch.equal(bits(a.cpu()), bits(b))
+    opt.close()
+
+
 def test_step_captures_into_a_hip_graph():
     """The step enqueues kernels only (no host synchronisation, no allocation), so the whole
     single-rank step can be captured once and replayed.  Every replay is compared with the
