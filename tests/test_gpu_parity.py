@@ -76,6 +76,20 @@ def test_scale_growth_and_backoff_sequences(name, interval, fault_steps):
     assert any(b == a / 2 for a, b in zip(scales, scales[1:]))  # and did back off
 
 
+def test_scale_floor_holds_on_gpu():
+    """Overflows in a row from a loss scale of 2 reach the floor of 1 and stay there; growth
+    resumes after the window.  Scale, t, tracker and skips match the oracle each step."""
+    import dataclasses
+    from harness import run_parity
+    _z()
+    faults = {s: [(0, 1, float("inf"))] for s in (1, 2, 3, 6)}
+    wl = dataclasses.replace(WORKLOADS["tiny"], init_scale=2.0, growth_interval=2, steps=9, faults=faults)
+    rep = run_parity(wl)
+    scales = [s.scale_gpu for s in rep.steps]
+    print(f"[floor] scales={scales}", flush=True)
+    assert scales == [1.0, 1.0, 1.0, 1.0, 2.0, 1.0, 1.0, 2.0, 2.0]
+
+
 @pytest.mark.parametrize("rank", [0, 1, 2])
 def test_dp_virtual_ranks_every_rank(rank):
     from harness import run_parity
