@@ -290,3 +290,38 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     with pytest.raises(ImportError):
         Z.zs_host_adamw_step(torch.zeros(4, dtype=torch.bfloat16), torch.bfloat16, torch.zeros(4), torch.zeros(4),
                              torch.zeros(4), 4, Z.hparams(), Z.state_host())
+
+
+def test_error_messages_stay_with_their_thread():
+    """zs_last_error is per thread: a rejected call on one thread does not overwrite the
+    message another thread reads."""
+    import threading
+
+    import zero_sharded_mixed_buffer_amd as Z
+    msgs = {}
+    barrier = threading.Barrier(2)
+
+    def fail_with(tag, numels):
+        try:
+            Z.zs_plan(numels, 2, 5)  # dp_rank outside the group
+        except Z.ZsInvalidArgument:
+            pass
+        barrier.wait(timeout=30)
+        msgs[tag] = Z.zs_last_error()
+
+    def fail_other(tag):
+        try:
+            Z.zs_plan([4], 0, 0)  # dp_world < 1
+        except Z.ZsInvalidArgument:
+            pass
+        barrier.wait(timeout=30)
+        msgs[tag] = Z.zs_last_error()
+
+    t1 = threading.Thread(target=fail_with, args=("rank", [4, 4]))
+    t2 = threading.Thread(target=fail_other, args=("world",))
+    t1.start()
+    t2.start()
+    t1.join(timeout=60)
+    t2.join(timeout=60)
+    assert msgs["rank"] != msgs["world"], msgs
+    assert "rank" in msgs["rank"].lower() and "world" in msgs["world"].lower(), msgs
