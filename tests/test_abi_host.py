@@ -317,8 +317,8 @@ def test_error_messages_stay_with_their_thread():
         barrier.wait(timeout=30)
         msgs[tag] = Z.zs_last_error()
 
-    t1 = threading.Thread(target=fail_with, args=("rank", [4, 4]))
-    t2 = threading.Thread(target=fail_other, args=("world",))
+    t1 = threading.Thread(target=fail_with, args=("rank", [4, 4]), daemon=True)
+    t2 = threading.Thread(target=fail_other, args=("world",), daemon=True)
     t1.start()
     t2.start()
     t1.join(timeout=60)

@@ -50,7 +50,7 @@ def test_threads_with_their_own_optimizers_step_concurrently():
         except Exception as e:  # reported below; a thread cannot fail the test itself
             errors.append((name, repr(e)))
 
-    threads = [threading.Thread(target=work, args=(i, n, off)) for i, (n, off) in enumerate(jobs)]
+    threads = [threading.Thread(target=work, args=(i, n, off), daemon=True) for i, (n, off) in enumerate(jobs)]
     for t in threads:
         t.start()
     for t in threads:
