@@ -29,8 +29,12 @@ design notes of the repository.
 
 Parity status of each function: every function below is pinned by a CPU test
 against values fixed by the pages or by mathematics (worked example, closed
-forms, brute force, exhaustive bit-pattern sweeps, library routines); none is
-"parity unpinned".
+forms, brute force, exhaustive bit-pattern sweeps, library routines).  The
+wiring of the stages in OracleRank.step (a global norm over every rank's
+partial, taken on the unscaled gradient, whose clip coefficient and unscale
+reach the update) is pinned end to end against torch.nn.utils.clip_grad_norm_
+followed by torch.optim.AdamW, at one rank and at two ranks sharing one flat
+buffer, with clipping active and a loss scale of 2^12.
 """
 
 from __future__ import annotations

@@ -288,3 +288,47 @@ def test_pack_bucket_mistakes_are_caught(monkeypatch, kind):
 def test_global_sum_dropping_a_rank_is_caught(monkeypatch):
     _patch(monkeypatch, "global_sumsq", lambda parts: sum(parts[1:]))
     assert _fails(P.test_sumsq_special_cases_and_invariants)
+
+
+def _rank_step_variant(kind):
+    """OracleRank.step with one wiring mistake: the norm from this rank's own partial only
+    (local_norm), the norm of the still-scaled gradient (scaled_norm), the clip coefficient
+    left out of the update (clip_dropped), the update fed the scaled gradient
+    (update_not_unscaled), or the bias correction stuck at t = 1 (t_stuck_at_one)."""
+    def step(self, shard_x, ext_overflow=False, other_sumsq=None):
+        lay = self.layout
+        overflow = Z.nonfinite_any(shard_x) or bool(ext_overflow)
+        rec = dict(overflow=overflow, loss_scale=self.scaler.loss_scale, local_sumsq=None, sumsq=None, norm=None,
+                   clip=None)
+        if not overflow:
+            scale = self.scaler.loss_scale
+            local = Z.sumsq_unscaled(shard_x, 1.0 if kind == "scaled_norm" else scale)
+            if kind == "local_norm" or lay.dp_world == 1:
+                ss = local
+            else:
+                ss = Z.global_sumsq([local if q == lay.dp_rank else other_sumsq[q] for q in range(lay.dp_world)])
+            norm, c = Z.clip_coefficient(ss, self.hp["max_norm"])
+            t = 1 if kind == "t_stuck_at_one" else self.scaler.step_t + 1
+            self.master, self.m, self.v = Z.adamw_update(
+                self.master, self.m, self.v, shard_x, 1.0 if kind == "update_not_unscaled" else scale,
+                1.0 if kind == "clip_dropped" else c, t, self.hp, self.decay)
+            self.params = Z.unpack(self.master, lay, self.params, whole_flat=False)
+            rec.update(local_sumsq=local, sumsq=ss, norm=norm, clip=c)
+        self.scaler = Z.scaler_update(self.scaler, overflow)
+        return rec
+    return step
+
+
+@pytest.mark.parametrize("kind", ["local_norm", "scaled_norm", "clip_dropped", "update_not_unscaled",
+                                  "t_stuck_at_one"])
+def test_rank_step_wiring_mistakes_are_caught(monkeypatch, kind):
+    monkeypatch.setattr(Z.OracleRank, "step", _rank_step_variant(kind))
+    assert _fails(lambda: P.test_rank_step_matches_torch_clip_and_adamw(0),
+                  P.test_two_ranks_exchanging_partials_match_one_torch_run), kind
+
+
+def test_rank_step_variant_without_mistake_passes(monkeypatch):
+    # the mistake-free rewrite passes every pin, so each failure above is the planted mistake's
+    monkeypatch.setattr(Z.OracleRank, "step", _rank_step_variant("none"))
+    assert not _fails(lambda: P.test_rank_step_matches_torch_clip_and_adamw(0),
+                      P.test_two_ranks_exchanging_partials_match_one_torch_run)

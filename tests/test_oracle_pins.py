@@ -459,6 +459,104 @@ def test_dp_split_equals_single_rank_when_unclipped():
 
 
 # ------------------------------------------------------------------------------------------
+# The whole rank step, end to end, against torch: a loss-scaled fp16 list whose global norm
+# is large enough to clip, through torch.nn.utils.clip_grad_norm_ over every tensor and then
+# torch.optim.AdamW ("3.7 Megatron-LM, DeepSpeed & Parallelism in Practice", sections
+# "DeepSpeed config for this run": gradient_clipping 1.0, and "Initializing a DeepSpeed
+# Engine": torch.optim.AdamW), for one rank and for two ranks that own equal halves of one
+# flat buffer and exchange their partial sums ("Deep dive: Megatron", section "Distributed
+# optimizer").  This pins the wiring of OracleRank.step: the norm is global, taken on the
+# unscaled gradient, and its clip coefficient and the unscale both reach the update.
+# ------------------------------------------------------------------------------------------
+
+STEP_NUMELS = [300, 77, 1024, 5, 640, 1]   # 2047 elements: two ranks split tensor 2
+STEP_SCALE = 2.0 ** 12
+STEP_HP = dict(HP, weight_decay=0.1)
+
+
+def _step_inputs(seed, steps):
+    """fp16 parameters N(0, 0.02) and `steps` lists of fp16 gradients N(0, 0.1) times the
+    loss scale: the unscaled norm is about 4.5, so the clip coefficient is about 0.22."""
+    gen = torch.Generator().manual_seed(seed)
+    params = [(torch.randn(n, generator=gen) * 0.02).to(torch.float16) for n in STEP_NUMELS]
+    grads = [[(torch.randn(n, generator=gen) * 0.1 * STEP_SCALE).to(torch.float16) for n in STEP_NUMELS]
+             for _ in range(steps)]
+    return params, grads
+
+
+def _torch_clip_adamw_step(masters, ms, vs, grads_unscaled, t, hp):
+    """clip_grad_norm_ over every tensor, then one torch.optim.AdamW step, all in fp64, from
+    the given fp32 state at step count t - 1.  Returns (norm, params, m, v) as lists."""
+    prms = [torch.nn.Parameter(p.double().clone()) for p in masters]
+    opt = torch.optim.AdamW(prms, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                            weight_decay=hp["weight_decay"], foreach=False)
+    for prm, m, v, g in zip(prms, ms, vs, grads_unscaled):
+        prm.grad = g.double().clone()
+        opt.state[prm] = {"step": torch.tensor(float(t - 1)), "exp_avg": m.double().clone(),
+                          "exp_avg_sq": v.double().clone()}
+    norm = float(torch.nn.utils.clip_grad_norm_(prms, hp["max_norm"]))
+    opt.step()
+    return (norm, [p.detach() for p in prms], [opt.state[p]["exp_avg"] for p in prms],
+            [opt.state[p]["exp_avg_sq"] for p in prms])
+
+
+def _split(flat, offsets, numels):
+    return [flat[o:o + n] for o, n in zip(offsets, numels)]
+
+
+def _assert_step_within_torch_bounds(master, m, v, p_ref, m_ref, v_ref, t, hp):
+    """The bounds of the single-tensor AdamW pin: moments within one fp32 ulp of torch's
+    fp64 moments, parameters within half an ulp plus what torch's unrounded moments move."""
+    for a, b in ((m, m_ref), (v, v_ref)):
+        assert torch.all((a.double() - b).abs() <= b.abs().mul(2.0 ** -23)), t
+    ratio = (m_ref / (1 - hp["beta1"] ** t)).abs() / ((v_ref / (1 - hp["beta2"] ** t)).sqrt() + hp["eps"])
+    bound = p_ref.abs().mul(2.0 ** -24) + hp["lr"] * 2.0 ** -23 * ratio + 1e-30
+    assert torch.all((master.double() - p_ref).abs() <= bound), t
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_rank_step_matches_torch_clip_and_adamw(seed):
+    params, steps = _step_inputs(seed, 5)
+    rank = O.OracleRank(STEP_NUMELS, 1, 0, params, O.OracleScaler(STEP_SCALE), STEP_HP)
+    offs = rank.layout.offsets
+    for t, grads in enumerate(steps, start=1):
+        before = [_split(x, offs, STEP_NUMELS) for x in (rank.master, rank.m, rank.v)]
+        rec = rank.step(O.shard_of(O.pack(grads, rank.layout), rank.layout))
+        unscaled = [g.double() / STEP_SCALE for g in grads]
+        norm, p_ref, m_ref, v_ref = _torch_clip_adamw_step(*before, unscaled, t, STEP_HP)
+        assert not rec["overflow"] and rec["loss_scale"] == STEP_SCALE
+        assert abs(rec["norm"] - norm) <= 1e-13 * norm
+        assert rec["clip"] <= 0.5 and abs(rec["clip"] - STEP_HP["max_norm"] / (norm + 1e-6)) <= 1e-14
+        _assert_step_within_torch_bounds(rank.master, rank.m, rank.v, torch.cat(p_ref), torch.cat(m_ref),
+                                         torch.cat(v_ref), t, STEP_HP)
+        assert rank.scaler.step_t == t
+
+
+def test_two_ranks_exchanging_partials_match_one_torch_run():
+    params, steps = _step_inputs(2, 5)
+    d = 2
+    ranks = [O.OracleRank(STEP_NUMELS, d, r, params, O.OracleScaler(STEP_SCALE), STEP_HP) for r in range(d)]
+    lay = ranks[0].layout
+    n_real = sum(STEP_NUMELS)
+    assert lay.offsets[2] < lay.shard_numel < lay.offsets[3]   # tensor 2 straddles the ranks
+    for t, grads in enumerate(steps, start=1):
+        whole = [torch.cat([getattr(r, k) for r in ranks])[:n_real] for k in ("master", "m", "v")]
+        before = [_split(x, lay.offsets, STEP_NUMELS) for x in whole]
+        flat = O.pack(grads, lay)
+        shards = [O.shard_of(flat, r.layout) for r in ranks]
+        parts = [O.sumsq_unscaled(s, STEP_SCALE) for s in shards]
+        recs = [r.step(s, other_sumsq=parts) for r, s in zip(ranks, shards)]
+        unscaled = [g.double() / STEP_SCALE for g in grads]
+        norm, p_ref, m_ref, v_ref = _torch_clip_adamw_step(*before, unscaled, t, STEP_HP)
+        for rec in recs:
+            assert abs(rec["norm"] - norm) <= 1e-13 * norm and rec["clip"] <= 0.5
+        assert recs[0]["clip"] == recs[1]["clip"]
+        after = [torch.cat([getattr(r, k) for r in ranks])[:n_real] for k in ("master", "m", "v")]
+        _assert_step_within_torch_bounds(*after, torch.cat(p_ref), torch.cat(m_ref), torch.cat(v_ref), t,
+                                         STEP_HP)
+
+
+# ------------------------------------------------------------------------------------------
 # Gradient accumulation into the flat buffer (the step before the path)
 # ------------------------------------------------------------------------------------------
 
