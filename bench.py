@@ -174,28 +174,35 @@ def measured_traffic(workload, kernel="k_adamw"):
     return summary["kernels"][kernel]["traffic_bytes"]
 
 
-def ceilings(torch, gib=4, reps=5):
-    """Practical HBM yardsticks on the same GPU: torch's device-to-device copy (read + write
-    of `gib` GiB each) and a triad a = b + 2c over three `gib` GiB fp32 buffers."""
-    n = gib * (1 << 30) // 4
-    a = torch.empty(n, dtype=torch.float32, device="cuda")
-    b = torch.ones(n, dtype=torch.float32, device="cuda")
-    c = torch.ones(n, dtype=torch.float32, device="cuda")
+def ceilings(torch, Z, opt, stream, reps=5):
+    """Measured HBM yardsticks on the step's own buffers (same placement in HBM), with the
+    library's probe kernels (include/zs_probe.h): the update kernel's launch shape and
+    access pattern with no arithmetic.  mix_4r4w reads the flat gradient shard (2 B) and
+    master, m, v (12 B) and writes master, m, v (12 B) and a parameter-sized buffer (2 B):
+    the 28 B per element of the update; copy is master -> m (one-to-one), read is master,
+    write is m.  They overwrite master, m and v, so they run after the timed steps."""
+    S = opt.shard_numel
+    n = S // 4096 * 4096
+    nb = n * 4 // 16384 * 16384
+    out = torch.empty(n, dtype=opt.param_dtype, device=opt.device)
+    sink = torch.zeros(1, dtype=torch.int32, device=opt.device)
+    g = opt.shard
+    cases = (("mix_4r4w", lambda: Z.zs_probe_mix(g, opt.master, opt.m, opt.v, out, n, stream), 28 * n),
+             ("copy", lambda: Z.zs_probe_copy(opt.master, opt.m, nb, stream), 2 * nb),
+             ("read", lambda: Z.zs_probe_read(opt.master, nb, sink, stream), nb),
+             ("write", lambda: Z.zs_probe_write(opt.m, nb, stream), nb))
     res = {}
-    for name, fn, nbytes in (("copy", lambda: a.copy_(b), 2 * 4 * n),
-                             ("triad", lambda: torch.add(b, c, alpha=2.0, out=a), 3 * 4 * n)):
+    for name, fn, nbytes in cases:
         fn()
-        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        e0.record(stream)
         for _ in range(reps):
             fn()
-        e1.record()
+        e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
         res[name] = {"gbps": nbytes / (ms * 1e-3) / 1e9, "ms": ms, "bytes": nbytes}
-    del a, b, c
-    torch.cuda.empty_cache()
+    del out, sink
     return res
 
 
@@ -235,7 +242,8 @@ def main():
                     help="also time the single-rank step captured once in a HIP graph and replayed, against the "
                          "same step issued call by call (launch-bound small lists)")
     ap.add_argument("--no-ceilings", dest="ceilings", action="store_false",
-                    help="skip timing a device-to-device copy and a triad (torch kernels) as bandwidth yardsticks")
+                    help="skip timing the probe kernels (the update's 4-read/4-write mix, copy, read, write) on the "
+                         "step's buffers as bandwidth yardsticks")
     ap.add_argument("--ceilings", dest="ceilings", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -499,12 +507,16 @@ def main():
                 f"elems/s={S / (e0.elapsed_time(e1) * 1e-3):.4g}")
     out["memory"] = {"max_allocated_gb": torch.cuda.max_memory_allocated() / 1e9,
                      "device_total_gb": torch.cuda.get_device_properties(0).total_memory / 1e9}
+    if args.ceilings:  # on the step's own buffers, which it overwrites: after every timed step
+        out["ceilings"] = ceilings(torch, Z, opt, stream)
+        mix = out["ceilings"]["mix_4r4w"]["gbps"]
+        out["roofline"]["ceiling_mix_4r4w_gbps"] = mix
+        out["roofline"]["frac_of_measured_ceiling"] = adamw_gbps / mix
+        log(f"ceilings: " + ", ".join(f"{k} {v['gbps']:.0f} GB/s" for k, v in out["ceilings"].items()) +
+            f"; adamw at {adamw_gbps / mix:.3f} of the 4R/4W mix")
     opt.close()
     del params, grads, opt
     torch.cuda.empty_cache()
-    if args.ceilings:
-        out["ceilings"] = ceilings(torch)
-        log(f"ceilings: {out['ceilings']}")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_baseline_elems, args.cpu_baseline_steps)

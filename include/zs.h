@@ -34,8 +34,8 @@
  *   - `stream` is a hipStream_t (NULL = the null stream). Every device step call only
  *     enqueues kernels on it and never synchronises the host; results live in device
  *     memory. The calls that synchronise are zs_state_read and zs_state_write (their
- *     stream), zs_offload_adamw_step (its stream: the host needs the step's scalars) and
- *     zs_layout_set_no_decay (the device, at set-up).
+ *     stream) and zs_offload_adamw_step (its stream: the host needs the step's scalars);
+ *     none synchronises the whole device.
  *   - Flat buffers, shard-sized fp32 arrays and flat parameter outputs must be 16-byte
  *     aligned (any PyTorch allocation is); a shard view into a flat buffer may start at
  *     any element.
@@ -142,11 +142,15 @@ zs_status zs_layout_info(const zs_layout* layout, int64_t* flat_numel, int64_t* 
  * carry their own weight_decay).  no_decay: host array of n_tensors flags (non-zero: that
  * tensor's elements update with a decay multiplier of exactly 1), or NULL to make every
  * tensor decay again (the default).  Applies to zs_adamw_step and zs_offload_adamw_step
- * on this layout.  Synchronises the device (work in flight may still read the previous
- * table), so call it at set-up, not between the calls of a step.
+ * calls made on this layout after it returns.  The new table is uploaded on `stream`
+ * without waiting for anything: device steps enqueued later on `stream` use it, steps on
+ * another stream must be ordered after `stream` by the caller.  Work enqueued before the
+ * call keeps reading the previous table, which the library keeps until
+ * zs_layout_destroy (a few bytes per segment), so no wait for it is needed.  Not to be
+ * called while another thread uses the layout.
  * Errors: ZS_EINVAL on a NULL layout or n_tensors different from the layout's;
- * ZS_ENOMEM / ZS_EHIP from the upload. */
-zs_status zs_layout_set_no_decay(zs_layout* layout, const uint8_t* no_decay, int32_t n_tensors);
+ * ZS_ENOMEM / ZS_EHIP from the upload (the previous table then stays in force). */
+zs_status zs_layout_set_no_decay(zs_layout* layout, const uint8_t* no_decay, int32_t n_tensors, void* stream);
 
 /* Device state for one rank (scaler, step count, flag, norm results) and the workspace of
  * the norm reduction, on the layout's device.  `init` gives the starting zs_state_host

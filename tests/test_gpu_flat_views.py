@@ -291,3 +291,20 @@ def test_step_flat_replays_in_a_hip_graph():
     assert gopt.read_state()["skipped_total"] == 1 and gopt.read_state()["step_t"] == 5
     gopt.close()
     eopt.close()
+
+
+def test_flat_views_with_several_ranks_need_align_8():
+    """Each rank writes its slice of the parameter buffer with 16-byte stores, so with several
+    ranks the slices must start on 16-byte boundaries: align 1 with an odd-sized list is
+    refused; align 8 gives every rank an aligned slice."""
+    Z = _z()
+    dev = torch.device("cuda", 0)
+    sizes = (5, 3, 9)  # 17 elements: shards of 9 at align 1
+    with pytest.raises(ValueError, match="multiple of 8"):
+        Z.ZeroShardedAdamW([torch.zeros(n, dtype=torch.bfloat16, device=dev) for n in sizes], dp_world=2,
+                           dp_rank=1, flat_views=True)
+    for r in range(2):
+        opt = Z.ZeroShardedAdamW([torch.zeros(n, dtype=torch.bfloat16, device=dev) for n in sizes], dp_world=2,
+                                 dp_rank=r, align=8, flat_views=True)
+        assert opt.param_shard.data_ptr() % 16 == 0 and opt.shard_numel % 8 == 0
+        opt.close()

@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
     ("qwen3_0.6b_dp2", 10),
     ("moe_3.4b_dp4", 10),
     ("ragged_20k", 20),
-    ("llama3_8b", 4),
+    ("llama3_8b", 10),
 ])
 def test_fullsize_sampled_parity(name, steps):
     import zero_sharded_mixed_buffer_amd as Z

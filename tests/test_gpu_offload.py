@@ -172,3 +172,84 @@ def test_every_variant_together():
             Z.zs_state_destroy(sq)
             Z.zs_layout_destroy(lq)
         opt.close()
+
+
+@pytest.mark.parametrize("with_out", [False, True])
+def test_offload_first_step_skipped_keeps_parameter_shard_valid(with_out):
+    """Rank 1 of 2, fp16 at the initial scale 2^16, step 1 overflowing on the other rank.
+    The flat parameter shard (the all-gather input) holds the rank's parameters from the
+    start; the skip writes neither it nor a caller's flat_param_out; the applied step 2
+    writes the cast of the new master into whichever of the two the update targets and
+    scatters it, as the device update does."""
+    import oracle as O
+    from harness import bits
+    Z = _z()
+    wl = WORKLOADS["tiny"]
+    dev = torch.device("cuda", 0)
+    hp = wl.hparams
+    params = gen.make_params(wl, dev)
+    opt = Z.ZeroShardedAdamW(params, lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                             weight_decay=hp["weight_decay"], max_norm=hp["max_norm"], dp_world=2, dp_rank=1,
+                             dynamic_loss_scale=True, init_scale=2.0 ** 16, offload=True, offload_chunk=10_000)
+    lay = O.plan_layout(wl.numels, 2, 1)
+    S = lay.shard_numel
+    p0 = [p.cpu() for p in params]
+    torch.cuda.synchronize()
+    assert torch.equal(bits(opt.flat_param.cpu()), bits(O.shard_of(O.pack(p0, lay), lay)))
+    out = torch.full((S,), 7.0, dtype=torch.float16, device=dev) if with_out else None
+    ext = torch.ones(1, dtype=torch.int32, device=dev)
+    exch = torch.zeros(2, dtype=torch.float64, device=dev)
+    print(f"[case] offload first-step skip, dp 2 rank 1, flat_param_out={with_out}", flush=True)
+
+    def step(k, scale):
+        opt.pack(gen.make_grads(wl, k, scale, dev, with_faults=False))
+        opt.check(ext_overflow=ext, local_sumsq_out=exch[1:2])
+        opt.norm(rank_sumsq=exch)
+        opt.update(flat_param_out=out)
+        torch.cuda.synchronize()
+
+    step(1, 2.0 ** 16)
+    st = opt.read_state()
+    assert st["skipped_total"] == 1 and st["step_t"] == 0 and st["loss_scale"] == 2.0 ** 15
+    assert torch.equal(bits(opt.flat_param.cpu()), bits(O.shard_of(O.pack(p0, lay), lay)))
+    if with_out:
+        assert bool((out == 7.0).all())
+    assert all(torch.equal(bits(a.cpu()), bits(b)) for a, b in zip(params, p0))
+    ext.zero_()
+    step(2, 2.0 ** 15)
+    st = opt.read_state()
+    assert st["skipped_total"] == 1 and st["step_t"] == 1
+    dest = out if with_out else opt.flat_param
+    assert torch.equal(bits(dest.cpu()), bits(O.cast_to(opt.master, torch.float16)))
+    want = O.unpack(opt.master, lay, p0, False)
+    assert all(torch.equal(bits(a.cpu()), bits(b)) for a, b in zip(params, want))
+    opt.close()
+
+
+def test_caller_tensors_are_checked_before_any_launch():
+    """Tensors handed to check / norm / update that a kernel would misread (another dtype) or
+    overrun (too few elements) are refused with nothing enqueued."""
+    Z = _z()
+    wl = WORKLOADS["qwen_mini_dp2"]
+    dev = torch.device("cuda", 0)
+    for offload in (False, True):
+        opt = Z.ZeroShardedAdamW(gen.make_params(wl, dev), dp_world=2, dp_rank=1, offload=offload,
+                                 offload_chunk=1 << 16)
+        S = opt.shard_numel
+        bad_calls = [
+            lambda: opt.check(ext_overflow=torch.zeros(1, dtype=torch.bool, device=dev)),
+            lambda: opt.check(ext_overflow=torch.zeros(1, dtype=torch.int32)),
+            lambda: opt.check(local_sumsq_out=torch.zeros(1, dtype=torch.float32, device=dev)),
+            lambda: opt.norm(rank_sumsq=torch.zeros(2, dtype=torch.float32, device=dev)),
+            lambda: opt.norm(rank_sumsq=torch.zeros(1, dtype=torch.float64, device=dev)),
+            lambda: opt.update(flat_param_out=torch.zeros(S - 1, dtype=torch.bfloat16, device=dev)),
+            lambda: opt.update(flat_param_out=torch.zeros(S, dtype=torch.float32, device=dev)),
+            lambda: opt.update(flat_param_out=torch.zeros(2 * S, dtype=torch.bfloat16, device=dev)[::2]),
+        ]
+        for i, call in enumerate(bad_calls):
+            with pytest.raises(ValueError):
+                call()
+        torch.cuda.synchronize()
+        st = opt.read_state()
+        assert st["step_t"] == 0 and st["skipped_total"] == 0  # nothing was committed
+        opt.close()

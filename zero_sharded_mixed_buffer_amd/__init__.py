@@ -34,6 +34,10 @@ from ._abi import (  # noqa: F401
     zs_plan_buckets,
     zs_plan,
     zs_plan_segments,
+    zs_probe_copy,
+    zs_probe_mix,
+    zs_probe_read,
+    zs_probe_write,
     zs_scaler_update,
     zs_step,
     zs_step_flat,

@@ -67,7 +67,7 @@ _SIGS = {
     "zs_pack": [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p],
     "zs_pack_accumulate": [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p],
     "zs_plan_buckets": [c_void_p, c_int32, c_int64, c_void_p, c_void_p],
-    "zs_layout_set_no_decay": [c_void_p, c_void_p, c_int32],
+    "zs_layout_set_no_decay": [c_void_p, c_void_p, c_int32, c_void_p],
     "zs_bucket_range": [c_void_p, c_int32, c_int32, c_void_p, c_void_p],
     "zs_pack_bucket": [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p],
     "zs_unscale_check": [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p],
@@ -82,6 +82,10 @@ _SIGS = {
                      c_void_p, c_int32, c_void_p],
     "zs_host_adamw_step": [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_int64, POINTER(AdamwHParams),
                            POINTER(StateHost), c_void_p, c_int32, c_int32],
+    "zs_probe_mix": [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_void_p],
+    "zs_probe_copy": [c_void_p, c_void_p, c_int64, c_void_p],
+    "zs_probe_read": [c_void_p, c_int64, c_void_p, c_void_p],
+    "zs_probe_write": [c_void_p, c_int64, c_void_p],
     "zs_offload_adamw_step": [c_void_p, c_void_p, c_int32, c_void_p, POINTER(AdamwHParams), c_void_p, c_void_p,
                               c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_int32, c_int32, c_void_p],
 }
@@ -220,13 +224,15 @@ def zs_bucket_range(layout, tensor_begin, tensor_end):
     return b.value, e.value
 
 
-def zs_layout_set_no_decay(layout, no_decay):
-    """Per-tensor no-decay flags (a sequence of bools, one per tensor), or None to clear."""
+def zs_layout_set_no_decay(layout, no_decay, stream=None):
+    """Per-tensor no-decay flags (a sequence of bools, one per tensor), or None to clear; the
+    table is uploaded on `stream` and applies to the steps enqueued after it there."""
     if no_decay is None:
-        _check(lib().zs_layout_set_no_decay(layout, None, 0), "zs_layout_set_no_decay")
+        _check(lib().zs_layout_set_no_decay(layout, None, 0, _stream(stream)), "zs_layout_set_no_decay")
         return
     flags = (ctypes.c_uint8 * max(len(no_decay), 1))(*[1 if f else 0 for f in no_decay])
-    _check(lib().zs_layout_set_no_decay(layout, ctypes.addressof(flags), len(no_decay)), "zs_layout_set_no_decay")
+    _check(lib().zs_layout_set_no_decay(layout, ctypes.addressof(flags), len(no_decay), _stream(stream)),
+           "zs_layout_set_no_decay")
 
 
 def zs_layout_info(layout):
@@ -373,3 +379,28 @@ def zs_offload_adamw_step(layout, shard, grad_dtype, state, hp: AdamwHParams, ma
                                        int(chunk_numel), _dptr(flat_param_out, "flat_param_out", W),
                                        dtype_code(param_dtype), int(n_threads), _stream(stream)),
            "zs_offload_adamw_step")
+
+
+# ---------------------------------------------------------------------------- bandwidth yardsticks
+# (include/zs_probe.h: the update's access patterns without its arithmetic; they overwrite the
+# buffers they are given)
+
+def zs_probe_mix(g, p, m, v, out, n, stream=None):
+    w = "zs_probe_mix"
+    _check(lib().zs_probe_mix(_dptr(g, "g", w), _dptr(p, "p", w), _dptr(m, "m", w), _dptr(v, "v", w),
+                              _dptr(out, "out", w), int(n), _stream(stream)), w)
+
+
+def zs_probe_copy(src, dst, nbytes, stream=None):
+    w = "zs_probe_copy"
+    _check(lib().zs_probe_copy(_dptr(src, "src", w), _dptr(dst, "dst", w), int(nbytes), _stream(stream)), w)
+
+
+def zs_probe_read(src, nbytes, sink, stream=None):
+    w = "zs_probe_read"
+    _check(lib().zs_probe_read(_dptr(src, "src", w), int(nbytes), _dptr(sink, "sink", w), _stream(stream)), w)
+
+
+def zs_probe_write(dst, nbytes, stream=None):
+    w = "zs_probe_write"
+    _check(lib().zs_probe_write(_dptr(dst, "dst", w), int(nbytes), _stream(stream)), w)

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libzs.so")
 
-SOURCES = ["zs_abi.cpp", "zs_kernels.hip"]
+SOURCES = ["zs_abi.cpp", "zs_kernels.hip", "zs_probe.hip"]
 HOST_SOURCES = ["zs_host.cpp", "zs_plan.cpp"]  # plain C++ (host step, planner), built by the host compiler
 HEADERS = ["zs_internal.h", "zs_host.h", "zs_plan.h"]
 

@@ -16,6 +16,7 @@
 
 #include "zs.h"
 #include "zs_host.h"
+#include "zs_probe.h"
 #include "zs_internal.h"
 #include "zs_plan.h"
 
@@ -161,6 +162,10 @@ struct zs_layout {
   int64_t nparts = 0;  // partial-sum slots: workgroups of the largest pack / check pass
   void* mem_nodecay = nullptr;         // per-segment no-decay flags of the shard map, or null
   std::vector<int64_t> nodecay_runs;   // the same as shard-relative [begin, end) pairs
+  // Tables replaced by zs_layout_set_no_decay: work enqueued before the replacement may
+  // still read them, so they (and the host copies their uploads read) live until destroy.
+  std::vector<void*> retired_tables;
+  std::vector<std::vector<uint8_t>> upload_sources;
 };
 
 struct zs_state {
@@ -285,49 +290,55 @@ extern "C" void zs_layout_destroy(zs_layout* l) {
   if (l->mem_shard) (void)hipFree(l->mem_shard);
   if (l->mem_full) (void)hipFree(l->mem_full);
   if (l->mem_nodecay) (void)hipFree(l->mem_nodecay);
+  for (void* t : l->retired_tables) (void)hipFree(t);
   delete l;
 }
 
-extern "C" zs_status zs_layout_set_no_decay(zs_layout* l, const uint8_t* no_decay, int32_t n_tensors) {
+extern "C" zs_status zs_layout_set_no_decay(zs_layout* l, const uint8_t* no_decay, int32_t n_tensors,
+                                            void* stream) {
+  const TraceRange trace("zs_layout_set_no_decay");
   zs_status st = check_layout(l);
   if (st != ZS_OK) return st;
   const int32_t n = static_cast<int32_t>(l->plan.numels.size());
   if (no_decay != nullptr && n_tensors != n)
     return fail(ZS_EINVAL, "no_decay has %d flags for %d tensors", n_tensors, n);
-  // work already enqueued may still read the previous table
-  hipError_t e = hipDeviceSynchronize();
-  if (e != hipSuccess) return hip_fail(e, "synchronising before replacing the no-decay table");
-  if (l->mem_nodecay) (void)hipFree(l->mem_nodecay);
-  l->mem_nodecay = nullptr;
-  l->map_shard.seg_nodecay = nullptr;
-  if (l->plan.dp_world == 1) l->map_full.seg_nodecay = nullptr;
-  l->nodecay_runs.clear();
-  if (no_decay == nullptr) return ok();
-  const HostMap m = build_map(l->plan, l->plan.shard_begin, l->plan.shard_numel);
-  const size_t nseg = m.seg_tensor.size();
-  std::vector<uint8_t> flags(std::max<size_t>(nseg, 1), 0);
-  for (size_t s = 0; s < nseg; ++s) {
-    const int32_t t = m.seg_tensor[s];
-    if (t < 0 || no_decay[t] == 0) continue;
-    flags[s] = 1;
-    if (!l->nodecay_runs.empty() && l->nodecay_runs.back() == m.seg_begin[s]) {
-      l->nodecay_runs.back() = m.seg_begin[s + 1];  // adjacent runs merge
-    } else {
-      l->nodecay_runs.push_back(m.seg_begin[s]);
-      l->nodecay_runs.push_back(m.seg_begin[s + 1]);
+  // Build the new table on the host first, so that a failure leaves the old one in force.
+  std::vector<int64_t> runs;
+  std::vector<uint8_t> flags;
+  if (no_decay != nullptr) {
+    const HostMap m = build_map(l->plan, l->plan.shard_begin, l->plan.shard_numel);
+    const size_t nseg = m.seg_tensor.size();
+    flags.assign(std::max<size_t>(nseg, 1), 0);
+    for (size_t s = 0; s < nseg; ++s) {
+      const int32_t t = m.seg_tensor[s];
+      if (t < 0 || no_decay[t] == 0) continue;
+      flags[s] = 1;
+      if (!runs.empty() && runs.back() == m.seg_begin[s]) {
+        runs.back() = m.seg_begin[s + 1];  // adjacent runs merge
+      } else {
+        runs.push_back(m.seg_begin[s]);
+        runs.push_back(m.seg_begin[s + 1]);
+      }
     }
   }
-  if (l->nodecay_runs.empty()) return ok();  // every element of this shard decays
   void* d = nullptr;
-  e = hipMalloc(&d, flags.size());
-  if (e != hipSuccess) return fail(ZS_ENOMEM, "hipMalloc for the no-decay table: %s", hipGetErrorString(e));
-  e = hipMemcpy(d, flags.data(), flags.size(), hipMemcpyHostToDevice);
-  if (e != hipSuccess) {
-    (void)hipFree(d);
-    l->nodecay_runs.clear();
-    return hip_fail(e, "uploading the no-decay table");
+  if (!runs.empty()) {  // some element of this shard takes no decay: upload its table
+    hipError_t e = hipMalloc(&d, flags.size());
+    if (e != hipSuccess) return fail(ZS_ENOMEM, "hipMalloc for the no-decay table: %s", hipGetErrorString(e));
+    l->upload_sources.push_back(std::move(flags));
+    const std::vector<uint8_t>& src = l->upload_sources.back();
+    e = hipMemcpyAsync(d, src.data(), src.size(), hipMemcpyHostToDevice, as_stream(stream));
+    if (e != hipSuccess) {
+      l->upload_sources.pop_back();
+      (void)hipFree(d);
+      return hip_fail(e, "uploading the no-decay table");
+    }
   }
+  // The kernels take the table's address at launch, so work enqueued earlier keeps reading
+  // the previous table; it is retired rather than freed (no device-wide wait here).
+  if (l->mem_nodecay) l->retired_tables.push_back(l->mem_nodecay);
   l->mem_nodecay = d;
+  l->nodecay_runs = std::move(runs);
   l->map_shard.seg_nodecay = static_cast<const uint8_t*>(d);
   if (l->plan.dp_world == 1) l->map_full.seg_nodecay = l->map_shard.seg_nodecay;
   return ok();
@@ -803,4 +814,57 @@ extern "C" zs_status zs_offload_adamw_step(const zs_layout* l, const void* shard
   }
   if (e != hipSuccess) return hip_fail(e, "offloaded step");
   return ok();
+}
+
+// ---------------------------------------------------------------------------- bandwidth yardsticks
+
+namespace {
+
+// Workgroups of a probe launch over `units` elements of kTile each: at least one, and fewer
+// than 2^24 (a launch holds fewer than 2^32 work-items).
+zs_status probe_units(int64_t total, int64_t unit, const char* what) {
+  if (total <= 0 || total % unit != 0) return fail(ZS_EINVAL, "%s: size must be a positive multiple of %lld", what,
+                                                   static_cast<long long>(unit));
+  if (total / unit >= (int64_t(1) << 24)) return fail(ZS_EINVAL, "%s: size exceeds one launch", what);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" zs_status zs_probe_mix(const void* g, float* p, float* m, float* v, void* out, int64_t n, void* stream) {
+  if (g == nullptr || p == nullptr || m == nullptr || v == nullptr || out == nullptr)
+    return fail(ZS_EINVAL, "zs_probe_mix: NULL pointer");
+  if (!aligned16(g) || !aligned16(p) || !aligned16(m) || !aligned16(v) || !aligned16(out))
+    return fail(ZS_EINVAL, "zs_probe_mix: pointers must be 16-byte aligned");
+  zs_status st = probe_units(n, zs::kTile, "zs_probe_mix");
+  if (st != ZS_OK) return st;
+  hipError_t e = zs::launch_probe_mix(g, p, m, v, out, n, as_stream(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "launching the mix probe");
+}
+
+extern "C" zs_status zs_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (src == nullptr || dst == nullptr) return fail(ZS_EINVAL, "zs_probe_copy: NULL pointer");
+  if (!aligned16(src) || !aligned16(dst)) return fail(ZS_EINVAL, "zs_probe_copy: pointers must be 16-byte aligned");
+  zs_status st = probe_units(bytes, 4 * zs::kTile, "zs_probe_copy");
+  if (st != ZS_OK) return st;
+  hipError_t e = zs::launch_probe_copy(src, dst, bytes, as_stream(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "launching the copy probe");
+}
+
+extern "C" zs_status zs_probe_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+  if (src == nullptr || sink == nullptr) return fail(ZS_EINVAL, "zs_probe_read: NULL pointer");
+  if (!aligned16(src)) return fail(ZS_EINVAL, "zs_probe_read: src must be 16-byte aligned");
+  zs_status st = probe_units(bytes, 4 * zs::kTile, "zs_probe_read");
+  if (st != ZS_OK) return st;
+  hipError_t e = zs::launch_probe_read(src, bytes, sink, as_stream(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "launching the read probe");
+}
+
+extern "C" zs_status zs_probe_write(void* dst, int64_t bytes, void* stream) {
+  if (dst == nullptr) return fail(ZS_EINVAL, "zs_probe_write: NULL pointer");
+  if (!aligned16(dst)) return fail(ZS_EINVAL, "zs_probe_write: dst must be 16-byte aligned");
+  zs_status st = probe_units(bytes, 4 * zs::kTile, "zs_probe_write");
+  if (st != ZS_OK) return st;
+  hipError_t e = zs::launch_probe_write(dst, bytes, as_stream(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "launching the write probe");
 }

@@ -84,4 +84,11 @@ hipError_t launch_unpack(const DevMap& map, const void* src, int src_dt, const u
                          const DevState* skip, hipStream_t s);
 hipError_t launch_scaler_update(DevState* st, hipStream_t s);
 
+// Bandwidth yardsticks (zs_probe.hip); sizes already checked: n a multiple of kTile, bytes a
+// multiple of 4 * kTile.
+hipError_t launch_probe_mix(const void* g, float* p, float* m, float* v, void* out, int64_t n, hipStream_t s);
+hipError_t launch_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+hipError_t launch_probe_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s);
+hipError_t launch_probe_write(void* dst, int64_t bytes, hipStream_t s);
+
 }  // namespace zs

@@ -151,10 +151,13 @@ struct TileSeg {
   int64_t seg_b, seg_e;  // range-relative bounds of the segment (uniform tiles)
 };
 
-__device__ __forceinline__ TileSeg tile_seg(const DevMap& mp, const uint64_t* ptrs, int64_t tile) {
+// The same for `span` consecutive tiles from `tile` (a pack block of several tiles): the
+// segments meeting them are tile_first[tile] .. tile_first[min(tile + span, ntiles)].
+__device__ __forceinline__ TileSeg span_seg(const DevMap& mp, const uint64_t* ptrs, int64_t tile, int64_t span) {
   TileSeg t;
+  const int64_t end = (tile + span < mp.ntiles) ? tile + span : mp.ntiles;
   t.lo = mp.tile_first[tile];
-  t.hi = mp.tile_first[tile + 1];
+  t.hi = mp.tile_first[end];
   t.uniform = (t.lo == t.hi);
   t.base = nullptr;
   t.seg_b = mp.seg_begin[t.lo];
@@ -164,6 +167,10 @@ __device__ __forceinline__ TileSeg tile_seg(const DevMap& mp, const uint64_t* pt
     if (tensor >= 0) t.base = reinterpret_cast<uint16_t*>(ptrs[tensor]) + (mp.seg_local[t.lo] - t.seg_b);
   }
   return t;
+}
+
+__device__ __forceinline__ TileSeg tile_seg(const DevMap& mp, const uint64_t* ptrs, int64_t tile) {
+  return span_seg(mp, ptrs, tile, 1);
 }
 
 // Elements delta .. delta+7 of the 16-element sequence a | b (a first), delta in 1..7:
@@ -464,7 +471,8 @@ __global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __
   __shared__ float wide[TO_F32 ? kPackBlock : 1];
   const int64_t block_base = (blk0 + work_unit()) * kPackBlock;
   const int64_t end = hi < mp.len ? hi : mp.len;
-  const TileSeg ts = tile_seg(mp, ptrs, block_base / kTile);
+  static_assert(kPackBlock % kTile == 0, "a pack block covers whole tiles");
+  const TileSeg ts = span_seg(mp, ptrs, block_base / kTile, kPackBlock / kTile);
   // uniform across the workgroup: no element of the block is clipped
   const bool whole = block_base >= lo && block_base + kPackBlock <= end;
   const double acc = whole

@@ -170,6 +170,13 @@ class ZeroShardedAdamW:
         self.flat_views = bool(flat_views)
         self.flat_params = None
         if self.flat_views:
+            if dp_world > 1 and self.shard_numel % 8:
+                # each rank's update writes its slice of the parameter buffer, which starts at
+                # element rank * S and must lie on a 16-byte boundary; align a multiple of 8
+                # makes S one (S is a multiple of align)
+                raise ValueError(f"flat_views with several ranks needs a shard size that is a multiple of 8 "
+                                 f"elements (it is {self.shard_numel}), so that every rank's slice of the parameter "
+                                 f"buffer starts on a 16-byte boundary: use align=8")
             if self.grad_dtype != self.param_dtype:
                 raise ValueError("flat_views needs the gradient buffer in the parameter dtype")
             if any(p.dtype != self.param_dtype or p.device != dev for p in params):
@@ -188,6 +195,7 @@ class ZeroShardedAdamW:
         self.local_sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
         self._grad_key = None
         self._grad_ptrs = None
+        self._grad_objs = []
         S = self.shard_numel
         if not self.offload and state_spacing:
             # master, m and v carved from one allocation, `state_spacing` bytes apart (at
@@ -220,10 +228,20 @@ class ZeroShardedAdamW:
             # with flat_views the host's new parameters go straight into the parameter buffer
             self.flat_param = self.param_shard if self.flat_views else torch.empty(S, dtype=self.param_dtype,
                                                                                    device=dev)
+            # the shard's current parameters, so that the buffer (the all-gather input with
+            # several ranks) is valid before the first applied step, and after a skipped one
+            self._seed_flat_param()
             seed = torch.empty(S, dtype=torch.float32, device=dev)
             A.zs_pack(self.layout, self.param_ptrs, self.param_dtype, seed, torch.float32, whole_flat=False)
             self.master.copy_(seed)  # synchronous: complete on return
             del seed
+
+    def _seed_flat_param(self):
+        """Offload mode without flat views: copy this rank's parameters (bit for bit) into
+        the flat parameter shard that the offloaded update writes."""
+        if self.offload and not self.flat_views:
+            A.zs_pack(self.layout, self.param_ptrs, self.param_dtype, self.flat_param, self.param_dtype,
+                      whole_flat=False)
 
     @property
     def shard(self):
@@ -239,15 +257,38 @@ class ZeroShardedAdamW:
         return self.flat_params[self.shard_begin:self.shard_begin + self.shard_numel]
 
     def _grad_table(self, grads):
-        key = tuple(g.data_ptr() for g in grads)
-        if key != self._grad_key:
+        """Device pointer table of a gradient list, rebuilt (and the list validated) unless it
+        holds the very tensor objects validated last time at the same addresses.  The
+        optimizer keeps those tensors alive, so their addresses cannot pass to other tensors
+        that were never checked."""
+        key = tuple(map(torch.Tensor.data_ptr, grads))
+        if key != self._grad_key or len(grads) != len(self._grad_objs) or \
+                not all(map(operator.is_, grads, self._grad_objs)):
             if len(grads) != len(self.numels) or any(g.numel() != n for g, n in zip(grads, self.numels)):
                 raise ValueError("gradients must match the parameter list")
             if any(g.dtype != self.model_grad_dtype for g in grads):
                 raise ValueError(f"gradients must be {self.model_grad_dtype}")
             self._grad_ptrs = pointer_table(grads, self.device)
             self._grad_key = key
+            self._grad_objs = list(grads)
         return self._grad_ptrs
+
+    def _device_arg(self, t, what, dtype, numel):
+        """A caller tensor that a kernel reads or writes: on this GPU, contiguous, of the
+        dtype the kernel takes, with at least `numel` elements (exactly, when exact)."""
+        if t is None:
+            return None
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{what} must be a torch tensor")
+        if t.device != self.device:
+            raise ValueError(f"{what} must live on {self.device}, not on {t.device}")
+        if t.dtype != dtype:
+            raise ValueError(f"{what} must be {dtype}, not {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{what} must be contiguous")
+        if t.numel() != numel:
+            raise ValueError(f"{what} must have {numel} elements, not {t.numel()}")
+        return t
 
     def pack(self, grads, stream=None, accumulate=False, last=True):
         """Pack the per-parameter gradients into the flat buffer, or add them to it
@@ -275,29 +316,34 @@ class ZeroShardedAdamW:
     def check(self, ext_overflow=None, local_sumsq_out=None, stream=None):
         """Overflow flag and local sum of squares of the shard (after the reduce-scatter);
         local_sumsq_out (a device double) receives the value to exchange with the other ranks."""
+        ext_overflow = self._device_arg(ext_overflow, "ext_overflow", torch.int32, 1)
+        local_sumsq_out = self._device_arg(local_sumsq_out, "local_sumsq_out", torch.float64, 1)
         A.zs_unscale_check(self.layout, self.shard, self.grad_dtype, self.state, ext_overflow,
                            local_sumsq_out if local_sumsq_out is not None else self.local_sumsq, stream=stream)
 
     def norm(self, rank_sumsq=None, stream=None):
         """Global norm and clip coefficient; rank_sumsq: device array of every rank's local sum
         of squares in rank order (required when dp_world > 1)."""
+        rank_sumsq = self._device_arg(rank_sumsq, "rank_sumsq", torch.float64, self.dp_world)
         A.zs_grad_norm(self.layout, None, self.grad_dtype, self.state, self.hp, rank_sumsq, None, stream=stream)
 
     def update(self, scatter=True, flat_param_out=None, stream=None):
         """AdamW on the shard, then the new parameters: scattered into the parameter tensors
         (scatter), written to flat_param_out, or with flat_views written into the rank's slice
         of the parameter buffer; then the scaler commit."""
+        flat_param_out = self._device_arg(flat_param_out, "flat_param_out", self.param_dtype, self.shard_numel)
         if self.offload:
             # The host updates the state chunk by chunk; the new parameters of the shard land
-            # in self.flat_param (the all-gather input with several ranks) and are scattered.
+            # in flat_param_out when given, else in self.flat_param (the all-gather input with
+            # several ranks), and are scattered from there.  An overflowed step writes neither.
+            out = flat_param_out if flat_param_out is not None else self.flat_param
             A.zs_offload_adamw_step(self.layout, self.shard, self.grad_dtype, self.state, self.hp, self.master,
                                     self.m, self.v, self.grad_stage, self.param_stage,
-                                    min(self.offload_chunk, max(self.shard_numel, 1)), self.flat_param,
+                                    min(self.offload_chunk, max(self.shard_numel, 1)), out,
                                     self.param_dtype, self.offload_threads, stream=stream)
-            if flat_param_out is not None:
-                flat_param_out.copy_(self.flat_param)
-            if scatter and not self.flat_views:  # views: the parameters are the buffer just written
-                A.zs_unpack(self.layout, self.flat_param, self.param_dtype, False, self.param_ptrs, self.param_dtype,
+            if scatter and not (self.flat_views and out is self.flat_param):
+                # views: the parameters are the buffer just written
+                A.zs_unpack(self.layout, out, self.param_dtype, False, self.param_ptrs, self.param_dtype,
                             self.state, stream=stream)
         elif self.flat_views and scatter and flat_param_out is None:
             # the parameters are views of the parameter buffer: write the shard's slice of it
@@ -399,7 +445,8 @@ class ZeroShardedAdamW:
         """Restore a state_dict() of this rank's layout (the same tensor sizes, dp_world,
         dp_rank and align; reshard_state_dicts() maps a checkpoint taken at another dp_world).
         Writes the scaler and step counters and the master, m and v shard; the model-dtype
-        parameters are restored by the model, as with torch.optim."""
+        parameters are restored by the model, as with torch.optim, before this call (with
+        offload=True the flat parameter shard is refilled from them here)."""
         if sd.get("format") != STATE_FORMAT:
             raise ValueError(f"not a {STATE_FORMAT} state dict")
         lay = sd["layout"]
@@ -415,8 +462,10 @@ class ZeroShardedAdamW:
         self.write_state({k: sd["state"][k] for k in PERSISTENT_STATE}, stream)
         for k in ("master", "m", "v"):
             getattr(self, k).copy_(sd[k].reshape(-1))
-        if self.master.is_cuda:
-            torch.cuda.synchronize(self.device)
+        # offloaded: the flat parameter shard follows the parameters, which the model restores
+        # first (restore the model's parameters before the optimizer's state)
+        self._seed_flat_param()
+        torch.cuda.synchronize(self.device)
 
     def close(self):
         if getattr(self, "state", None):
