@@ -346,6 +346,29 @@ zs_status zs_step_flat(const zs_layout* layout, const void* flat, zs_dtype grad_
                        const zs_adamw_hparams* hp, float* master, float* m, float* v, void* flat_param_out,
                        zs_dtype param_dtype, void* stream);
 
+/* zs_step_flat for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  It needs no layout and no zs_state
+ * and allocates nothing: the reduction workspace and the pre-commit state are a fixed device
+ * array inside the library (about 16.8 MB, one per GPU, held until the process ends).
+ * The same launches and arithmetic as zs_step_flat on a single-rank layout of n elements with
+ * align 1 and no no-decay tensors, so the same results bit for bit.
+ *   flat: n elements of grad_dtype (bf16 or fp16), 16-byte aligned: the gradients.
+ *   n: 1 .. 8,589,934,592 elements (2^21 check workgroups of 4096: the array's capacity).
+ *   state: DEVICE pointer to a zs_state_host in the caller's memory (8-byte aligned), read and
+ *          committed on the device by each call like the state of zs_step_flat; the caller
+ *          fills it once with valid starting values (as zs_state_create checks them) and may
+ *          read it back like any device buffer.
+ *   master, m, v: n fp32 elements each, 16-byte aligned; flat_param_out: n elements of
+ *          param_dtype (bf16 or fp16), 16-byte aligned.
+ * Every call on a GPU shares that GPU's array, and calls on one GPU that overlap (different
+ * streams without ordering, or several host threads) race on it: order them.  The array keeps
+ * the last call's contents; each slot a call reads is written earlier in the same call.
+ * Errors: ZS_EINVAL on NULL pointers, dtypes, misalignment, invalid hyper-parameters or n
+ * outside 1 .. 8,589,934,592 (nothing is enqueued then); ZS_EHIP from the runtime. */
+zs_status zs_step_flat_noalloc(const void* flat, zs_dtype grad_dtype, int64_t n, zs_state_host* state,
+                               const zs_adamw_hparams* hp, float* master, float* m, float* v, void* flat_param_out,
+                               zs_dtype param_dtype, void* stream);
+
 /* Offloaded optimizer step: the fp32 master, m and v live in host memory and the host CPU
  * runs the update, which is bound by memory bandwidth, not by arithmetic ("3.7
  * Megatron-LM, DeepSpeed & Parallelism in Practice", section "ZeRO-Offload and

@@ -41,6 +41,7 @@ from ._abi import (  # noqa: F401
     zs_scaler_update,
     zs_step,
     zs_step_flat,
+    zs_step_flat_noalloc,
     zs_state_create,
     zs_state_destroy,
     zs_state_read,

@@ -80,6 +80,8 @@ _SIGS = {
                 c_void_p, c_void_p, c_int32, c_void_p],
     "zs_step_flat": [c_void_p, c_void_p, c_int32, c_void_p, POINTER(AdamwHParams), c_void_p, c_void_p, c_void_p,
                      c_void_p, c_int32, c_void_p],
+    "zs_step_flat_noalloc": [c_void_p, c_int32, c_int64, c_void_p, POINTER(AdamwHParams), c_void_p, c_void_p,
+                             c_void_p, c_void_p, c_int32, c_void_p],
     "zs_host_adamw_step": [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_int64, POINTER(AdamwHParams),
                            POINTER(StateHost), c_void_p, c_int32, c_int32],
     "zs_probe_mix": [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_void_p],
@@ -350,6 +352,18 @@ def zs_step_flat(layout, flat, grad_dtype, state, hp: AdamwHParams, master, m, v
                               _dptr(master, "master", W), _dptr(m, "m", W), _dptr(v, "v", W),
                               _dptr(flat_param_out, "flat_param_out", W), dtype_code(param_dtype),
                               _stream(stream)), W)
+
+
+def zs_step_flat_noalloc(flat, grad_dtype, n, state, hp: AdamwHParams, master, m, v, flat_param_out,
+                         param_dtype=ZS_BF16, stream=None):
+    """zs_step_flat with no layout, no zs_state and no allocation: `state` is device memory
+    holding a zs_state_host (e.g. a uint8 tensor of ctypes.sizeof(StateHost) bytes), and the
+    library's fixed per-GPU scratch replaces the state's workspace."""
+    W = "zs_step_flat_noalloc"
+    _check(lib().zs_step_flat_noalloc(_dptr(flat, "flat", W), dtype_code(grad_dtype), int(n),
+                                      _dptr(state, "state", W), byref(hp), _dptr(master, "master", W),
+                                      _dptr(m, "m", W), _dptr(v, "v", W), _dptr(flat_param_out, "flat_param_out", W),
+                                      dtype_code(param_dtype), _stream(stream)), W)
 
 
 def zs_last_error():

@@ -683,6 +683,47 @@ extern "C" zs_status zs_step_flat(const zs_layout* l, const void* flat, zs_dtype
   return ok();
 }
 
+extern "C" zs_status zs_step_flat_noalloc(const void* flat, zs_dtype grad_dtype, int64_t n, zs_state_host* state,
+                                          const zs_adamw_hparams* hp, float* master, float* m, float* v,
+                                          void* flat_param_out, zs_dtype param_dtype, void* stream) {
+  const TraceRange trace("zs_step_flat_noalloc");
+  zs_status st = check_hparams(hp);
+  if (st != ZS_OK) return st;
+  if (flat == nullptr || state == nullptr || flat_param_out == nullptr || master == nullptr || m == nullptr ||
+      v == nullptr)
+    return fail(ZS_EINVAL, "flat, state, flat_param_out, master, m and v must not be NULL");
+  if (!is_half_dtype(grad_dtype) || !is_half_dtype(param_dtype))
+    return fail(ZS_EINVAL, "grad_dtype and param_dtype must be bf16 or fp16");
+  if (n < 1) return fail(ZS_EINVAL, "n must be positive");
+  const int64_t max_n = zs::kNoAllocMaxParts * zs::kPackBlock;
+  if (n > max_n)
+    return fail(ZS_EINVAL, "n = %lld exceeds the %lld elements the fixed scratch of zs_step_flat_noalloc covers",
+                static_cast<long long>(n), static_cast<long long>(max_n));
+  if (!aligned16(flat) || !aligned16(flat_param_out))
+    return fail(ZS_EINVAL, "flat and flat_param_out must be 16-byte aligned");
+  if (!aligned16(master) || !aligned16(m) || !aligned16(v)) return fail(ZS_EINVAL, "master, m, v must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(state) & 7u) != 0) return fail(ZS_EINVAL, "state must be 8-byte aligned");
+  zs::NoAllocScratch sc{};
+  hipError_t e = zs::noalloc_scratch(&sc);
+  if (e != hipSuccess) return hip_fail(e, "looking up the scratch of the allocation-free step");
+  hipStream_t s = as_stream(stream);
+  // The launches of zs_step_flat, with the scratch in place of the state's workspace: the
+  // check's partial sums, the finalize (which keeps the pre-commit state for the update), the
+  // update into the flat parameter buffer.
+  const int64_t parts = zs::reduction_blocks(n);
+  e = zs::launch_check(flat, n, grad_dtype, sc.partials, s);
+  if (e != hipSuccess) return hip_fail(e, "launching check");
+  e = zs::launch_step_finalize_ext(sc.partials, parts, sc.level2, state, sc.pre, hp->max_norm, s);
+  if (e != hipSuccess) return hip_fail(e, "launching the step finalize");
+  DevMap map{};  // no segment tables: nothing is scattered and every element decays
+  map.len = n;
+  map.ntiles = (n + zs::kTile - 1) / zs::kTile;
+  const zs::AdamwArgs a{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
+  e = zs::launch_adamw(map, flat, grad_dtype, master, m, v, a, sc.pre, nullptr, flat_param_out, param_dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "launching adamw");
+  return ok();
+}
+
 extern "C" const char* zs_last_error(void) { return g_last_error.c_str(); }
 
 // ---------------------------------------------------------------------------- offloaded step

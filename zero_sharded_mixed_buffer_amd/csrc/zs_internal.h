@@ -77,6 +77,21 @@ hipError_t launch_norm_finalize(DevState* st, const double* rank_sumsq, int dp_w
 // launch of that step takes `pre` as its state.
 hipError_t launch_step_finalize(const double* partials, int64_t nparts, double* level2, DevState* st,
                                 DevState* pre, double max_norm, hipStream_t s);
+// The allocation-free step (zs_step_flat_noalloc): its finalize reads and commits a bare
+// zs_state_host in the caller's memory, and its workspace is a fixed device array of the
+// library, one per GPU, holding kNoAllocMaxParts first-level partial sums: check passes of
+// at most kNoAllocMaxParts * kPackBlock elements.
+constexpr int64_t kNoAllocMaxParts = int64_t(1) << 21;
+constexpr int kMaxDevices = 64;
+struct NoAllocScratch {
+  DevState* pre;
+  double* level2;    // kLevel2 slots
+  double* partials;  // kNoAllocMaxParts slots
+};
+// The calling thread's current device's scratch (its address is looked up once per device).
+hipError_t noalloc_scratch(NoAllocScratch* out);
+hipError_t launch_step_finalize_ext(const double* partials, int64_t nparts, double* level2, zs_state_host* st,
+                                    DevState* pre, double max_norm, hipStream_t s);
 hipError_t launch_adamw(const DevMap& map, const void* shard, int grad_dt, float* master, float* m, float* v,
                         const AdamwArgs& hp, const DevState* st, const uint64_t* param_ptrs, void* flat_out,
                         int param_dt, hipStream_t s);

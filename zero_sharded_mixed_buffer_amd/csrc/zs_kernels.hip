@@ -22,6 +22,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "zs_internal.h"
 
 namespace zs {
@@ -660,6 +662,24 @@ __global__ __launch_bounds__(kThreads) void k_step_finalize(const double* __rest
   }
 }
 
+// The same finalize for a state that lives in the caller's memory as a bare zs_state_host
+// (the allocation-free step): the state is read, finalized and committed in registers, the
+// pre-commit copy goes to `pre` and the committed fields back to the caller.
+__global__ __launch_bounds__(kThreads) void k_step_finalize_ext(const double* __restrict__ partials, int64_t nparts,
+                                                                zs_state_host* __restrict__ st,
+                                                                DevState* __restrict__ pre, double max_norm) {
+  const double raw = fold_partials(partials, nparts);
+  if (threadIdx.x == 0) {
+    DevState d{};
+    d.h = *st;
+    flag_commit(&d, raw, nullptr, kFlagSet, nullptr);
+    norm_commit(&d, nullptr, 1, 0, nullptr, max_norm);
+    *pre = d;
+    scaler_commit(&d);
+    *st = d.h;
+  }
+}
+
 // ------------------------------------------------------------------ AdamW + cast + scatter
 
 // Per-step scalars, evaluated in fp64 by every workgroup from the device state.
@@ -1010,6 +1030,51 @@ hipError_t launch_step_finalize(const double* partials, int64_t nparts, double* 
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_step_finalize, dim3(1), dim3(kThreads), 0, s, partials, nparts, st, pre, max_norm);
   return hipGetLastError();
+}
+
+hipError_t launch_step_finalize_ext(const double* partials, int64_t nparts, double* level2, zs_state_host* st,
+                                    DevState* pre, double max_norm, hipStream_t s) {
+  hipError_t e = reduce_level2(&partials, &nparts, level2, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_step_finalize_ext, dim3(1), dim3(kThreads), 0, s, partials, nparts, st, pre, max_norm);
+  return hipGetLastError();
+}
+
+// Scratch of the allocation-free step, one copy per GPU for the life of the process: the
+// pre-commit state, the second-level partial sums, then one first-level partial sum per
+// check workgroup.  Every slot a call reads was written earlier in the same call, so nothing
+// needs clearing between calls.
+constexpr int64_t kNoAllocPre = 32;  // doubles reserved for the pre-commit DevState
+static_assert(sizeof(DevState) <= kNoAllocPre * sizeof(double), "pre-commit state slot too small");
+constexpr int64_t kNoAllocDoubles = kNoAllocPre + kLevel2 + kNoAllocMaxParts;
+static __device__ __align__(256) double scratch[kNoAllocDoubles];
+
+hipError_t noalloc_scratch(NoAllocScratch* out) {
+  // The array's name is a host-side stand-in: its device address comes from the runtime, once
+  // per device, with that device current.
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+      e = hipGetSymbolAddress(&addr[dev], HIP_SYMBOL(scratch));
+      if (e != hipSuccess) {
+        addr[dev] = nullptr;
+        return e;
+      }
+    }
+    p = addr[dev];
+  }
+  double* d = static_cast<double*>(p);
+  out->pre = reinterpret_cast<DevState*>(d);
+  out->level2 = d + kNoAllocPre;
+  out->partials = d + kNoAllocPre + kLevel2;
+  return hipSuccess;
 }
 
 hipError_t launch_norm_finalize(DevState* st, const double* rank_sumsq, int dp_world, int dp_rank,
