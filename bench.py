@@ -30,12 +30,43 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(wl, n_elems, steps):
+def host_info():
+    """The host the CPU baseline ran on: CPU model, hardware threads, memory."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    ram = None
+    try:
+        with open("/proc/meminfo") as fh:
+            ram = int(fh.readline().split()[1]) * 1024 / 1e9
+    except (OSError, ValueError, IndexError):
+        pass
+    return {"cpu": model, "hardware_threads": os.cpu_count(), "ram_gb": ram}
+
+
+def cpu_baseline(wl, n_elems, steps, threads=None):
     """Time the CPU oracle (as it stands) on a bounded slice of the workload: one tensor of
-    n_elems elements drawn from the workload's distributions, `steps` whole steps."""
+    n_elems elements drawn from the workload's distributions, `steps` whole steps, on
+    `threads` torch threads (None: torch's default, every core it was given)."""
     import torch
 
     import oracle as O
+    saved = torch.get_num_threads()
+    if threads is not None:
+        torch.set_num_threads(threads)
+    try:
+        return _cpu_baseline(torch, O, wl, n_elems, steps)
+    finally:
+        torch.set_num_threads(saved)
+
+
+def _cpu_baseline(torch, O, wl, n_elems, steps):
     gen = torch.Generator().manual_seed(wl.seed)
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float16
     params = [torch.randn(n_elems, generator=gen).mul_(wl.param_sigma).to(dt)]
@@ -143,6 +174,13 @@ def run_offload(args, wl, torch, Z, gen):
     }
 
 
+def _median(xs):
+    xs = sorted(xs)
+    if not xs:
+        return None
+    return xs[len(xs) // 2] if len(xs) % 2 else 0.5 * (xs[len(xs) // 2 - 1] + xs[len(xs) // 2])
+
+
 def kernel_source_sha256():
     """Hash of the kernel sources with comments and blank space removed, so that counter
     summaries stay valid across comment edits and go stale on any code change."""
@@ -231,9 +269,15 @@ def main():
                     help="1d: tensors with at most one dimension (biases, norm weights) take no weight decay")
     ap.add_argument("--state-spacing-gib", type=float, default=0.0,
                     help="place master, m and v this many GiB apart in one allocation (0: three allocations)")
+    ap.add_argument("--placement", choices=["tune", "separate"], default="tune",
+                    help="tune: the optimizer carves its gradient buffer and master/m/v from one allocation in the "
+                         "order its update measures fastest (the default); separate: four allocations")
     ap.add_argument("--log-steps", type=int, default=0,
                     help="after the timed region, run this many more steps reading the state after each and "
                          "print one [zs_step k] line per step (scale, skips, norm, clip, time)")
+    ap.add_argument("--faults", action="store_true",
+                    help="apply the workload's fault schedule (non-finite gradients on its fault steps, drawn for "
+                         "--steps steps) in the timed steps and report the skipped steps' time separately")
     ap.add_argument("--flat-views", action="store_true",
                     help="parameters and gradients as views into contiguous buffers (backward fills the "
                          "gradient buffer): the step checks the buffer instead of packing, and the update "
@@ -287,7 +331,8 @@ def main():
                              init_scale=wl.init_scale, growth_interval=wl.growth_interval, accum_dtype=accum,
                              no_decay="1d" if args.no_decay == "1d" else None,
                              state_spacing=int(args.state_spacing_gib * (1 << 30)) or None,
-                             flat_views=args.flat_views)
+                             flat_views=args.flat_views, placement=args.placement)
+    log(f"placement of the optimizer's buffers: {opt.placement}")
     views = args.flat_views
     if views:
         if G != 1 or args.bucket_numel or args.graph:
@@ -325,13 +370,47 @@ def main():
             Z.zs_state_destroy(sq)
             Z.zs_layout_destroy(lq)
     separate_check = (buckets is not None or d > 1) and not views
+    # --faults: the timed steps follow the workload's fault schedule.  A fault step packs a
+    # gradient list whose affected tensors are copies holding the non-finite values, through
+    # a pointer table built beforehand; with several ranks, another rank whose shard holds a
+    # fault sends a non-finite partial sum, as its own check would.
+    schedule, fault_tables, fault_exch, clean_exch = {}, {}, {}, None
+    if args.faults:
+        if G != 1 or buckets is not None or views or args.graph:
+            print(json.dumps({"error": "--faults times the plain step (one micro-step, one pack)"}))
+            sys.exit(2)
+        schedule = wl.faults_for(args.steps)
+        offsets = Z.zs_plan(wl.numels, d, r, wl.align)[0]
+        clean_exch = exchange.clone() if d > 1 else None
+        for k, items in schedule.items():
+            faulty = list(grads)
+            for t, idx, val in items:
+                if faulty[t] is grads[t]:
+                    faulty[t] = grads[t].clone()
+                faulty[t].view(-1)[idx] = val
+            fault_tables[k] = (faulty, Z.pointer_table(faulty, dev))
+            if d > 1:
+                ex = clean_exch.clone()
+                for t, idx, val in items:
+                    q = (offsets[t] + idx) // S
+                    if q != r:
+                        ex[q] = math.inf
+                fault_exch[k] = ex
+        torch.cuda.synchronize()
+        log(f"fault schedule over {args.steps} steps: steps {sorted(schedule)} "
+            f"({sum(len(v) for v in schedule.values())} non-finite values)")
+    fault_step = [None]  # the timed step being issued (1-based) when it is a fault step
 
     def pack_pass(k):
         last = k == G - 1
         if views:  # the gradients are already in the buffer (the shard: after the reduce-scatter)
             opt.check(local_sumsq_out=exchange[r:r + 1] if d > 1 else None, stream=stream)
             return
-        if buckets is None:
+        if fault_step[0] is not None:
+            _, table = fault_tables[fault_step[0]]
+            Z.zs_pack(lay, table, opt.model_grad_dtype, opt.flat, opt.grad_dtype, whole_flat=True,
+                      fuse_check=st if d == 1 else None, stream=stream)
+        elif buckets is None:
             opt.pack(grads, stream, accumulate=k > 0, last=last)
         else:
             for b in buckets:
@@ -375,11 +454,19 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
+        if schedule:
+            fault_step[0] = (k + 1) if (k + 1) in schedule else None
+            if d > 1 and ((k + 1) in schedule or k in schedule):  # the other ranks' partials
+                exchange.copy_(fault_exch[k + 1] if (k + 1) in schedule else clean_exch)
         one_step(evs[k])
+    fault_step[0] = None
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     state = opt.read_state()
-    assert state["skipped_total"] == 0 and state["step_t"] == args.warmup + args.steps
+    n_skip = len(schedule)
+    assert state["skipped_total"] == n_skip and state["step_t"] == args.warmup + args.steps - n_skip, state
+    if d > 1 and schedule:
+        exchange.copy_(clean_exch)
     graph_replay = None
     if args.graph:
         if d != 1 or G != 1 or buckets is not None:
@@ -418,9 +505,11 @@ def main():
             f"{graph_replay['single_call_ms_per_step']:.4f} ms/step, four-call sequence "
             f"{graph_replay['sequence_ms_per_step']:.4f} ms/step")
         del graph
-    pack_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    first_pack_ms = sum(e[0].elapsed_time(e[4]) for e in evs) / args.steps
-    adamw_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    # kernel averages over the applied steps (a skipped step's update returns at once)
+    applied = [e for k, e in enumerate(evs) if (k + 1) not in schedule]
+    pack_ms = sum(e[0].elapsed_time(e[1]) for e in applied) / len(applied)
+    first_pack_ms = sum(e[0].elapsed_time(e[4]) for e in applied) / len(applied)
+    adamw_ms = sum(e[2].elapsed_time(e[3]) for e in applied) / len(applied)
     ms_per_step = elapsed * 1e3 / args.steps
     step_ms = sorted(e[0].elapsed_time(e[5]) for e in evs)  # per-step HIP-event durations
     step_median = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (
@@ -476,7 +565,7 @@ def main():
                    "accum_dtype": ("fp32" if accum is not None else wl.dtype),
                    "bucket_numel": args.bucket_numel or None, "buckets": len(buckets) if buckets else None,
                    "no_decay": args.no_decay, "state_spacing_gib": args.state_spacing_gib or None,
-                   "flat_views": views},
+                   "flat_views": views, "placement": opt.placement},
         "achieved_hbm_gbps": step_gbps,
         "hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": step_bytes,
@@ -484,6 +573,14 @@ def main():
                        "finalize_and_scaler": ms_per_step - pack_ms - adamw_ms},
         "unpack_after_allgather": unpack,
         "graph_replay": graph_replay,
+        "faults": None if not args.faults else {
+            "fault_steps": sorted(schedule),
+            "non_finite_values": sum(len(v) for v in schedule.values()),
+            "skipped_ms_each": [evs[k - 1][0].elapsed_time(evs[k - 1][5]) for k in sorted(schedule)],
+            "applied_ms_median": _median([evs[k][0].elapsed_time(evs[k][5]) for k in range(args.steps)
+                                          if (k + 1) not in schedule]),
+            "skipped_steps_note": "a skipped step runs the pack (or the shard check), the flag and norm finalize, "
+                                  "an update kernel that returns at once and the scaler commit"},
         "accumulation": None if G == 1 else {
             "first_pack_ms": first_pack_ms, "first_pack_gbps": first_bytes / first_pack_ms / 1e6,
             "accumulate_ms_each": (pack_ms - first_pack_ms) / (G - 1),
@@ -518,8 +615,10 @@ def main():
     del params, grads, opt
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle baseline")
+        log("timing the CPU oracle baseline (all threads, then one)")
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_baseline_elems, args.cpu_baseline_steps)
+        out["cpu_baseline_serial"] = cpu_baseline(wl, args.cpu_baseline_elems // 8, 3, threads=1)
+        out["cpu_host"] = host_info()
     print(json.dumps(out), flush=True)
 
 

@@ -149,6 +149,18 @@ class Workload:
     faults: dict = field(default_factory=dict)
     hparams: dict = field(default_factory=lambda: dict(HPARAMS))
     growth_interval: int = GROWTH_INTERVAL
+    fault_spec: tuple = ()     # how `faults` was drawn, to draw the schedule of a longer run
+
+    def faults_for(self, steps):
+        """The fault schedule of a run of `steps` steps: `faults` for the workload's own step
+        count, otherwise drawn the same way for the longer (or shorter) run."""
+        if steps == self.steps or not self.fault_spec:
+            return {k: v for k, v in self.faults.items() if k <= steps}
+        kind, seed = self.fault_spec[0], self.fault_spec[1]
+        if kind == "bernoulli":
+            return _faults_bernoulli(seed, steps, self.fault_spec[2], self.fault_spec[3], self.numels)
+        n_steps = max(1, round(self.fault_spec[2] * steps))
+        return _faults_scattered(seed, steps, n_steps, self.fault_spec[3], self.numels)
 
     @property
     def numels(self):
@@ -204,13 +216,15 @@ def _build():
     moe = tuple(_moe_like())
     moe_numels = [int(np.prod(s)) for _, s in moe]
     wl["moe_3.4b_dp4"] = Workload("moe_3.4b_dp4", moe, "fp16", 4, 0, True, 2.0 ** 16, 1e-4, 0.02, 10, 3,
-                                  faults=_faults_bernoulli(3, 10, 1e-3, 4, moe_numels))
+                                  faults=_faults_bernoulli(3, 10, 1e-3, 4, moe_numels),
+                                  fault_spec=("bernoulli", 3, 1e-3, 4))
     llama = tuple(_llama3_like())
     wl["llama3_8b"] = Workload("llama3_8b", llama, "bf16", 1, 0, False, 1.0, 1e-3, 0.02, 10, 4)
     rag = tuple(_ragged_shapes(5, 6000, 14000, 2_000_000_000))
     rag_numels = [s[0] for _, s in rag]
     wl["ragged_20k"] = Workload("ragged_20k", rag, "bf16", 1, 0, False, 1.0, 1e-3, 0.02, 20, 5,
-                                faults=_faults_scattered(5, 20, 2, 2000, rag_numels))
+                                faults=_faults_scattered(5, 20, 2, 2000, rag_numels),
+                                fault_spec=("scattered", 5, 0.1, 2000))
 
     # Reduced-size variants with the same structure, for parity runs the oracle finishes in seconds.
     mini_rag = tuple(_ragged_shapes(15, 300, 700, 6_000_000))

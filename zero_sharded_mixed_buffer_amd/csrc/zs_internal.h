@@ -25,6 +25,21 @@ constexpr int kLevel2 = 1024;  // first-level partial-sum workgroups of the two-
 // A shard of at most this many tiles runs the AdamW kernel with four workgroups per tile.
 constexpr int64_t kSplitTiles = 256;
 
+// XCD-aware work order.  The dispatcher deals consecutive workgroups to the eight XCDs in
+// turn.  Run length R: 0 keeps that order (XCD x gets every eighth unit); R > 0 gives each
+// XCD runs of R consecutive units (the units of each group of 8R are dealt as eight runs);
+// kXcdWhole gives each XCD one contiguous eighth of the range.
+constexpr int kXcds = 8;
+constexpr int64_t kXcdWhole = -1;
+constexpr int64_t kXcdRunAdamw = 16;
+constexpr int64_t kXcdRunPack = kXcdWhole;
+// Workgroups launched for `units` units of work in the order of run length `run`.
+inline int64_t launch_units(int64_t units, int64_t run) {
+  if (run == 0) return units;
+  const int64_t group = kXcds * (run > 0 ? run : 1);
+  return (units + group - 1) / group * group;
+}
+
 // Workgroups (and partial sums) of a pack or check pass over len elements.
 inline int64_t reduction_blocks(int64_t len) { return (len + kPackBlock - 1) / kPackBlock; }
 

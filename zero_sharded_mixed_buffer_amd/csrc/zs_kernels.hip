@@ -278,6 +278,26 @@ __device__ __forceinline__ void scatter(const DevMap& mp, const uint64_t* ptrs, 
 // Work unit (tile or pack block) of this workgroup.
 __device__ __forceinline__ int64_t work_unit() { return blockIdx.x; }
 
+// Work unit of this workgroup among `units` in the XCD-aware order of run length RUN
+// (launched with launch_units(units, RUN) workgroups); -1 for the workgroups beyond the last
+// unit (fewer than one group).  The map is a bijection on the launched range.
+template <int64_t RUN>
+__device__ __forceinline__ int64_t ordered_unit(int64_t units) {
+  const int64_t b = blockIdx.x;
+  if constexpr (RUN == 0) {
+    return b;
+  } else if constexpr (RUN == kXcdWhole) {
+    const int64_t per = (units + kXcds - 1) / kXcds;
+    const int64_t u = (b % kXcds) * per + b / kXcds;
+    return u < units ? u : -1;
+  } else {
+    constexpr int64_t group = kXcds * RUN;
+    const int64_t w = b % group;
+    const int64_t u = (b - w) + (w % kXcds) * RUN + w / kXcds;
+    return u < units ? u : -1;
+  }
+}
+
 __device__ __forceinline__ int group_count(int64_t len, int64_t q) {
   const int64_t rem = len - q;
   return rem >= kGroup ? kGroup : (rem > 0 ? static_cast<int>(rem) : 0);
@@ -468,10 +488,12 @@ __device__ __forceinline__ double pack_block(const DevMap& mp, const uint64_t* p
 template <int SDT, bool TO_F32, bool ACC, bool CHECK>
 __global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __restrict__ ptrs,
                                                    void* __restrict__ dst, double* __restrict__ partials,
-                                                   int64_t blk0, int64_t lo, int64_t hi) {
+                                                   int64_t blk0, int64_t nblk, int64_t lo, int64_t hi) {
   __shared__ v4u stage[kPackChunks + 1];
   __shared__ float wide[TO_F32 ? kPackBlock : 1];
-  const int64_t block_base = (blk0 + work_unit()) * kPackBlock;
+  const int64_t unit = ordered_unit<kXcdRunPack>(nblk);
+  if (unit < 0) return;  // uniform across the workgroup
+  const int64_t block_base = (blk0 + unit) * kPackBlock;
   const int64_t end = hi < mp.len ? hi : mp.len;
   static_assert(kPackBlock % kTile == 0, "a pack block covers whole tiles");
   const TileSeg ts = span_seg(mp, ptrs, block_base / kTile, kPackBlock / kTile);
@@ -482,7 +504,7 @@ __global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __
       : pack_block<SDT, TO_F32, ACC, CHECK, true>(mp, ptrs, dst, ts, block_base, lo, end, stage, wide);
   if (CHECK) {
     const double r = block_sum(acc);
-    if (threadIdx.x == 0) partials[blockIdx.x] = r;
+    if (threadIdx.x == 0) partials[unit] = r;
   }
 }
 
@@ -768,8 +790,10 @@ __global__ __launch_bounds__(kThreads) void k_adamw(DevMap mp, const void* __res
   const StepScalars k = step_scalars(hp, st);
   const bool g_vec = (GDT == ZS_FP32) ? aligned16(shard) : aligned8(shard);
   const int64_t n = mp.len;
-  const int64_t tile = work_unit() / SPLIT;
-  const int64_t base = tile * kTile + (work_unit() % SPLIT) * (kTile / SPLIT);
+  const int64_t unit = ordered_unit<SPLIT == 1 ? kXcdRunAdamw : 0>(mp.ntiles * SPLIT);
+  if (unit < 0) return;  // uniform across the workgroup
+  const int64_t tile = unit / SPLIT;
+  const int64_t base = tile * kTile + (unit % SPLIT) * (kTile / SPLIT);
   v4f gv[kQuads];
   v4f pv[kQuads], mv[kQuads], vv[kQuads];
   int cnts[kQuads];
@@ -950,11 +974,11 @@ __global__ __launch_bounds__(kThreads) void k_unpack(DevMap mp, const void* __re
 
 template <int SDT>
 static void pack_dispatch(const dim3& G, hipStream_t s, const DevMap& map, const uint64_t* src_ptrs, void* dst,
-                          bool f32, bool acc, double* partials, int64_t blk0, int64_t lo, int64_t hi) {
+                          bool f32, bool acc, double* partials, int64_t blk0, int64_t nblk, int64_t lo, int64_t hi) {
   const dim3 B(kThreads);
   const bool chk = (partials != nullptr);
 #define ZS_PACK(F, A, C) \
-  hipLaunchKernelGGL((k_pack<SDT, F, A, C>), G, B, 0, s, map, src_ptrs, dst, partials, blk0, lo, hi)
+  hipLaunchKernelGGL((k_pack<SDT, F, A, C>), G, B, 0, s, map, src_ptrs, dst, partials, blk0, nblk, lo, hi)
   if (f32) {
     if (acc) {
       if (chk) ZS_PACK(true, true, true); else ZS_PACK(true, true, false);
@@ -978,12 +1002,12 @@ hipError_t launch_pack(const DevMap& map, const uint64_t* src_ptrs, int src_dt, 
   const int64_t blk0 = lo / kPackBlock;
   const int64_t nb = (hi + kPackBlock - 1) / kPackBlock - blk0;
   if (nb <= 0) return hipSuccess;
-  const dim3 G(static_cast<unsigned>(nb));
+  const dim3 G(static_cast<unsigned>(launch_units(nb, kXcdRunPack)));
   const bool f32 = (dst_dt == ZS_FP32);
   if (src_dt == ZS_BF16)
-    pack_dispatch<ZS_BF16>(G, s, map, src_ptrs, dst, f32, accumulate, partials, blk0, lo, hi);
+    pack_dispatch<ZS_BF16>(G, s, map, src_ptrs, dst, f32, accumulate, partials, blk0, nb, lo, hi);
   else
-    pack_dispatch<ZS_FP16>(G, s, map, src_ptrs, dst, f32, accumulate, partials, blk0, lo, hi);
+    pack_dispatch<ZS_FP16>(G, s, map, src_ptrs, dst, f32, accumulate, partials, blk0, nb, lo, hi);
   return hipGetLastError();
 }
 
@@ -1113,10 +1137,12 @@ static void adamw_dispatch_g(const dim3& G, hipStream_t s, const DevMap& map, co
                              float* m, float* v, const AdamwArgs& hp, const DevState* st, const uint64_t* ptrs,
                              uint16_t* flat_out) {
   if (map.ntiles <= kSplitTiles)
-    adamw_dispatch_s<GDT, PDT, GROUPS, kQuadsPerThread>(dim3(G.x * kQuadsPerThread), s, map, shard, master, m, v,
-                                                         hp, st, ptrs, flat_out);
+    adamw_dispatch_s<GDT, PDT, GROUPS, kQuadsPerThread>(
+        dim3(static_cast<unsigned>(launch_units(map.ntiles * kQuadsPerThread, 0))), s, map, shard, master, m,
+        v, hp, st, ptrs, flat_out);
   else
-    adamw_dispatch_s<GDT, PDT, GROUPS, 1>(G, s, map, shard, master, m, v, hp, st, ptrs, flat_out);
+    adamw_dispatch_s<GDT, PDT, GROUPS, 1>(dim3(static_cast<unsigned>(launch_units(map.ntiles, kXcdRunAdamw))), s, map,
+                                          shard, master, m, v, hp, st, ptrs, flat_out);
 }
 
 template <int GDT, int PDT>

@@ -37,6 +37,10 @@ def pointer_table(tensors, device):
     return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
 
 
+# Shards of at least this many elements choose the placement of their buffers by measurement
+# (ZeroShardedAdamW._tune_placement); below it the update is too short for placement to show.
+TUNE_MIN_ELEMENTS = 1 << 26
+
 # Checkpoint format of ZeroShardedAdamW.state_dict(), and the state fields it keeps (the
 # others are results of the latest check and norm, recomputed by the next step).
 STATE_FORMAT = "zs-rank-state-1"
@@ -109,6 +113,10 @@ class ZeroShardedAdamW:
     no_decay: one flag per tensor (True: no weight decay), or "1d" for every tensor with
         at most one dimension.
     state_spacing: carve master / m / v from one allocation this many bytes apart.
+    placement: "tune" (default): a shard of at least TUNE_MIN_ELEMENTS elements carves the
+        gradient buffer and master / m / v from one allocation, in the order of the four
+        whose update measured fastest at construction (see _tune_placement); "separate":
+        four allocations.
     flat_views: the parameters and their .grad become views into two flat buffers laid out
         like the gradient buffer (a contiguous parameter buffer and a contiguous gradient
         buffer that backward fills in place).  step() with no gradient list then checks the
@@ -120,7 +128,7 @@ class ZeroShardedAdamW:
                  dp_world=1, dp_rank=0, align=1, dynamic_loss_scale=None, init_scale=None, scale_floor=1.0,
                  growth_interval=1000, grad_dtype=None, accum_dtype=None, offload=False,
                  offload_chunk=1 << 24, offload_threads=0, no_decay=None, state_spacing=None,
-                 flat_views=False):
+                 flat_views=False, placement="tune"):
         params = list(params)
         if not params:
             raise ValueError("empty parameter list")
@@ -166,7 +174,8 @@ class ZeroShardedAdamW:
                 A.zs_layout_set_no_decay(self.layout, self.no_decay)
         dev = self.device
         self.offload = bool(offload)
-        self.flat = torch.zeros(self.flat_numel, dtype=self.grad_dtype, device=dev)
+        if placement not in ("tune", "separate"):
+            raise ValueError("placement is 'tune' or 'separate'")
         self.flat_views = bool(flat_views)
         self.flat_params = None
         if self.flat_views:
@@ -183,21 +192,23 @@ class ZeroShardedAdamW:
                 raise ValueError("flat_views needs every parameter in one dtype on one device")
             offsets = A.zs_plan(self.numels, dp_world, dp_rank, align)[0]
             self.flat_params = torch.zeros(self.flat_numel, dtype=self.param_dtype, device=dev)
-            self._grad_views = []
             with torch.no_grad():
                 for p, off, n in zip(params, offsets, self.numels):
                     view = self.flat_params[off:off + n].view(p.shape)
                     view.copy_(p)
                     p.data = view
-                    p.grad = self.flat[off:off + n].view(p.shape)
-                    self._grad_views.append(p.grad)
         self.param_ptrs = pointer_table(params, dev)
         self.local_sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
         self._grad_key = None
         self._grad_ptrs = None
         self._grad_objs = []
         S = self.shard_numel
-        if not self.offload and state_spacing:
+        self.placement = {"mode": "separate"}
+        tune = (placement == "tune" and not self.offload and not state_spacing and S >= TUNE_MIN_ELEMENTS)
+        if tune and self._tune_placement():
+            pass  # flat, master, m and v carved from the arena, master seeded
+        elif not self.offload and state_spacing:
+            self.flat = torch.zeros(self.flat_numel, dtype=self.grad_dtype, device=dev)
             # master, m and v carved from one allocation, `state_spacing` bytes apart (at
             # least their own size): on MI355X, arrays streamed together run faster when
             # they sit some GiB apart in HBM than when they sit back to back
@@ -209,6 +220,7 @@ class ZeroShardedAdamW:
             self.v = self._state_arena[2 * gap:2 * gap + S]
             A.zs_pack(self.layout, self.param_ptrs, self.param_dtype, self.master, torch.float32, whole_flat=False)
         elif not self.offload:
+            self.flat = torch.zeros(self.flat_numel, dtype=self.grad_dtype, device=dev)
             self.master = torch.empty(S, dtype=torch.float32, device=dev)
             self.m = torch.zeros(S, dtype=torch.float32, device=dev)
             self.v = torch.zeros(S, dtype=torch.float32, device=dev)
@@ -217,6 +229,7 @@ class ZeroShardedAdamW:
             # Optimizer state in host memory (only the CPU touches it, so it need not be
             # pinned), pinned two-chunk staging buffers for the copies, and the device buffer
             # that receives the new parameters of the shard.
+            self.flat = torch.zeros(self.flat_numel, dtype=self.grad_dtype, device=dev)
             self.offload_chunk = int(offload_chunk)
             self.offload_threads = int(offload_threads)
             self.master = torch.empty(S, dtype=torch.float32)
@@ -235,6 +248,85 @@ class ZeroShardedAdamW:
             A.zs_pack(self.layout, self.param_ptrs, self.param_dtype, seed, torch.float32, whole_flat=False)
             self.master.copy_(seed)  # synchronous: complete on return
             del seed
+        if self.flat_views:  # every .grad a view of the gradient buffer, wherever it was placed
+            self._grad_views = []
+            for p, off, n in zip(params, A.zs_plan(self.numels, dp_world, dp_rank, align)[0], self.numels):
+                p.grad = self.flat[off:off + n].view(p.shape)
+                self._grad_views.append(p.grad)
+
+    def _tune_placement(self):
+        """Carve the gradient buffer and master, m, v from one allocation, in the order (of
+        the 24) whose update runs fastest here, and seed the master.  On MI355X the streams
+        of the update run up to a few per cent faster or slower depending on where in HBM
+        they sit relative to one another (the physical-address hash that spreads them over
+        channels), and that varies with the memory an allocation receives; measuring the
+        real update on the real buffers is the reliable way to pick.  Each candidate is
+        timed with the update kernel itself at lr = 0 on zero gradients and moments, which
+        writes back the very (finite) parameters it reads (the master is the exact fp32
+        widening of the parameters, and their nearest-even cast is the parameters again), so
+        nothing the caller sees changes.  Returns False (nothing allocated) when the single allocation
+        does not fit."""
+        import itertools
+        dev, S = self.device, self.shard_numel
+        step = 1 << 21
+        gbytes = torch.empty(0, dtype=self.grad_dtype).element_size()
+        sizes = {"flat": self.flat_numel * gbytes, "master": 4 * S, "m": 4 * S, "v": 4 * S}
+        padded = {k: (b + step - 1) // step * step for k, b in sizes.items()}
+        try:
+            arena = torch.empty(sum(padded.values()), dtype=torch.uint8, device=dev)
+        except torch.cuda.OutOfMemoryError:
+            return False
+        dtypes = {"flat": self.grad_dtype, "master": torch.float32, "m": torch.float32, "v": torch.float32}
+        numel = {"flat": self.flat_numel, "master": S, "m": S, "v": S}
+
+        def carve(order):
+            out, off = {}, 0
+            for k in order:
+                out[k] = arena[off:off + sizes[k]].view(dtypes[k])[:numel[k]]
+                off += padded[k]
+            return out
+
+        hp = self.hp
+        frozen = A.hparams(0.0, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.max_norm)
+        out_flat = self.param_shard if self.flat_views else None
+        ptrs = None if self.flat_views else self.param_ptrs
+        stream = torch.cuda.current_stream(dev)
+        times = {}
+        with torch.cuda.device(dev):
+            for order in itertools.permutations(("flat", "master", "m", "v")):
+                b = carve(order)
+                b["flat"].zero_()
+                b["m"].zero_()
+                b["v"].zero_()
+                A.zs_pack(self.layout, self.param_ptrs, self.param_dtype, b["master"], torch.float32,
+                          whole_flat=False, stream=stream)
+                shard = b["flat"][self.shard_begin:self.shard_begin + S]
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                A.zs_adamw_step(self.layout, shard, self.grad_dtype, b["master"], b["m"], b["v"], frozen, self.state,
+                                ptrs, out_flat, self.param_dtype, stream=stream)
+                ev[0].record(stream)
+                A.zs_adamw_step(self.layout, shard, self.grad_dtype, b["master"], b["m"], b["v"], frozen, self.state,
+                                ptrs, out_flat, self.param_dtype, stream=stream)
+                ev[1].record(stream)
+                A.zs_adamw_step(self.layout, shard, self.grad_dtype, b["master"], b["m"], b["v"], frozen, self.state,
+                                ptrs, out_flat, self.param_dtype, stream=stream)
+                ev[2].record(stream)
+                ev[2].synchronize()
+                times["".join(k[0] if k != "master" else "M" for k in order)] = min(ev[0].elapsed_time(ev[1]),
+                                                                                   ev[1].elapsed_time(ev[2]))
+            best = min(times, key=times.get)
+            order = [{"f": "flat", "M": "master", "m": "m", "v": "v"}[c] for c in best]
+            b = carve(order)
+            b["flat"].zero_()
+            b["m"].zero_()
+            b["v"].zero_()
+            A.zs_pack(self.layout, self.param_ptrs, self.param_dtype, b["master"], torch.float32, whole_flat=False,
+                      stream=stream)
+        self._arena = arena
+        self.flat, self.master, self.m, self.v = b["flat"], b["master"], b["m"], b["v"]
+        self.placement = {"mode": "tuned", "order": best, "update_ms": times[best],
+                          "update_ms_range": [min(times.values()), max(times.values())], "candidates": len(times)}
+        return True
 
     def _seed_flat_param(self):
         """Offload mode without flat views: copy this rank's parameters (bit for bit) into
