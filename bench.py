@@ -174,6 +174,28 @@ def run_offload(args, wl, torch, Z, gen):
     }
 
 
+def one_draw_inputs(torch, gen, wl, dev):
+    """Parameters and gradients of the workload as views into one buffer each, every tensor
+    starting on a 512-byte boundary (as the caching allocator places separate small
+    tensors), each buffer filled by a single draw with the workload's distribution: the same
+    tensor list and kernel paths as one draw per tensor, with a handful of dispatches
+    instead of thousands (for counter runs)."""
+    dt = gen.TORCH_DTYPE[wl.dtype]
+    offs, pos = [], 0
+    for n in wl.numels:
+        offs.append(pos)
+        pos += (n + 255) // 256 * 256
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed)
+    bufs = []
+    for sigma in (wl.param_sigma, wl.grad_sigma * wl.init_scale):
+        x = torch.randn(pos, generator=g, device=dev, dtype=torch.float32)
+        bufs.append(x.mul_(sigma).to(dt))
+        del x
+    views = [[b[o:o + n].view(shape) for o, n, (_, shape) in zip(offs, wl.numels, wl.shapes)] for b in bufs]
+    return views[0], views[1]
+
+
 def _median(xs):
     xs = sorted(xs)
     if not xs:
@@ -275,6 +297,9 @@ def main():
     ap.add_argument("--log-steps", type=int, default=0,
                     help="after the timed region, run this many more steps reading the state after each and "
                          "print one [zs_step k] line per step (scale, skips, norm, clip, time)")
+    ap.add_argument("--one-draw", action="store_true",
+                    help="draw the parameters and gradients as views into one buffer each (one draw per buffer "
+                         "instead of one per tensor), for profiler runs that count every dispatch")
     ap.add_argument("--faults", action="store_true",
                     help="apply the workload's fault schedule (non-finite gradients on its fault steps, drawn for "
                          "--steps steps) in the timed steps and report the skipped steps' time separately")
@@ -319,8 +344,11 @@ def main():
     hp = wl.hparams
     log(f"workload {wl.name}: {len(wl.numels)} tensors, {wl.n_elems} elements, dp {wl.dp_world}")
     t_setup = time.perf_counter()
-    params = gen.make_params(wl, dev)
-    grads = gen.make_grads(wl, 1, wl.init_scale, dev, with_faults=False)
+    if args.one_draw:
+        params, grads = one_draw_inputs(torch, gen, wl, dev)
+    else:
+        params = gen.make_params(wl, dev)
+        grads = gen.make_grads(wl, 1, wl.init_scale, dev, with_faults=False)
     torch.cuda.synchronize()
     log(f"inputs resident after {time.perf_counter() - t_setup:.1f} s")
     G = max(1, args.grad_accum)
@@ -565,12 +593,13 @@ def main():
                    "accum_dtype": ("fp32" if accum is not None else wl.dtype),
                    "bucket_numel": args.bucket_numel or None, "buckets": len(buckets) if buckets else None,
                    "no_decay": args.no_decay, "state_spacing_gib": args.state_spacing_gib or None,
-                   "flat_views": views, "placement": opt.placement},
+                   "flat_views": views, "placement": opt.placement, "one_draw": args.one_draw},
         "achieved_hbm_gbps": step_gbps,
         "hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": step_bytes,
         "kernels_ms": {"pack_check": pack_ms, "adamw_cast_scatter": adamw_ms,
-                       "finalize_and_scaler": ms_per_step - pack_ms - adamw_ms},
+                       "finalize_and_scaler": sum(e[0].elapsed_time(e[5]) for e in applied) / len(applied)
+                       - pack_ms - adamw_ms},
         "unpack_after_allgather": unpack,
         "graph_replay": graph_replay,
         "faults": None if not args.faults else {
