@@ -1,0 +1,80 @@
+"""The measured placement of the optimizer's buffers (ZeroShardedAdamW(placement="tune")):
+choosing it changes nothing the caller can see.  The parameters are bit-identical after
+construction, and the tuned optimizer's steps equal those of one with four separate
+allocations bit for bit (the kernels are the same; only where the buffers sit differs)."""
+
+import pytest
+import torch
+
+from workloads import WORKLOADS, gen
+
+pytestmark = pytest.mark.gpu
+
+
+def _z():
+    import zero_sharded_mixed_buffer_amd as Z
+    Z.lib()
+    return Z
+
+
+def _bits(x):
+    return x.view(torch.int32 if x.element_size() == 4 else torch.int16)
+
+
+@pytest.mark.parametrize("name,views", [("llama_mini", False), ("moe_mini_dp4", False), ("ragged_mini", True)])
+def test_tuned_placement_is_invisible(monkeypatch, name, views):
+    import zero_sharded_mixed_buffer_amd.optimizer as OPT
+    Z = _z()
+    monkeypatch.setattr(OPT, "TUNE_MIN_ELEMENTS", 0)  # tune even these small shards
+    wl = WORKLOADS[name]
+    dev = torch.device("cuda", 0)
+    hp = wl.hparams
+    p0 = gen.make_params(wl, dev)
+    kw = dict(lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"], weight_decay=hp["weight_decay"],
+              max_norm=hp["max_norm"], dp_world=wl.dp_world, dp_rank=wl.dp_rank, align=wl.align,
+              dynamic_loss_scale=wl.dynamic, init_scale=wl.init_scale, flat_views=views)
+    pa = [p.clone() for p in p0]
+    pb = [p.clone() for p in p0]
+    a = Z.ZeroShardedAdamW(pa, placement="tune", **kw)
+    b = Z.ZeroShardedAdamW(pb, placement="separate", **kw)
+    torch.cuda.synchronize()
+    print(f"[case] placement {name} views={views}: {a.placement}", flush=True)
+    assert a.placement["mode"] == "tuned" and a.placement["candidates"] == 24
+    assert b.placement["mode"] == "separate"
+    assert all(torch.equal(_bits(x), _bits(y)) for x, y in zip(pa, p0)), "tuning changed the parameters"
+    for opt in (a, b):
+        assert torch.equal(_bits(opt.master.cpu()), _bits(b.master.cpu()))
+        assert int(torch.count_nonzero(opt.m)) == 0 and int(torch.count_nonzero(opt.v)) == 0
+    d, r = wl.dp_world, wl.dp_rank
+    S = a.shard_numel
+    exch = [torch.zeros(d, dtype=torch.float64, device=dev) for _ in range(2)]
+    for step in range(1, 4):
+        grads = gen.make_grads(wl, step, wl.init_scale, dev, with_faults=False)
+        for opt, params, ex in ((a, pa, exch[0]), (b, pb, exch[1])):
+            if views:
+                with torch.no_grad():
+                    for p, g in zip(params, grads):
+                        p.grad.copy_(g)
+                opt.step()
+            elif d == 1:
+                opt.step(grads)
+            else:  # this rank's step; the other ranks' partial sums from their shards of the same buffer
+                opt.pack(grads)
+                opt.check(local_sumsq_out=ex[r:r + 1])
+                for q in range(d):
+                    if q != r:
+                        lq = Z.zs_layout_create(wl.numels, d, q, wl.align)
+                        sq = Z.zs_state_create(lq, Z.state_host(wl.init_scale, 1.0, wl.dynamic, wl.growth_interval))
+                        Z.zs_unscale_check(lq, opt.flat[q * S:(q + 1) * S], opt.grad_dtype, sq, None, ex[q:q + 1])
+                        torch.cuda.synchronize()
+                        Z.zs_state_destroy(sq)
+                        Z.zs_layout_destroy(lq)
+                opt.norm(rank_sumsq=ex)
+                opt.update()
+        torch.cuda.synchronize()
+        for k in ("master", "m", "v"):
+            assert torch.equal(_bits(getattr(a, k).cpu()), _bits(getattr(b, k).cpu())), (step, k)
+        assert all(torch.equal(_bits(x), _bits(y)) for x, y in zip(pa, pb)), step
+        assert a.read_state() == b.read_state()
+    a.close()
+    b.close()

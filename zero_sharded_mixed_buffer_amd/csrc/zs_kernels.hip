@@ -8,9 +8,11 @@
 // device segment map (zs_internal.h): a tile of 4096 flat elements that lies inside one
 // tensor (every tile of a large tensor) takes a uniform fast path with one base pointer;
 // when that tensor's address is not 16-byte aligned (ragged lists), the tile goes through
-// LDS and is funnel-shifted into aligned 16-byte chunks.  Tiles that meet several segments
-// look each 8-element group up by binary search over the tile's few segments and fall back
-// to 2-byte accesses only where a group straddles a boundary.
+// LDS and is funnel-shifted into aligned 16-byte chunks.  A whole pack block that meets
+// several segments copies each segment's piece into LDS and reads its groups back; other
+// tiles that meet several segments (the update's scatter, the unpack, the edges of a
+// bucket's range) look each 8-element group up by binary search over the tile's few
+// segments and fall back to 2-byte accesses only where a group straddles a boundary.
 //
 // Numerics (the pages keep master weights and Adam moments in FP32 and ask for sensitive
 // reductions in higher precision - "Deep dive: Megatron", section "Precision"):
@@ -363,6 +365,34 @@ __device__ __forceinline__ double pack_block(const DevMap& mp, const uint64_t* p
       jlos[u] = 0;
       cnts[u] = kGroup;
       vals[u] = funnel16(stage[k], stage[k + 1], delta);
+    }
+  } else if (!EDGE && !ts.uniform) {
+    // A full block across segments: copy each segment's piece of the block into LDS in
+    // element order (consecutive lanes, consecutive elements; padding as zeros), then read
+    // the 8-element groups back.  One pass over the block's few segments replaces a segment
+    // search per group and 2-byte loads wherever a group's source is misaligned.
+    uint16_t* outb = reinterpret_cast<uint16_t*>(stage);
+    for (int sg = ts.lo; sg <= ts.hi; ++sg) {  // uniform across the workgroup
+      const int64_t sb = mp.seg_begin[sg], se = mp.seg_begin[sg + 1];
+      const int64_t a = sb > block_base ? sb : block_base;
+      const int64_t b = se < block_base + kPackBlock ? se : block_base + kPackBlock;
+      if (a >= b) continue;
+      const int32_t tensor = mp.seg_tensor[sg];
+      if (tensor < 0) {
+        for (int64_t e = a + threadIdx.x; e < b; e += kThreads) outb[e - block_base] = 0;
+      } else {
+        const uint16_t* src = reinterpret_cast<const uint16_t*>(ptrs[tensor]) + mp.seg_local[sg] + (a - sb);
+        for (int64_t e = a + threadIdx.x; e < b; e += kThreads)
+          outb[e - block_base] = __builtin_nontemporal_load(src + (e - a));
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kPackGroups; ++u) {
+      const v4u x = stage[u * kThreads + threadIdx.x];
+      jlos[u] = 0;
+      cnts[u] = kGroup;
+      vals[u] = G16{{x.x, x.y, x.z, x.w}};
     }
   } else {
 #pragma unroll
