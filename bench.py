@@ -527,7 +527,32 @@ def main():
             opt.update(stream=stream)
         torch.cuda.synchronize()
         t_s = time.perf_counter() - t_s
+        # GPU-only time per step: 50 steps captured in one graph, replayed, timed with events
+        # on the replay stream (the host issue cost of the calls drops out)
+        gpu_only = {}
+        for kind in ("zs_step", "four_calls"):
+            g50 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g50):
+                cap = torch.cuda.current_stream()
+                for _ in range(50):
+                    if kind == "zs_step":
+                        opt.step(grads, stream=cap)
+                    else:
+                        opt.pack(grads, cap)
+                        opt.norm(stream=cap)
+                        opt.update(stream=cap)
+            g50.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(4):
+                g50.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            gpu_only[kind] = e0.elapsed_time(e1) / 200
+            del g50
         graph_replay = {"ms_per_step": t_g * 1e3 / args.steps, "single_call_ms_per_step": t_e * 1e3 / args.steps,
+                        "gpu_only_ms_per_step": gpu_only,
                         "sequence_ms_per_step": t_s * 1e3 / args.steps}
         log(f"graph replay {graph_replay['ms_per_step']:.4f} ms/step, zs_step call by call "
             f"{graph_replay['single_call_ms_per_step']:.4f} ms/step, four-call sequence "
