@@ -33,6 +33,8 @@ constexpr int kXcds = 8;
 constexpr int64_t kXcdWhole = -1;
 constexpr int64_t kXcdRunAdamw = 16;
 constexpr int64_t kXcdRunPack = kXcdWhole;
+constexpr int64_t kXcdRunCheck = kXcdWhole;
+constexpr int64_t kXcdRunUnpack = kXcdWhole;
 // Workgroups launched for `units` units of work in the order of run length `run`.
 inline int64_t launch_units(int64_t units, int64_t run) {
   if (run == 0) return units;
@@ -41,7 +43,7 @@ inline int64_t launch_units(int64_t units, int64_t run) {
 }
 
 // Workgroups (and partial sums) of a pack or check pass over len elements.
-inline int64_t reduction_blocks(int64_t len) { return (len + kPackBlock - 1) / kPackBlock; }
+__host__ __device__ inline int64_t reduction_blocks(int64_t len) { return (len + kPackBlock - 1) / kPackBlock; }
 
 // Segment map of one flat range (a rank's shard or the whole buffer), in device memory.
 // Segment i covers range-relative [seg_begin[i], seg_begin[i+1]) and lies inside tensor

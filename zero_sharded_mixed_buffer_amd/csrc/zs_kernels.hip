@@ -277,10 +277,7 @@ __device__ __forceinline__ void scatter(const DevMap& mp, const uint64_t* ptrs, 
     st16_elem(dst, g, cnt);
 }
 
-// Work unit (tile or pack block) of this workgroup.
-__device__ __forceinline__ int64_t work_unit() { return blockIdx.x; }
-
-// Work unit of this workgroup among `units` in the XCD-aware order of run length RUN
+// Work unit (tile or pack block) of this workgroup among `units` in the XCD-aware order of run length RUN
 // (launched with launch_units(units, RUN) workgroups); -1 for the workgroups beyond the last
 // unit (fewer than one group).  The map is a bijection on the launched range.
 template <int64_t RUN>
@@ -544,11 +541,13 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) void k_check(const uint16_t* __restrict__ shard, int64_t n,
                                                     double* __restrict__ partials) {
   constexpr int kPackGroups = int(kPackBlock / (int64_t(kThreads) * kGroup));
+  const int64_t unit = ordered_unit<kXcdRunCheck>(reduction_blocks(n));
+  if (unit < 0) return;  // uniform across the workgroup
   const bool vec_ok = aligned16(shard);
   G16 vals[kPackGroups];
 #pragma unroll
   for (int u = 0; u < kPackGroups; ++u) {
-    const int64_t q = work_unit() * kPackBlock + int64_t(u * kThreads + threadIdx.x) * kGroup;
+    const int64_t q = unit * kPackBlock + int64_t(u * kThreads + threadIdx.x) * kGroup;
     const int cnt = group_count(n, q);
     vals[u] = (cnt == kGroup && vec_ok) ? ld16_vec(shard + q) : ld16_elem(shard + q, cnt);
   }
@@ -556,18 +555,20 @@ __global__ __launch_bounds__(kThreads) void k_check(const uint16_t* __restrict__
 #pragma unroll
   for (int u = 0; u < kPackGroups; ++u) acc += sumsq8<DT>(vals[u]);
   const double r = block_sum(acc);
-  if (threadIdx.x == 0) partials[blockIdx.x] = r;
+  if (threadIdx.x == 0) partials[unit] = r;
 }
 
 // The same pass over an fp32 shard (a gradient-accumulation buffer).
 __global__ __launch_bounds__(kThreads) void k_check_f32(const float* __restrict__ shard, int64_t n,
                                                         double* __restrict__ partials) {
   constexpr int kPackGroups = int(kPackBlock / (int64_t(kThreads) * kGroup));
+  const int64_t unit = ordered_unit<kXcdRunCheck>(reduction_blocks(n));
+  if (unit < 0) return;  // uniform across the workgroup
   const bool vec_ok = aligned16(shard);
   double acc = 0.0;
 #pragma unroll
   for (int u = 0; u < kPackGroups; ++u) {
-    const int64_t q = work_unit() * kPackBlock + int64_t(u * kThreads + threadIdx.x) * kGroup;
+    const int64_t q = unit * kPackBlock + int64_t(u * kThreads + threadIdx.x) * kGroup;
     const int cnt = group_count(n, q);
     float f[kGroup] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (cnt == kGroup && vec_ok) {
@@ -586,7 +587,7 @@ __global__ __launch_bounds__(kThreads) void k_check_f32(const float* __restrict_
     }
   }
   const double r = block_sum(acc);
-  if (threadIdx.x == 0) partials[blockIdx.x] = r;
+  if (threadIdx.x == 0) partials[unit] = r;
 }
 
 // First level of the fixed-order reduction of many partial sums: workgroup b adds
@@ -955,8 +956,9 @@ __global__ __launch_bounds__(kThreads) void k_unpack(DevMap mp, const void* __re
                                                      const DevState* __restrict__ skip,
                                                      const uint64_t* __restrict__ ptrs) {
   if (skip != nullptr && skip->h.overflow) return;
+  const int64_t tile = ordered_unit<kXcdRunUnpack>(mp.ntiles);
+  if (tile < 0) return;  // uniform across the workgroup
   const bool vec_ok = aligned16(src);
-  const int64_t tile = work_unit();
   {
     const TileSeg ts = tile_seg(mp, ptrs, tile);
     const int64_t base = tile * kTile;
@@ -1045,7 +1047,7 @@ hipError_t launch_check(const void* shard, int64_t n, int dt, double* partials, 
   const int64_t nb = reduction_blocks(n);
   if (nb == 0) return hipSuccess;
   const uint16_t* p = static_cast<const uint16_t*>(shard);
-  const dim3 G(static_cast<unsigned>(nb)), B(kThreads);
+  const dim3 G(static_cast<unsigned>(launch_units(nb, kXcdRunCheck))), B(kThreads);
   if (dt == ZS_BF16)
     hipLaunchKernelGGL((k_check<ZS_BF16>), G, B, 0, s, p, n, partials);
   else if (dt == ZS_FP16)
@@ -1213,7 +1215,7 @@ hipError_t launch_adamw(const DevMap& map, const void* shard, int grad_dt, float
 hipError_t launch_unpack(const DevMap& map, const void* src, int src_dt, const uint64_t* dst_ptrs, int dst_dt,
                          const DevState* skip, hipStream_t s) {
   if (map.ntiles == 0) return hipSuccess;
-  const dim3 G(static_cast<unsigned>(map.ntiles)), B(kThreads);
+  const dim3 G(static_cast<unsigned>(launch_units(map.ntiles, kXcdRunUnpack))), B(kThreads);
   const bool f32 = (src_dt == ZS_FP32);
   if (dst_dt == ZS_BF16) {
     if (f32)
