@@ -361,6 +361,9 @@ def main():
                              state_spacing=int(args.state_spacing_gib * (1 << 30)) or None,
                              flat_views=args.flat_views, placement=args.placement)
     log(f"placement of the optimizer's buffers: {opt.placement}")
+    # the placement tuning holds candidate allocations for a moment; the steps' peak is counted apart
+    construction_peak = torch.cuda.max_memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
     views = args.flat_views
     if views:
         if G != 1 or args.bucket_numel or args.graph:
@@ -657,6 +660,7 @@ def main():
                 f"norm={st_k['grad_norm']:.6g} clip={st_k['clip_coef']:.6g} ms={e0.elapsed_time(e1):.3f} "
                 f"elems/s={S / (e0.elapsed_time(e1) * 1e-3):.4g}")
     out["memory"] = {"max_allocated_gb": torch.cuda.max_memory_allocated() / 1e9,
+                     "construction_peak_gb": construction_peak / 1e9,
                      "device_total_gb": torch.cuda.get_device_properties(0).total_memory / 1e9}
     if args.ceilings:  # on the step's own buffers, which it overwrites: after every timed step
         out["ceilings"] = ceilings(torch, Z, opt, stream)

@@ -1,5 +1,6 @@
 """The measured placement of the optimizer's buffers (ZeroShardedAdamW(placement="tune")):
-choosing it changes nothing the caller can see.  The parameters are bit-identical after
+choosing it changes nothing the caller can see, and the candidate allocations it times are
+released.  The parameters are bit-identical after
 construction, and the tuned optimizer's steps equal those of one with four separate
 allocations bit for bit (the kernels are the same; only where the buffers sit differs)."""
 
@@ -40,6 +41,7 @@ def test_tuned_placement_is_invisible(monkeypatch, name, views):
     torch.cuda.synchronize()
     print(f"[case] placement {name} views={views}: {a.placement}", flush=True)
     assert a.placement["mode"] == "tuned" and a.placement["candidates"] == 24
+    assert a.placement["arenas"] == len(a.placement["arena_ms"]) == OPT.TUNE_MAX_ARENAS
     assert b.placement["mode"] == "separate"
     assert all(torch.equal(_bits(x), _bits(y)) for x, y in zip(pa, p0)), "tuning changed the parameters"
     for opt in (a, b):
@@ -78,3 +80,34 @@ def test_tuned_placement_is_invisible(monkeypatch, name, views):
         assert a.read_state() == b.read_state()
     a.close()
     b.close()
+
+
+def test_candidate_allocations_are_released(monkeypatch):
+    """The tuning holds several candidate allocations while it times them and keeps one: after
+    construction the optimizer holds exactly what it holds when it times a single candidate."""
+    import zero_sharded_mixed_buffer_amd.optimizer as OPT
+    Z = _z()
+    monkeypatch.setattr(OPT, "TUNE_MIN_ELEMENTS", 0)
+    wl = WORKLOADS["llama_mini"]
+    dev = torch.device("cuda", 0)
+    p0 = gen.make_params(wl, dev)
+    held = {}
+    for k in (1, 5):
+        monkeypatch.setattr(OPT, "TUNE_MAX_ARENAS", k)
+        params = [p.clone() for p in p0]
+        torch.cuda.synchronize()
+        before = torch.cuda.memory_allocated(dev)
+        opt = Z.ZeroShardedAdamW(params, placement="tune")
+        torch.cuda.synchronize()
+        held[k] = torch.cuda.memory_allocated(dev) - before
+        print(f"[case] candidates {k}: {opt.placement}, holds {held[k]} bytes", flush=True)
+        assert opt.placement["mode"] == "tuned"
+        if k == 1:
+            assert opt.placement["arenas"] == 1 and opt.placement["arena_ms"] == []
+        else:
+            assert opt.placement["arenas"] == k and len(opt.placement["arena_ms"]) == k
+            assert opt.placement["arena_ms"][opt.placement["arena_pick"]] == min(opt.placement["arena_ms"])
+        opt.close()
+        del opt, params
+    assert held[5] == held[1]
+

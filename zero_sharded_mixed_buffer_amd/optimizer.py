@@ -40,6 +40,10 @@ def pointer_table(tensors, device):
 # Shards of at least this many elements choose the placement of their buffers by measurement
 # (ZeroShardedAdamW._tune_placement); below it the update is too short for placement to show.
 TUNE_MIN_ELEMENTS = 1 << 26
+# The tuning first times up to this many separate allocations of the buffers, together using
+# at most this fraction of the free device memory, and keeps the fastest.
+TUNE_MAX_ARENAS = 8
+TUNE_ARENA_MEMORY_FRACTION = 0.5
 
 # Checkpoint format of ZeroShardedAdamW.state_dict(), and the state fields it keeps (the
 # others are results of the latest check and norm, recomputed by the next step).
@@ -114,9 +118,9 @@ class ZeroShardedAdamW:
         at most one dimension.
     state_spacing: carve master / m / v from one allocation this many bytes apart.
     placement: "tune" (default): a shard of at least TUNE_MIN_ELEMENTS elements carves the
-        gradient buffer and master / m / v from one allocation, in the order of the four
-        whose update measured fastest at construction (see _tune_placement); "separate":
-        four allocations.
+        gradient buffer and master / m / v from one allocation: the fastest of several
+        candidates, with the four in the order whose update measured fastest in it (see
+        _tune_placement); "separate": four allocations.
     flat_views: the parameters and their .grad become views into two flat buffers laid out
         like the gradient buffer (a contiguous parameter buffer and a contiguous gradient
         buffer that backward fills in place).  step() with no gradient list then checks the
@@ -203,6 +207,7 @@ class ZeroShardedAdamW:
         self._grad_ptrs = None
         self._grad_objs = []
         S = self.shard_numel
+        self.flat_param = None  # offload mode: the device buffer of the shard's new parameters
         self.placement = {"mode": "separate"}
         tune = (placement == "tune" and not self.offload and not state_spacing and S >= TUNE_MIN_ELEMENTS)
         if tune and self._tune_placement():
@@ -255,77 +260,93 @@ class ZeroShardedAdamW:
                 self._grad_views.append(p.grad)
 
     def _tune_placement(self):
-        """Carve the gradient buffer and master, m, v from one allocation, in the order (of
-        the 24) whose update runs fastest here, and seed the master.  On MI355X the streams
-        of the update run up to a few per cent faster or slower depending on where in HBM
-        they sit relative to one another (the physical-address hash that spreads them over
-        channels), and that varies with the memory an allocation receives; measuring the
-        real update on the real buffers is the reliable way to pick.  Each candidate is
-        timed with the update kernel itself at lr = 0 on zero gradients and moments, which
-        writes back the very (finite) parameters it reads (the master is the exact fp32
-        widening of the parameters, and their nearest-even cast is the parameters again), so
-        nothing the caller sees changes.  Returns False (nothing allocated) when the single allocation
-        does not fit."""
+        """Carve the gradient buffer and master, m, v from one allocation, choosing by
+        measurement both the allocation and the order of the four buffers in it, and seed the
+        master.  On MI355X the update's streams run at rates that depend on the physical
+        memory an allocation receives: separate allocations of the same size, held at once,
+        measured 5.6-5.8 or 6.3-6.5 TB/s and kept their rate from pass to pass, while the 24
+        orders within one allocation moved it by 2-4 %.  So the tuning times up to
+        TUNE_MAX_ARENAS candidate allocations (together at most TUNE_ARENA_MEMORY_FRACTION of
+        the free memory; one when only one fits), keeps the fastest, releases the others, and
+        then times the 24 orders in the one it kept.  Each timing runs the update kernel
+        itself at lr = 0 on zero gradients and moments, which writes back the very (finite)
+        parameters it reads (the master is the exact fp32 widening of the parameters, and
+        their nearest-even cast is the parameters again), so nothing the caller sees
+        changes.  Returns False (nothing allocated) when no allocation fits."""
         import itertools
         dev, S = self.device, self.shard_numel
         step = 1 << 21
         gbytes = torch.empty(0, dtype=self.grad_dtype).element_size()
         sizes = {"flat": self.flat_numel * gbytes, "master": 4 * S, "m": 4 * S, "v": 4 * S}
         padded = {k: (b + step - 1) // step * step for k, b in sizes.items()}
-        try:
-            arena = torch.empty(sum(padded.values()), dtype=torch.uint8, device=dev)
-        except torch.cuda.OutOfMemoryError:
+        total = sum(padded.values())
+        free, _ = torch.cuda.mem_get_info(dev)
+        n_arenas = max(1, min(TUNE_MAX_ARENAS, int(free * TUNE_ARENA_MEMORY_FRACTION) // total))
+        arenas = []
+        for _ in range(n_arenas):
+            try:
+                arenas.append(torch.empty(total, dtype=torch.uint8, device=dev))
+            except torch.cuda.OutOfMemoryError:
+                break
+        if not arenas:
             return False
         dtypes = {"flat": self.grad_dtype, "master": torch.float32, "m": torch.float32, "v": torch.float32}
         numel = {"flat": self.flat_numel, "master": S, "m": S, "v": S}
 
-        def carve(order):
+        def carve(arena, order):
             out, off = {}, 0
             for k in order:
                 out[k] = arena[off:off + sizes[k]].view(dtypes[k])[:numel[k]]
                 off += padded[k]
             return out
 
+        def seed(b):
+            b["flat"].zero_()
+            b["m"].zero_()
+            b["v"].zero_()
+            A.zs_pack(self.layout, self.param_ptrs, self.param_dtype, b["master"], torch.float32,
+                      whole_flat=False, stream=stream)
+
         hp = self.hp
         frozen = A.hparams(0.0, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.max_norm)
         out_flat = self.param_shard if self.flat_views else None
         ptrs = None if self.flat_views else self.param_ptrs
         stream = torch.cuda.current_stream(dev)
-        times = {}
+
+        def update_ms(b):
+            """The faster of two timed updates after an untimed one (lr 0, see above)."""
+            seed(b)
+            shard = b["flat"][self.shard_begin:self.shard_begin + S]
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            for k in range(3):
+                if k:
+                    ev[k - 1].record(stream)
+                A.zs_adamw_step(self.layout, shard, self.grad_dtype, b["master"], b["m"], b["v"], frozen, self.state,
+                                ptrs, out_flat, self.param_dtype, stream=stream)
+            ev[2].record(stream)
+            ev[2].synchronize()
+            return min(ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]))
+
+        names = ("flat", "master", "m", "v")
         with torch.cuda.device(dev):
-            for order in itertools.permutations(("flat", "master", "m", "v")):
-                b = carve(order)
-                b["flat"].zero_()
-                b["m"].zero_()
-                b["v"].zero_()
-                A.zs_pack(self.layout, self.param_ptrs, self.param_dtype, b["master"], torch.float32,
-                          whole_flat=False, stream=stream)
-                shard = b["flat"][self.shard_begin:self.shard_begin + S]
-                ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-                A.zs_adamw_step(self.layout, shard, self.grad_dtype, b["master"], b["m"], b["v"], frozen, self.state,
-                                ptrs, out_flat, self.param_dtype, stream=stream)
-                ev[0].record(stream)
-                A.zs_adamw_step(self.layout, shard, self.grad_dtype, b["master"], b["m"], b["v"], frozen, self.state,
-                                ptrs, out_flat, self.param_dtype, stream=stream)
-                ev[1].record(stream)
-                A.zs_adamw_step(self.layout, shard, self.grad_dtype, b["master"], b["m"], b["v"], frozen, self.state,
-                                ptrs, out_flat, self.param_dtype, stream=stream)
-                ev[2].record(stream)
-                ev[2].synchronize()
-                times["".join(k[0] if k != "master" else "M" for k in order)] = min(ev[0].elapsed_time(ev[1]),
-                                                                                   ev[1].elapsed_time(ev[2]))
+            arena_ms = [update_ms(carve(a, names)) for a in arenas] if len(arenas) > 1 else []
+            pick = min(range(len(arena_ms)), key=arena_ms.__getitem__) if arena_ms else 0
+            arena = arenas[pick]
+            del arenas
+            if arena_ms:
+                torch.cuda.empty_cache()  # hand the candidates not kept back to the device
+            times = {}
+            for order in itertools.permutations(names):
+                times["".join(k[0] if k != "master" else "M" for k in order)] = update_ms(carve(arena, order))
             best = min(times, key=times.get)
-            order = [{"f": "flat", "M": "master", "m": "m", "v": "v"}[c] for c in best]
-            b = carve(order)
-            b["flat"].zero_()
-            b["m"].zero_()
-            b["v"].zero_()
-            A.zs_pack(self.layout, self.param_ptrs, self.param_dtype, b["master"], torch.float32, whole_flat=False,
-                      stream=stream)
+            b = carve(arena, [{"f": "flat", "M": "master", "m": "m", "v": "v"}[c] for c in best])
+            seed(b)
         self._arena = arena
         self.flat, self.master, self.m, self.v = b["flat"], b["master"], b["m"], b["v"]
         self.placement = {"mode": "tuned", "order": best, "update_ms": times[best],
-                          "update_ms_range": [min(times.values()), max(times.values())], "candidates": len(times)}
+                          "update_ms_range": [min(times.values()), max(times.values())], "candidates": len(times),
+                          "arenas": max(1, len(arena_ms)), "arena_pick": pick,
+                          "arena_ms": [round(t, 4) for t in arena_ms]}
         return True
 
     def _seed_flat_param(self):
