@@ -359,7 +359,8 @@ def main():
                              init_scale=wl.init_scale, growth_interval=wl.growth_interval, accum_dtype=accum,
                              no_decay="1d" if args.no_decay == "1d" else None,
                              state_spacing=int(args.state_spacing_gib * (1 << 30)) or None,
-                             flat_views=args.flat_views, placement=args.placement)
+                             flat_views=args.flat_views, placement=args.placement,
+                             allgather_input=wl.dp_world > 1 and not args.flat_views)
     log(f"placement of the optimizer's buffers: {opt.placement}")
     # the placement tuning holds candidate allocations for a moment; the steps' peak is counted apart
     construction_peak = torch.cuda.max_memory_allocated()
@@ -387,7 +388,7 @@ def main():
     # partial sums come from their shards of the same buffer, computed once beforehand
     # (on a real group the other GPUs compute them).
     exchange = torch.zeros(d, dtype=torch.float64, device=dev) if d > 1 else None
-    flat_param = torch.empty(S, dtype=opt.param_dtype, device=dev) if d > 1 and not views else None
+    flat_param = opt.flat_param if d > 1 and not views else None  # the optimizer's all-gather input
     if d > 1:
         if not views:
             opt.pack(grads, stream)

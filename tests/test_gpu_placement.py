@@ -111,3 +111,61 @@ def test_candidate_allocations_are_released(monkeypatch):
         del opt, params
     assert held[5] == held[1]
 
+
+
+@pytest.mark.parametrize("placement", ["tune", "separate"])
+def test_owned_allgather_input_matches_flat_param_out(monkeypatch, placement):
+    """allgather_input=True: the optimizer's own all-gather input (carved from the tuned
+    arena, or allocated apart) starts as the shard's parameters, and update(scatter=False)
+    writes it with exactly what update(flat_param_out=...) writes into a caller's buffer,
+    step after step."""
+    import zero_sharded_mixed_buffer_amd.optimizer as OPT
+    Z = _z()
+    monkeypatch.setattr(OPT, "TUNE_MIN_ELEMENTS", 0)
+    wl = WORKLOADS["moe_mini_dp4"]
+    dev = torch.device("cuda", 0)
+    hp = wl.hparams
+    p0 = gen.make_params(wl, dev)
+    kw = dict(lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"], weight_decay=hp["weight_decay"],
+              max_norm=hp["max_norm"], dp_world=wl.dp_world, dp_rank=wl.dp_rank, align=wl.align,
+              dynamic_loss_scale=wl.dynamic, init_scale=wl.init_scale)
+    a = Z.ZeroShardedAdamW([p.clone() for p in p0], placement=placement, allgather_input=True, **kw)
+    b = Z.ZeroShardedAdamW([p.clone() for p in p0], placement="separate", **kw)
+    assert b.flat_param is None
+    assert a.placement["mode"] == ("tuned" if placement == "tune" else "separate")
+    if placement == "tune":
+        lo, hi = a._arena.data_ptr(), a._arena.data_ptr() + a._arena.numel()
+        assert lo <= a.flat_param.data_ptr() and a.flat_param.data_ptr() + 2 * a.shard_numel <= hi
+    offsets = Z.zs_plan(wl.numels, wl.dp_world, wl.dp_rank, wl.align)[0]
+    whole = torch.zeros(a.flat_numel, dtype=p0[0].dtype, device=dev)
+    for p, off in zip(p0, offsets):
+        whole[off:off + p.numel()] = p.reshape(-1)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(a.flat_param), _bits(whole[a.shard_begin:a.shard_begin + a.shard_numel]))
+    out_b = torch.full((b.shard_numel,), -1.0, dtype=b.param_dtype, device=dev)
+    r = wl.dp_rank
+    exch = torch.zeros(wl.dp_world, dtype=torch.float64, device=dev)
+    for step in range(1, 4):
+        grads = gen.make_grads(wl, step, wl.init_scale, dev, with_faults=False)
+        for opt in (a, b):  # the other ranks' partial sums stay zero: the same for both
+            opt.pack(grads)
+            opt.check(local_sumsq_out=exch[r:r + 1])
+        a.norm(rank_sumsq=exch)
+        b.norm(rank_sumsq=exch)
+        a.update(scatter=False)
+        b.update(scatter=False, flat_param_out=out_b)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(a.flat_param), _bits(out_b)), step
+        for k in ("master", "m", "v"):
+            assert torch.equal(_bits(getattr(a, k)), _bits(getattr(b, k))), (step, k)
+    a.close()
+    b.close()
+
+
+def test_allgather_input_needs_several_ranks_without_views():
+    Z = _z()
+    wl = WORKLOADS["llama_mini"]
+    dev = torch.device("cuda", 0)
+    params = gen.make_params(wl, dev)
+    with pytest.raises(ValueError, match="allgather_input"):
+        Z.ZeroShardedAdamW(params, allgather_input=True)

@@ -126,13 +126,17 @@ class ZeroShardedAdamW:
         buffer that backward fills in place).  step() with no gradient list then checks the
         buffer and writes the new parameters straight into the parameter buffer: no pack
         and no scatter.
+    allgather_input: with dp_world > 1 on the GPU (no flat views, no offload), the optimizer
+        owns self.flat_param, this rank's slice of the all-gather input (2 bytes per shard
+        element), seeded with the shard's parameters, placed with the tuned buffers and
+        written by update(scatter=False).  Without it the caller passes flat_param_out.
     """
 
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, max_norm=1.0,
                  dp_world=1, dp_rank=0, align=1, dynamic_loss_scale=None, init_scale=None, scale_floor=1.0,
                  growth_interval=1000, grad_dtype=None, accum_dtype=None, offload=False,
                  offload_chunk=1 << 24, offload_threads=0, no_decay=None, state_spacing=None,
-                 flat_views=False, placement="tune"):
+                 flat_views=False, placement="tune", allgather_input=False):
         params = list(params)
         if not params:
             raise ValueError("empty parameter list")
@@ -207,11 +211,17 @@ class ZeroShardedAdamW:
         self._grad_ptrs = None
         self._grad_objs = []
         S = self.shard_numel
-        self.flat_param = None  # offload mode: the device buffer of the shard's new parameters
+        # the device buffer of the shard's new parameters: offload mode's, or the all-gather
+        # input that allgather_input asks for
+        self.flat_param = None
+        owns_out = bool(allgather_input)
+        if owns_out and (dp_world == 1 or self.flat_views or self.offload):
+            raise ValueError("allgather_input is for dp_world > 1 on the GPU without flat_views (offload mode and "
+                             "flat views have their own parameter shard buffer)")
         self.placement = {"mode": "separate"}
         tune = (placement == "tune" and not self.offload and not state_spacing and S >= TUNE_MIN_ELEMENTS)
-        if tune and self._tune_placement():
-            pass  # flat, master, m and v carved from the arena, master seeded
+        if tune and self._tune_placement(owns_out):
+            pass  # flat, master, m, v (and the all-gather input) carved from the arena, master seeded
         elif not self.offload and state_spacing:
             self.flat = torch.zeros(self.flat_numel, dtype=self.grad_dtype, device=dev)
             # master, m and v carved from one allocation, `state_spacing` bytes apart (at
@@ -224,12 +234,18 @@ class ZeroShardedAdamW:
             self.m = self._state_arena[gap:gap + S]
             self.v = self._state_arena[2 * gap:2 * gap + S]
             A.zs_pack(self.layout, self.param_ptrs, self.param_dtype, self.master, torch.float32, whole_flat=False)
+            if owns_out:
+                self.flat_param = torch.empty(S, dtype=self.param_dtype, device=dev)
+                self._seed_flat_param()
         elif not self.offload:
             self.flat = torch.zeros(self.flat_numel, dtype=self.grad_dtype, device=dev)
             self.master = torch.empty(S, dtype=torch.float32, device=dev)
             self.m = torch.zeros(S, dtype=torch.float32, device=dev)
             self.v = torch.zeros(S, dtype=torch.float32, device=dev)
             A.zs_pack(self.layout, self.param_ptrs, self.param_dtype, self.master, torch.float32, whole_flat=False)
+            if owns_out:
+                self.flat_param = torch.empty(S, dtype=self.param_dtype, device=dev)
+                self._seed_flat_param()
         else:
             # Optimizer state in host memory (only the CPU touches it, so it need not be
             # pinned), pinned two-chunk staging buffers for the copies, and the device buffer
@@ -259,10 +275,11 @@ class ZeroShardedAdamW:
                 p.grad = self.flat[off:off + n].view(p.shape)
                 self._grad_views.append(p.grad)
 
-    def _tune_placement(self):
+    def _tune_placement(self, owns_out=False):
         """Carve the gradient buffer and master, m, v from one allocation, choosing by
         measurement both the allocation and the order of the four buffers in it, and seed the
-        master.  On MI355X the update's streams run at rates that depend on the physical
+        master; with owns_out the rank's slice of the all-gather input follows the four in
+        the allocation, and every timing writes it as the step's update does.  On MI355X the update's streams run at rates that depend on the physical
         memory an allocation receives: separate allocations of the same size, held at once,
         measured 5.6-5.8 or 6.3-6.5 TB/s and kept their rate from pass to pass, while the 24
         orders within one allocation moved it by 2-4 %.  So the tuning times up to
@@ -278,6 +295,8 @@ class ZeroShardedAdamW:
         step = 1 << 21
         gbytes = torch.empty(0, dtype=self.grad_dtype).element_size()
         sizes = {"flat": self.flat_numel * gbytes, "master": 4 * S, "m": 4 * S, "v": 4 * S}
+        if owns_out:
+            sizes["out"] = S * torch.empty(0, dtype=self.param_dtype).element_size()
         padded = {k: (b + step - 1) // step * step for k, b in sizes.items()}
         total = sum(padded.values())
         free, _ = torch.cuda.mem_get_info(dev)
@@ -290,12 +309,13 @@ class ZeroShardedAdamW:
                 break
         if not arenas:
             return False
-        dtypes = {"flat": self.grad_dtype, "master": torch.float32, "m": torch.float32, "v": torch.float32}
-        numel = {"flat": self.flat_numel, "master": S, "m": S, "v": S}
+        dtypes = {"flat": self.grad_dtype, "master": torch.float32, "m": torch.float32, "v": torch.float32,
+                  "out": self.param_dtype}
+        numel = {"flat": self.flat_numel, "master": S, "m": S, "v": S, "out": S}
 
         def carve(arena, order):
             out, off = {}, 0
-            for k in order:
+            for k in (*order, "out") if owns_out else order:
                 out[k] = arena[off:off + sizes[k]].view(dtypes[k])[:numel[k]]
                 off += padded[k]
             return out
@@ -309,14 +329,16 @@ class ZeroShardedAdamW:
 
         hp = self.hp
         frozen = A.hparams(0.0, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.max_norm)
-        out_flat = self.param_shard if self.flat_views else None
-        ptrs = None if self.flat_views else self.param_ptrs
+        # the update the step makes: into the parameter buffer (views), into the all-gather
+        # input (owns_out), or scattered into the parameters
+        ptrs = None if (self.flat_views or owns_out) else self.param_ptrs
         stream = torch.cuda.current_stream(dev)
 
         def update_ms(b):
             """The faster of two timed updates after an untimed one (lr 0, see above)."""
             seed(b)
             shard = b["flat"][self.shard_begin:self.shard_begin + S]
+            out_flat = self.param_shard if self.flat_views else b.get("out")
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
             for k in range(3):
                 if k:
@@ -343,6 +365,9 @@ class ZeroShardedAdamW:
             seed(b)
         self._arena = arena
         self.flat, self.master, self.m, self.v = b["flat"], b["master"], b["m"], b["v"]
+        if owns_out:
+            self.flat_param = b["out"]
+            self._seed_flat_param()
         self.placement = {"mode": "tuned", "order": best, "update_ms": times[best],
                           "update_ms_range": [min(times.values()), max(times.values())], "candidates": len(times),
                           "arenas": max(1, len(arena_ms)), "arena_pick": pick,
@@ -350,9 +375,10 @@ class ZeroShardedAdamW:
         return True
 
     def _seed_flat_param(self):
-        """Offload mode without flat views: copy this rank's parameters (bit for bit) into
-        the flat parameter shard that the offloaded update writes."""
-        if self.offload and not self.flat_views:
+        """Without flat views: copy this rank's parameters (bit for bit) into the flat
+        parameter shard that the update writes (offload mode, or allgather_input), so that it
+        is valid before the first applied step and after a skipped one."""
+        if self.flat_param is not None and not self.flat_views:
             A.zs_pack(self.layout, self.param_ptrs, self.param_dtype, self.flat_param, self.param_dtype,
                       whole_flat=False)
 
@@ -443,7 +469,8 @@ class ZeroShardedAdamW:
     def update(self, scatter=True, flat_param_out=None, stream=None):
         """AdamW on the shard, then the new parameters: scattered into the parameter tensors
         (scatter), written to flat_param_out, or with flat_views written into the rank's slice
-        of the parameter buffer; then the scaler commit."""
+        of the parameter buffer; then the scaler commit.  With allgather_input,
+        scatter=False without flat_param_out writes self.flat_param."""
         flat_param_out = self._device_arg(flat_param_out, "flat_param_out", self.param_dtype, self.shard_numel)
         if self.offload:
             # The host updates the state chunk by chunk; the new parameters of the shard land
@@ -463,8 +490,11 @@ class ZeroShardedAdamW:
             A.zs_adamw_step(self.layout, self.shard, self.grad_dtype, self.master, self.m, self.v, self.hp,
                             self.state, None, self.param_shard, self.param_dtype, stream=stream)
         else:
+            out = flat_param_out
+            if out is None and not scatter:
+                out = self.flat_param  # the owned all-gather input, or None: the state only
             A.zs_adamw_step(self.layout, self.shard, self.grad_dtype, self.master, self.m, self.v, self.hp,
-                            self.state, self.param_ptrs if scatter else None, flat_param_out, self.param_dtype,
+                            self.state, self.param_ptrs if scatter else None, out, self.param_dtype,
                             stream=stream)
         A.zs_scaler_update(self.state, stream=stream)
 
@@ -558,8 +588,9 @@ class ZeroShardedAdamW:
         """Restore a state_dict() of this rank's layout (the same tensor sizes, dp_world,
         dp_rank and align; reshard_state_dicts() maps a checkpoint taken at another dp_world).
         Writes the scaler and step counters and the master, m and v shard; the model-dtype
-        parameters are restored by the model, as with torch.optim, before this call (with
-        offload=True the flat parameter shard is refilled from them here)."""
+        parameters are restored by the model, as with torch.optim, before this call (the
+        flat parameter shard of offload=True or allgather_input=True is refilled from them
+        here)."""
         if sd.get("format") != STATE_FORMAT:
             raise ValueError(f"not a {STATE_FORMAT} state dict")
         lay = sd["layout"]
@@ -575,8 +606,8 @@ class ZeroShardedAdamW:
         self.write_state({k: sd["state"][k] for k in PERSISTENT_STATE}, stream)
         for k in ("master", "m", "v"):
             getattr(self, k).copy_(sd[k].reshape(-1))
-        # offloaded: the flat parameter shard follows the parameters, which the model restores
-        # first (restore the model's parameters before the optimizer's state)
+        # the flat parameter shard (offload, allgather_input) follows the parameters, which the
+        # model restores first (restore the model's parameters before the optimizer's state)
         self._seed_flat_param()
         torch.cuda.synchronize(self.device)
 
