@@ -622,7 +622,8 @@ def main():
                    "accum_dtype": ("fp32" if accum is not None else wl.dtype),
                    "bucket_numel": args.bucket_numel or None, "buckets": len(buckets) if buckets else None,
                    "no_decay": args.no_decay, "state_spacing_gib": args.state_spacing_gib or None,
-                   "flat_views": views, "placement": opt.placement, "one_draw": args.one_draw},
+                   "flat_views": views, "placement": opt.placement,
+                   "allgather_input_owned": opt.flat_param is not None, "one_draw": args.one_draw},
         "achieved_hbm_gbps": step_gbps,
         "hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": step_bytes,
