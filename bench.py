@@ -317,7 +317,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU: the per-rank step runs on one MI355X with no "
+        print(json.dumps({"error": "this benchmark measures one GPU: the per-rank step runs on one MI355X with no "
                                    "collectives, so --gpus must be 1"}))
         sys.exit(2)
 
