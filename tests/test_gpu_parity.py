@@ -205,6 +205,11 @@ def _edge_case(numels, dtype, dp_world=1, dp_rank=0, align=1, steps=3, zero_grad
     ([7, 9, 4097, 1, 8191], torch.bfloat16, 3, 2, 1),   # last shard, tail padding
     ([4096 * 3 + 5, 11, 2], torch.float16, 2, 1, 8),    # straddling tensor, aligned starts
     ([1000] * 40, torch.bfloat16, 4, 3, 64),            # gaps + padding
+    ([255] * 70, torch.bfloat16, 1, 0, 1),              # 16-17 segments per pack block: either side of
+                                                        # the chunked path's limit
+    ([273] * 60 + [4099, 3], torch.float16, 2, 1, 1),   # 15-16 misaligned segments per pack block
+    ([701] * 30, torch.bfloat16, 1, 0, 8),              # misaligned pieces and padding in one pack block
+    ([1] * 5000 + [4097], torch.bfloat16, 1, 0, 1),     # thousands of segments per pack block
 ])
 def test_edge_case_lists(numels, dtype, d, r, align):
     print(f"[case] edge numels={numels} d={d} r={r} align={align}", flush=True)

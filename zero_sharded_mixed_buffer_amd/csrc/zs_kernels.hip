@@ -334,16 +334,23 @@ __device__ __forceinline__ G16 gather16_masked(const DevMap& mp, const uint64_t*
 
 constexpr int kPackGroups = int(kPackBlock / (int64_t(kThreads) * kGroup));
 constexpr int kPackChunks = int(kPackBlock / kGroup);  // 16-byte chunks of one block
+// A block across at most kMixPieces segments loads its pieces as whole 16-byte chunks: a
+// piece of n elements starting d elements into a chunk takes ceil((d + n) / 8) chunks, so
+// the pieces of one block take at most kPackChunks + 2 * kMixPieces of them.
+constexpr int kMixPieces = 16;
+constexpr int kStageChunks = kPackChunks + 2 * kMixPieces;
+constexpr int kPadPiece = -(1 << 30);  // a padding piece: its elements are zero
 
 // One block of the pack: elements [block_base, block_base + kPackBlock) of the flat range,
 // of which only those in [lo, end) are read from the tensors and written.  EDGE = false
 // promises that the whole block lies in [lo, end), so every group is full and needs no
 // mask.  Returns this thread's share of the sum of squares of the written values (CHECK).
-// `stage` (kPackChunks + 1 chunks) and `wide` (kPackBlock floats) are the block's LDS.
+// `stage` (kStageChunks chunks), `wide` (kPackBlock floats) and the piece tables `mix_lo`,
+// `mix_off` (kMixPieces entries) are the block's LDS.
 template <int SDT, bool TO_F32, bool ACC, bool CHECK, bool EDGE>
 __device__ __forceinline__ double pack_block(const DevMap& mp, const uint64_t* ptrs, void* dst, const TileSeg& ts,
                                              int64_t block_base, int64_t lo, int64_t end, v4u* stage,
-                                             float* wide) {
+                                             float* wide, int* mix_lo, int* mix_off) {
   G16 vals[kPackGroups];
   int jlos[kPackGroups];
   int cnts[kPackGroups];
@@ -363,10 +370,62 @@ __device__ __forceinline__ double pack_block(const DevMap& mp, const uint64_t* p
       cnts[u] = kGroup;
       vals[u] = funnel16(stage[k], stage[k + 1], delta);
     }
+  } else if (!EDGE && !ts.uniform && ts.hi - ts.lo < kMixPieces) {
+    // A full block across a few segments: load each tensor piece of the block as the
+    // aligned 16-byte chunks that cover it (a chunk holding any byte of the piece lies in the
+    // piece's page) into LDS, one piece after the other, then give each element of a lane's
+    // group the LDS element of its piece (padding reads as zero).  The block's loads stay
+    // 16 bytes wide wherever its pieces start.
+    const uint16_t* raw = reinterpret_cast<const uint16_t*>(stage);
+    int r = 0;  // chunks loaded so far, uniform across the workgroup
+    for (int pc = 0; pc <= ts.hi - ts.lo; ++pc) {  // uniform across the workgroup
+      const int sg = ts.lo + pc;
+      const int64_t sb = mp.seg_begin[sg], se = mp.seg_begin[sg + 1];
+      const int64_t a = sb > block_base ? sb : block_base;
+      const int64_t b = se < block_base + kPackBlock ? se : block_base + kPackBlock;
+      const int32_t tensor = mp.seg_tensor[sg];
+      int off = kPadPiece;
+      if (tensor >= 0 && a < b) {
+        const uint16_t* src = reinterpret_cast<const uint16_t*>(ptrs[tensor]) + mp.seg_local[sg] + (a - sb);
+        const uintptr_t c0 = reinterpret_cast<uintptr_t>(src) & ~uintptr_t(15);
+        const int d = int((reinterpret_cast<uintptr_t>(src) - c0) >> 1);
+        const int nch = int((d + (b - a) + kGroup - 1) / kGroup);
+        const v4u* chunks = reinterpret_cast<const v4u*>(c0);
+        for (int i = threadIdx.x; i < nch; i += kThreads) stage[r + i] = ld_v4u(chunks + i);
+        off = r * kGroup + d - int(a - block_base);  // LDS element of block element e: off + e
+        r += nch;
+      }
+      if (threadIdx.x == 0) {
+        mix_lo[pc] = int(a - block_base);
+        mix_off[pc] = off;
+      }
+    }
+    __syncthreads();
+    const int np = ts.hi - ts.lo + 1;
+#pragma unroll
+    for (int u = 0; u < kPackGroups; ++u) {
+      const int e0 = (u * kThreads + threadIdx.x) * kGroup;
+      int offs[kGroup];
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) offs[j] = mix_off[0];
+      for (int pc = 1; pc < np; ++pc) {  // uniform across the workgroup
+        const int lo_p = mix_lo[pc], off_p = mix_off[pc];
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j)
+          if (e0 + j >= lo_p) offs[j] = off_p;
+      }
+      G16 g = g16_zero();
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j)
+        if (offs[j] != kPadPiece) g.set(j, raw[offs[j] + e0 + j]);
+      jlos[u] = 0;
+      cnts[u] = kGroup;
+      vals[u] = g;
+    }
   } else if (!EDGE && !ts.uniform) {
-    // A full block across segments: copy each segment's piece of the block into LDS in
+    // A full block across many segments: copy each segment's piece of the block into LDS in
     // element order (consecutive lanes, consecutive elements; padding as zeros), then read
-    // the 8-element groups back.  One pass over the block's few segments replaces a segment
+    // the 8-element groups back.  One pass over the block's segments replaces a segment
     // search per group and 2-byte loads wherever a group's source is misaligned.
     uint16_t* outb = reinterpret_cast<uint16_t*>(stage);
     for (int sg = ts.lo; sg <= ts.hi; ++sg) {  // uniform across the workgroup
@@ -516,8 +575,9 @@ template <int SDT, bool TO_F32, bool ACC, bool CHECK>
 __global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __restrict__ ptrs,
                                                    void* __restrict__ dst, double* __restrict__ partials,
                                                    int64_t blk0, int64_t nblk, int64_t lo, int64_t hi) {
-  __shared__ v4u stage[kPackChunks + 1];
+  __shared__ v4u stage[kStageChunks];
   __shared__ float wide[TO_F32 ? kPackBlock : 1];
+  __shared__ int mix_lo[kMixPieces], mix_off[kMixPieces];
   const int64_t unit = ordered_unit<kXcdRunPack>(nblk);
   if (unit < 0) return;  // uniform across the workgroup
   const int64_t block_base = (blk0 + unit) * kPackBlock;
@@ -527,8 +587,10 @@ __global__ __launch_bounds__(kThreads) void k_pack(DevMap mp, const uint64_t* __
   // uniform across the workgroup: no element of the block is clipped
   const bool whole = block_base >= lo && block_base + kPackBlock <= end;
   const double acc = whole
-      ? pack_block<SDT, TO_F32, ACC, CHECK, false>(mp, ptrs, dst, ts, block_base, lo, end, stage, wide)
-      : pack_block<SDT, TO_F32, ACC, CHECK, true>(mp, ptrs, dst, ts, block_base, lo, end, stage, wide);
+      ? pack_block<SDT, TO_F32, ACC, CHECK, false>(mp, ptrs, dst, ts, block_base, lo, end, stage, wide, mix_lo,
+                                                    mix_off)
+      : pack_block<SDT, TO_F32, ACC, CHECK, true>(mp, ptrs, dst, ts, block_base, lo, end, stage, wide, mix_lo,
+                                                   mix_off);
   if (CHECK) {
     const double r = block_sum(acc);
     if (threadIdx.x == 0) partials[unit] = r;
