@@ -80,6 +80,12 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ v4u ld_v4u(const void* p) { return __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p)); }
+// The same load through a global-address-space pointer: a global (not flat) load, which the
+// compiler can keep in flight across the LDS writes that follow it.
+typedef __attribute__((address_space(1))) const v4u gv4u;
+__device__ __forceinline__ v4u ld_v4u_global(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<gv4u*>(reinterpret_cast<uintptr_t>(p)));
+}
 __device__ __forceinline__ void st_v4u(void* p, v4u x) { __builtin_nontemporal_store(x, reinterpret_cast<v4u*>(p)); }
 __device__ __forceinline__ v4f ld_v4f(const float* p) { return __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p)); }
 __device__ __forceinline__ void st_v4f(float* p, v4f x) { __builtin_nontemporal_store(x, reinterpret_cast<v4f*>(p)); }
@@ -339,6 +345,8 @@ constexpr int kPackChunks = int(kPackBlock / kGroup);  // 16-byte chunks of one 
 // the pieces of one block take at most kPackChunks + 2 * kMixPieces of them.
 constexpr int kMixPieces = 16;
 constexpr int kStageChunks = kPackChunks + 2 * kMixPieces;
+static_assert(kStageChunks <= 3 * kThreads, "a piece's chunks take at most three loads per lane");
+static_assert(kPackChunks % kThreads == 0, "the staged block's chunks split evenly over the lanes");
 constexpr int kPadPiece = -(1 << 30);  // a padding piece: its elements are zero
 
 // One block of the pack: elements [block_base, block_base + kPackBlock) of the flat range,
@@ -360,8 +368,17 @@ __device__ __forceinline__ double pack_block(const DevMap& mp, const uint64_t* p
   const bool staged = !EDGE && ts.uniform && ts.base != nullptr && delta != 0 && block_base - delta >= ts.seg_b &&
                       block_base - delta + kPackBlock + kGroup <= ts.seg_e;
   if (staged) {
+    // every load issued before the first LDS write: one memory latency per block
     const v4u* chunk = reinterpret_cast<const v4u*>(ts.base + (block_base - delta));
-    for (int i = threadIdx.x; i <= kPackChunks; i += kThreads) stage[i] = ld_v4u(chunk + i);
+    constexpr int kPer = kPackChunks / kThreads;
+    v4u c[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) c[j] = ld_v4u_global(chunk + j * kThreads + threadIdx.x);
+    v4u tail = v4u{0u, 0u, 0u, 0u};
+    if (threadIdx.x == 0) tail = ld_v4u_global(chunk + kPackChunks);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) stage[j * kThreads + threadIdx.x] = c[j];
+    if (threadIdx.x == 0) stage[kPackChunks] = tail;
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kPackGroups; ++u) {
@@ -391,7 +408,19 @@ __device__ __forceinline__ double pack_block(const DevMap& mp, const uint64_t* p
         const int d = int((reinterpret_cast<uintptr_t>(src) - c0) >> 1);
         const int nch = int((d + (b - a) + kGroup - 1) / kGroup);
         const v4u* chunks = reinterpret_cast<const v4u*>(c0);
-        for (int i = threadIdx.x; i < nch; i += kThreads) stage[r + i] = ld_v4u(chunks + i);
+        // nch <= kStageChunks < 3 * kThreads: at most three loads per lane, all issued
+        // before the LDS writes
+        v4u c[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          const int i = j * kThreads + threadIdx.x;
+          if (i < nch) c[j] = ld_v4u_global(chunks + i);
+        }
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          const int i = j * kThreads + threadIdx.x;
+          if (i < nch) stage[r + i] = c[j];
+        }
         off = r * kGroup + d - int(a - block_base);  // LDS element of block element e: off + e
         r += nch;
       }
