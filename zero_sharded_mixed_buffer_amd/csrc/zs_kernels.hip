@@ -636,11 +636,20 @@ __global__ __launch_bounds__(kThreads) void k_check(const uint16_t* __restrict__
   if (unit < 0) return;  // uniform across the workgroup
   const bool vec_ok = aligned16(shard);
   G16 vals[kPackGroups];
+  if (vec_ok && (unit + 1) * kPackBlock <= n) {  // uniform: a full aligned block, loads issued together
+    v4u c[kPackGroups];
 #pragma unroll
-  for (int u = 0; u < kPackGroups; ++u) {
-    const int64_t q = unit * kPackBlock + int64_t(u * kThreads + threadIdx.x) * kGroup;
-    const int cnt = group_count(n, q);
-    vals[u] = (cnt == kGroup && vec_ok) ? ld16_vec(shard + q) : ld16_elem(shard + q, cnt);
+    for (int u = 0; u < kPackGroups; ++u)
+      c[u] = ld_v4u_global(shard + unit * kPackBlock + int64_t(u * kThreads + threadIdx.x) * kGroup);
+#pragma unroll
+    for (int u = 0; u < kPackGroups; ++u) vals[u] = G16{{c[u].x, c[u].y, c[u].z, c[u].w}};
+  } else {
+#pragma unroll
+    for (int u = 0; u < kPackGroups; ++u) {
+      const int64_t q = unit * kPackBlock + int64_t(u * kThreads + threadIdx.x) * kGroup;
+      const int cnt = group_count(n, q);
+      vals[u] = (cnt == kGroup && vec_ok) ? ld16_vec(shard + q) : ld16_elem(shard + q, cnt);
+    }
   }
   double acc = 0.0;
 #pragma unroll
