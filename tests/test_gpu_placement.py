@@ -162,6 +162,39 @@ def test_owned_allgather_input_matches_flat_param_out(monkeypatch, placement):
     b.close()
 
 
+def test_allgather_input_follows_restored_parameters():
+    """load_state_dict refills the owned all-gather input from the parameters the model
+    restored first, so that a rank resumed at a skipped step hands out its real parameters."""
+    Z = _z()
+    wl = WORKLOADS["moe_mini_dp4"]
+    dev = torch.device("cuda", 0)
+    p0 = gen.make_params(wl, dev)
+    params = [p.clone() for p in p0]
+    kw = dict(dp_world=wl.dp_world, dp_rank=wl.dp_rank, align=wl.align, dynamic_loss_scale=wl.dynamic,
+              init_scale=wl.init_scale, allgather_input=True)
+    opt = Z.ZeroShardedAdamW(params, **kw)
+    sd = opt.state_dict()
+    exch = torch.zeros(wl.dp_world, dtype=torch.float64, device=dev)
+    grads = gen.make_grads(wl, 1, wl.init_scale, dev, with_faults=False)
+    opt.pack(grads)
+    opt.check(local_sumsq_out=exch[wl.dp_rank:wl.dp_rank + 1])
+    opt.norm(rank_sumsq=exch)
+    opt.update(scatter=False)  # the all-gather input now holds the stepped shard
+    torch.cuda.synchronize()
+    offsets = Z.zs_plan(wl.numels, wl.dp_world, wl.dp_rank, wl.align)[0]
+    whole = torch.zeros(opt.flat_numel, dtype=p0[0].dtype, device=dev)
+    for p, off in zip(p0, offsets):
+        whole[off:off + p.numel()] = p.reshape(-1)
+    want = whole[opt.shard_begin:opt.shard_begin + opt.shard_numel]
+    assert not torch.equal(_bits(opt.flat_param), _bits(want))
+    with torch.no_grad():  # the model restores its parameters, then the optimizer its state
+        for p, q in zip(params, p0):
+            p.copy_(q)
+    opt.load_state_dict(sd)
+    assert torch.equal(_bits(opt.flat_param), _bits(want))
+    opt.close()
+
+
 def test_allgather_input_needs_several_ranks_without_views():
     Z = _z()
     wl = WORKLOADS["llama_mini"]
