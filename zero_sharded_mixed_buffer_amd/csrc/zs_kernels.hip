@@ -9,7 +9,8 @@
 // tensor (every tile of a large tensor) takes a uniform fast path with one base pointer;
 // when that tensor's address is not 16-byte aligned (ragged lists), the tile goes through
 // LDS and is funnel-shifted into aligned 16-byte chunks.  A whole pack block that meets
-// several segments copies each segment's piece into LDS and reads its groups back; other
+// several segments loads each segment's piece into LDS (as 16-byte chunks when the block
+// meets at most 16 segments) and reads its groups back; other
 // tiles that meet several segments (the update's scatter, the unpack, the edges of a
 // bucket's range) look each 8-element group up by binary search over the tile's few
 // segments and fall back to 2-byte accesses only where a group straddles a boundary.
@@ -17,8 +18,9 @@
 // Numerics (the pages keep master weights and Adam moments in FP32 and ask for sensitive
 // reductions in higher precision - "Deep dive: Megatron", section "Precision"):
 //   - the sum of squares is accumulated in fp64 from exact fp16/bf16 -> fp64 widening;
-//   - the AdamW update is evaluated in fp64 (CDNA4 has full-rate fp64 vector ALUs and the
-//     kernel is HBM-bound) and each stored fp32 value is rounded once;
+//   - the AdamW update is evaluated in fp64 (CDNA4's fp64 vector rate, half its fp32
+//     rate, is far above what this HBM-bound kernel needs) and each stored fp32 value is
+//     rounded once;
 //   - model-dtype parameters are the round-to-nearest-even cast of the new fp32 master.
 // No kernel uses atomics: every reduction has a fixed order, so results are reproducible.
 
