@@ -42,7 +42,7 @@ def pointer_table(tensors, device):
 TUNE_MIN_ELEMENTS = 1 << 26
 # The tuning first times up to this many separate allocations of the buffers, together using
 # at most this fraction of the free device memory, and keeps the fastest.
-TUNE_MAX_ARENAS = 16
+TUNE_MAX_ARENAS = 64
 TUNE_ARENA_MEMORY_FRACTION = 0.5
 
 # Checkpoint format of ZeroShardedAdamW.state_dict(), and the state fields it keeps (the
