@@ -45,6 +45,17 @@ TUNE_MIN_ELEMENTS = 1 << 26
 TUNE_MAX_ARENAS = 64
 TUNE_ARENA_MEMORY_FRACTION = 0.5
 
+
+def tune_arena_count(free_bytes, arena_bytes, max_arenas=None, fraction=None):
+    """How many candidate arenas of arena_bytes the placement tuning allocates when
+    free_bytes of device memory are free: as many as `fraction` of it holds, at most
+    `max_arenas`, and always one (the tuning then falls back if even that does not fit)."""
+    max_arenas = TUNE_MAX_ARENAS if max_arenas is None else max_arenas
+    fraction = TUNE_ARENA_MEMORY_FRACTION if fraction is None else fraction
+    if arena_bytes <= 0:
+        raise ValueError("arena_bytes must be positive")
+    return max(1, min(int(max_arenas), int(free_bytes * fraction) // int(arena_bytes)))
+
 # Checkpoint format of ZeroShardedAdamW.state_dict(), and the state fields it keeps (the
 # others are results of the latest check and norm, recomputed by the next step).
 STATE_FORMAT = "zs-rank-state-1"
@@ -300,7 +311,7 @@ class ZeroShardedAdamW:
         padded = {k: (b + step - 1) // step * step for k, b in sizes.items()}
         total = sum(padded.values())
         free, _ = torch.cuda.mem_get_info(dev)
-        n_arenas = max(1, min(TUNE_MAX_ARENAS, int(free * TUNE_ARENA_MEMORY_FRACTION) // total))
+        n_arenas = tune_arena_count(free, total)
         arenas = []
         for _ in range(n_arenas):
             try:
