@@ -1,7 +1,7 @@
 /*
  * zs_probe.h - bandwidth yardsticks exported by libzs.so beside the optimizer step (zs.h).
  *
- * They are not part of the step.  The measurement harness times them on the same buffers
+ * They are not part of the step.  A benchmark times them on the same buffers
  * as the step, to learn what the machine delivers for the step's own access patterns with
  * the arithmetic taken away ("3.7 Megatron-LM, DeepSpeed & Parallelism in Practice",
  * section "ZeRO-Offload and ZeRO-Infinity": the optimizer step is bound by memory
