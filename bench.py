@@ -290,10 +290,11 @@ def main():
     ap.add_argument("--no-decay", choices=["none", "1d"], default="none",
                     help="1d: tensors with at most one dimension (biases, norm weights) take no weight decay")
     ap.add_argument("--state-spacing-gib", type=float, default=0.0,
-                    help="place master, m and v this many GiB apart in one allocation (0: three allocations)")
+                    help="place master, m and v this many GiB apart in one allocation (0: the --placement policy)")
     ap.add_argument("--placement", choices=["tune", "separate"], default="tune",
-                    help="tune: the optimizer carves its gradient buffer and master/m/v from one allocation in the "
-                         "order its update measures fastest (the default); separate: four allocations")
+                    help="tune: the optimizer carves its gradient buffer and master/m/v from the fastest of several "
+                         "candidate allocations, in the order its update measures fastest there (the default); "
+                         "separate: four allocations")
     ap.add_argument("--log-steps", type=int, default=0,
                     help="after the timed region, run this many more steps reading the state after each and "
                          "print one [zs_step k] line per step (scale, skips, norm, clip, time)")
