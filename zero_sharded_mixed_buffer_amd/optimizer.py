@@ -131,7 +131,9 @@ class ZeroShardedAdamW:
     placement: "tune" (default): a shard of at least TUNE_MIN_ELEMENTS elements carves the
         gradient buffer and master / m / v from one allocation: the fastest of several
         candidates, with the four in the order whose update measured fastest in it (see
-        _tune_placement); "separate": four allocations.
+        _tune_placement); "separate": four allocations.  While it is built, the candidates
+        together hold at most TUNE_ARENA_MEMORY_FRACTION of the free device memory and at
+        most TUNE_MAX_ARENAS of them are tried (module constants a caller may lower).
     flat_views: the parameters and their .grad become views into two flat buffers laid out
         like the gradient buffer (a contiguous parameter buffer and a contiguous gradient
         buffer that backward fills in place).  step() with no gradient list then checks the
